@@ -1,0 +1,294 @@
+"""CPU oracle for Subquadratic Sparse Attention (SSA) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The product path (the HIP library and its binding) never
+calls it and fails loudly when its native library is missing.
+
+What it computes, from the write-up "Subquadratic Sparse Attention (SSA)"
+(git.hmmc.top/jonsmirl/ssa), introduction paragraph (mechanism steps i-iii) and
+section "The idea in one screen" (recovery law and routing score):
+
+  for each query row (sequence, q-head h, position t):
+    1. per complete key block c of the row's KV head: mean mu_c and population
+       covariance Sigma_c of its B keys (the "per-block summary statistics");
+    2. routing score r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q over the blocks
+       whose last key is <= t;
+    3. keep the top-k scores (ties to the lower block index);
+    4. key set S(t) = union of the selected blocks and the local window
+       [max(0, t-W+1), t], each key once;
+    5. exact softmax attention over S(t): O and the log-sum-exp LSE;
+    6. the dropped softmax mass 1 - (dense causal weight on S(t)).
+
+All arithmetic is float64 on values that are exact copies of the caller's
+inputs (float32 or bfloat16 values).  There is no blocking, fusion or
+reordering beyond what the definition states; matmul, einsum and lexsort are
+used as library primitives.  Readings of points the write-up leaves open:
+  * the score uses raw q and raw key statistics, beta on raw logits;
+  * Sigma_c is the population (1/B) covariance;
+  * only complete blocks are routable, and only if their last key is <= t;
+  * the window [max(0, t-W+1), t] includes t; S(t) is a set;
+  * k larger than the number of routable blocks selects them all (-1 padding);
+  * GQA: q-head h reads KV head h // (Hq/Hkv);
+  * LSE is the natural log of sum_{j in S} exp(scale * q.k_j).
+
+Every function here is pinned by a CPU test against something other than
+itself (closed forms, textbook formulations, brute force, library routines);
+the one study that has no such pin (planted-outlier recall) says so.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Params:
+    """Method parameters in the write-up's notation."""
+
+    block: int      # B, keys per block
+    top_k: int      # k, blocks kept per query
+    window: int     # W, local window length (>= 1)
+    beta: float     # routing inverse temperature on raw logits
+    scale: float    # softmax scale on raw logits (float32 value of 1/sqrt(d))
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact float64 copy of a float32 / bfloat16 array (torch or numpy)."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch  # local: only for the dtype check
+        if x.dtype != torch.float64:
+            x = x.to(torch.float64)
+        return x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+# -- step 1: per-block summary statistics ------------------------------------
+
+def block_stats(K: np.ndarray, B: int) -> tuple[np.ndarray, np.ndarray]:
+    """Mean and population covariance of every complete block of B keys.
+
+    K: [n, d] keys of one (sequence, KV head).  Returns mu [nb, d] and
+    sigma [nb, d, d] with nb = n // B.  Sigma_c = (1/B) sum_j (k_j - mu_c)(k_j - mu_c)^T,
+    the covariance whose quadratic form q^T Sigma_c q is the variance of the
+    logit q.k_j across the block ("The idea in one screen").
+    """
+    K = as_f64(K)
+    n, d = K.shape
+    nb = n // B
+    mu = np.zeros((nb, d))
+    sigma = np.zeros((nb, d, d))
+    for c in range(nb):
+        blk = K[c * B:(c + 1) * B]
+        m = blk.sum(axis=0) / B
+        X = blk - m
+        mu[c] = m
+        sigma[c] = (X.T @ X) / B
+    return mu, sigma
+
+
+# -- step 2: routing score over routable blocks -------------------------------
+
+def routable_blocks(t: int, B: int, nb: int) -> int:
+    """Number of blocks routable for query position t: blocks c with (c+1)B-1 <= t."""
+    return max(0, min(nb, (t + 1) // B))
+
+
+def route_scores(q: np.ndarray, mu: np.ndarray, sigma: np.ndarray, beta: float) -> np.ndarray:
+    """r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q for every block given.
+
+    Second-cumulant (tempered) routing score, "The idea in one screen".
+    q: [d]; mu: [C, d]; sigma: [C, d, d].  Returns [C].
+    """
+    q = as_f64(q)
+    mean_term = mu @ q
+    var_term = np.einsum("i,cij,j->c", q, sigma, q)
+    return mean_term + 0.5 * beta * var_term
+
+
+def route_scores_from_logits(q: np.ndarray, K: np.ndarray, B: int, C: int,
+                             beta: float) -> np.ndarray:
+    """The same score computed from the logits: mean_j(q.k_j) + (beta/2) var_pop_j(q.k_j).
+
+    This is the reading "block mean plus the variance of the logit across the
+    block" of the routing score, evaluated on the B keys of each block directly.
+    """
+    q = as_f64(q)
+    K = as_f64(K)
+    out = np.zeros(C)
+    for c in range(C):
+        s = K[c * B:(c + 1) * B] @ q
+        m = s.sum() / B
+        out[c] = m + 0.5 * beta * (((s - m) ** 2).sum() / B)
+    return out
+
+
+# -- step 3: top-k selection ---------------------------------------------------
+
+def select_topk(r: np.ndarray, k: int) -> tuple[np.ndarray, float, float]:
+    """Top-k block indices of the scores r (ties to the lower index).
+
+    Returns (idx, r_k, r_k1): idx is int32 [k], the selected block indices in
+    ascending order padded with -1 when fewer than k blocks exist; r_k and r_k1
+    are the k-th and (k+1)-th largest scores (nan where they do not exist).
+    """
+    r = np.asarray(r, dtype=np.float64)
+    E = r.shape[0]
+    order = np.lexsort((np.arange(E), -r))   # primary key -r, then block index
+    keep = min(k, E)
+    idx = np.full(k, -1, dtype=np.int32)
+    idx[:keep] = np.sort(order[:keep])
+    r_k = float(r[order[k - 1]]) if 0 < k <= E else math.nan
+    r_k1 = float(r[order[k]]) if k < E else math.nan
+    return idx, r_k, r_k1
+
+
+# -- step 4: key-set assembly --------------------------------------------------
+
+def key_set(t: int, idx: np.ndarray, B: int, W: int) -> np.ndarray:
+    """S(t) = union of the selected blocks' keys and the window [max(0,t-W+1), t]."""
+    keys: set[int] = set()
+    for c in np.asarray(idx).tolist():
+        if c >= 0:
+            keys.update(range(c * B, (c + 1) * B))
+    keys.update(range(max(0, t - W + 1), t + 1))
+    return np.array(sorted(keys), dtype=np.int64)
+
+
+# -- step 5: exact softmax attention over the selected keys ------------------
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndarray,
+           scale: float) -> tuple[np.ndarray, float]:
+    """Exact softmax attention of q over the keys S: returns (O [d], LSE).
+
+    s_j = scale * q.k_j;  O = sum_j softmax(s)_j v_j;  LSE = ln sum_j exp(s_j).
+    """
+    q = as_f64(q)
+    s = scale * (as_f64(K)[S] @ q)
+    m = s.max()
+    p = np.exp(s - m)
+    l = p.sum()
+    O = (p @ as_f64(V)[S]) / l
+    return O, float(m + math.log(l))
+
+
+# -- step 6: dropped mass ------------------------------------------------------
+
+def dropped_mass(q: np.ndarray, K: np.ndarray, S: np.ndarray, t: int,
+                 scale: float) -> tuple[float, float]:
+    """Dropped softmax mass of S(t) against dense causal attention over j <= t.
+
+    Returns (eps_from_lse, eps_direct): 1 - exp(LSE_S - LSE_full), and the sum
+    of the dense softmax probabilities of the keys j <= t that are not in S.
+    """
+    q = as_f64(q)
+    s = scale * (as_f64(K)[: t + 1] @ q)
+    m = s.max()
+    p = np.exp(s - m)
+    p = p / p.sum()
+    inside = np.zeros(t + 1, dtype=bool)
+    inside[S] = True
+    eps_direct = float(p[~inside].sum())
+    l_full = math.log(np.exp(s - m).sum()) + m
+    l_sel = math.log(np.exp(s[S] - m).sum()) + m
+    return float(-math.expm1(l_sel - l_full)), eps_direct
+
+
+# -- the full row --------------------------------------------------------------
+
+def prefill_row(q, K, V, mu, sigma, p: Params, t: int, with_dense: bool = False) -> dict:
+    """Every step for one query row at position t of one (sequence, q-head).
+
+    K, V: [n, d] of the row's KV head; mu, sigma: that head's block statistics.
+    """
+    nb = mu.shape[0]
+    C = routable_blocks(t, p.block, nb)
+    r = route_scores(q, mu[:C], sigma[:C], p.beta)
+    idx, r_k, r_k1 = select_topk(r, p.top_k)
+    S = key_set(t, idx, p.block, p.window)
+    O, lse = attend(q, K, V, S, p.scale)
+    out = dict(idx=idx, scores=r, r_k=r_k, r_k1=r_k1, S=S, O=O, lse=lse)
+    if with_dense:
+        O_full, lse_full = attend(q, K, V, np.arange(t + 1), p.scale)
+        eps, eps_direct = dropped_mass(q, K, S, t, p.scale)
+        out.update(O_full=O_full, lse_full=lse_full, eps=eps, eps_direct=eps_direct)
+    return out
+
+
+class PrefillOracle:
+    """Per-row oracle over a whole prefill input, caching per-head statistics.
+
+    Q: [b, Hq, n, d]; K, V: [b, Hkv, n, d] (torch or numpy, any float dtype).
+    """
+
+    def __init__(self, Q, K, V, p: Params):
+        self.Q, self.K, self.V, self.p = Q, K, V, p
+        self.hq, self.hkv = Q.shape[1], K.shape[1]
+        self._cache: dict[tuple[int, int], tuple] = {}
+
+    def head(self, b: int, kv: int):
+        key = (b, kv)
+        if key not in self._cache:
+            Kh = as_f64(self.K[b, kv])
+            Vh = as_f64(self.V[b, kv])
+            mu, sigma = block_stats(Kh, self.p.block)
+            self._cache[key] = (Kh, Vh, mu, sigma)
+        return self._cache[key]
+
+    def drop(self, b: int, kv: int) -> None:
+        self._cache.pop((b, kv), None)
+
+    def row(self, b: int, h: int, t: int, with_dense: bool = False) -> dict:
+        kv = h // (self.hq // self.hkv)
+        Kh, Vh, mu, sigma = self.head(b, kv)
+        return prefill_row(as_f64(self.Q[b, h, t]), Kh, Vh, mu, sigma, self.p, t, with_dense)
+
+
+# -- decode --------------------------------------------------------------------
+
+def decode_step(q, k_new, v_new, K_cache, V_cache, L: int, p: Params,
+                with_dense: bool = False) -> dict:
+    """One decode step for one (sequence, q-head): append at L, query at t = L.
+
+    K_cache/V_cache: [>= L, d] of the head's KV head (first L rows valid).
+    The step is the prefill definition at t = L over the L+1 keys.
+    """
+    K = np.concatenate([as_f64(K_cache)[:L], as_f64(k_new)[None]], axis=0)
+    V = np.concatenate([as_f64(V_cache)[:L], as_f64(v_new)[None]], axis=0)
+    mu, sigma = block_stats(K, p.block)
+    return prefill_row(as_f64(q), K, V, mu, sigma, p, L, with_dense)
+
+
+# -- the recovery law ------------------------------------------------------------
+
+def recovery_weight(beta: float, delta: float, mu: float) -> float:
+    """w* = sigma(beta*Delta - log mu): softmax weight of one target with margin
+    Delta over mu equal distractors ("The idea in one screen", recovery law)."""
+    z = beta * delta - math.log(mu)
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+# -- study without a pin ----------------------------------------------------------
+
+def planted_recall(oracle: PrefillOracle, plants: list[dict], beta: float | None = None) -> float:
+    """Fraction of planted outliers whose block the target row selects.
+
+    PARITY UNPINNED: the write-up states only the qualitative result
+    (second-cumulant routing recovers targets that centroid routing misses).
+    """
+    if not plants:
+        return math.nan
+    p = oracle.p if beta is None else Params(oracle.p.block, oracle.p.top_k, oracle.p.window,
+                                             beta, oracle.p.scale)
+    hits = 0
+    for pl in plants:
+        kv = pl["h"] // (oracle.hq // oracle.hkv)
+        Kh, Vh, mu, sigma = oracle.head(pl["b"], kv)
+        t = pl["t"]
+        C = routable_blocks(t, p.block, mu.shape[0])
+        r = route_scores(as_f64(oracle.Q[pl["b"], pl["h"], t]), mu[:C], sigma[:C], p.beta)
+        idx, _, _ = select_topk(r, p.top_k)
+        hits += int(pl["block"] in idx.tolist())
+    return hits / len(plants)

@@ -1,0 +1,477 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each check is a function of the oracle implementation, so the same check can be
+run against a copy of the oracle with a planted mistake (see test_mutants_*):
+every check must pass on the oracle, and each plausible mistake (a dropped
+term, a wrong factor, a wrong index or bound, a transposed operand) must fail
+at least one of them.
+"""
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import ssa_oracle as OR
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _impl(**overrides):
+    """The oracle's functions as a namespace, with some replaced (for mutants)."""
+    ns = types.SimpleNamespace(
+        block_stats=OR.block_stats, route_scores=OR.route_scores,
+        route_scores_from_logits=OR.route_scores_from_logits, select_topk=OR.select_topk,
+        routable_blocks=OR.routable_blocks, key_set=OR.key_set, attend=OR.attend,
+        dropped_mass=OR.dropped_mass, recovery_weight=OR.recovery_weight)
+    for k, v in overrides.items():
+        setattr(ns, k, v)
+
+    def prefill_row(q, K, V, mu, sigma, p, t, with_dense=False):
+        C = ns.routable_blocks(t, p.block, mu.shape[0])
+        r = ns.route_scores(q, mu[:C], sigma[:C], p.beta)
+        idx, r_k, r_k1 = ns.select_topk(r, p.top_k)
+        S = ns.key_set(t, idx, p.block, p.window)
+        Oo, lse = ns.attend(q, K, V, S, p.scale)
+        out = dict(idx=idx, scores=r, S=S, O=Oo, lse=lse)
+        if with_dense:
+            Of, lf = ns.attend(q, K, V, np.arange(t + 1), p.scale)
+            eps, eps_d = ns.dropped_mass(q, K, S, t, p.scale)
+            out.update(O_full=Of, lse_full=lf, eps=eps, eps_direct=eps_d)
+        return out
+    ns.prefill_row = prefill_row
+    return ns
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# -- checks (each raises AssertionError on failure) ---------------------------
+
+def check_golden(ns):
+    g = _golden()
+    rs = g["routing_score"]
+    K = np.array(rs["keys"], float)
+    mu, sigma = ns.block_stats(K, rs["block_size"])
+    np.testing.assert_allclose(mu, rs["mu"], atol=1e-15)
+    np.testing.assert_allclose(sigma, rs["sigma"], atol=1e-15)
+    q = np.array(rs["q"], float)
+    for beta, want in rs["scores"].items():
+        r = ns.route_scores(q, mu, sigma, float(beta))
+        np.testing.assert_allclose(r, want, atol=1e-12)
+        idx, _, _ = ns.select_topk(r, 1)
+        assert idx.tolist() == rs["top1"][beta]
+    tk = g["topk_ties"]
+    for case in tk["cases"]:
+        idx, r_k, r_k1 = ns.select_topk(np.array(tk["scores"], float), case["k"])
+        assert idx.tolist() == case["idx"]
+        for got, want in ((r_k, case["r_k"]), (r_k1, case["r_k1"])):
+            assert (math.isnan(got) if want is None else got == want)
+    rt = g["routable"]
+    for t, want in rt["cases"]:
+        assert ns.routable_blocks(t, rt["block_size"], rt["n_blocks"]) == want
+    ks = g["key_set"]
+    for case in ks["cases"]:
+        S = ns.key_set(case["t"], np.array(case["idx"]), ks["block_size"], case["window"])
+        assert S.tolist() == case["keys"]
+    at = g["attention"]
+    for case in at["cases"]:
+        Oo, lse = ns.attend(np.array(at["q"]), np.array(at["keys"], float),
+                            np.array(at["values"], float), np.array([0, 1]), case["scale"])
+        np.testing.assert_allclose(Oo, case["O"], atol=1e-12)
+        assert abs(lse - case["lse"]) < 1e-12
+    for case in g["recovery_law"]["cases"]:
+        assert abs(ns.recovery_weight(case["beta"], case["delta"], case["mu"]) - case["w"]) < 1e-12
+    dm = g["dropped_mass"]
+    eps, eps_d = ns.dropped_mass(np.array(dm["q"], float), np.array(dm["keys"], float),
+                                 np.array(dm["S"]), dm["t"], dm["scale"])
+    assert abs(eps - dm["eps"]) < 1e-12 and abs(eps_d - dm["eps"]) < 1e-12
+
+
+def check_stats_vs_library(ns, seed=0):
+    """P1: block stats against np.mean / np.cov(bias=True); quadratic form = logit variance."""
+    rng = np.random.default_rng(seed)
+    B, d, nb = 16, 8, 5
+    K = rng.normal(size=(nb * B + 3, d)) + rng.normal(size=(d,))
+    mu, sigma = ns.block_stats(K, B)
+    assert mu.shape == (nb, d) and sigma.shape == (nb, d, d)
+    for c in range(nb):
+        blk = K[c * B:(c + 1) * B]
+        np.testing.assert_allclose(mu[c], np.mean(blk, axis=0), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(sigma[c], np.cov(blk, rowvar=False, bias=True), rtol=1e-12,
+                                   atol=1e-14)
+        q = rng.normal(size=d)
+        logits = blk @ q
+        assert abs(q @ mu[c] - np.mean(logits)) <= 1e-12 * max(1, abs(np.mean(logits)))
+        assert abs(q @ sigma[c] @ q - np.var(logits)) <= 1e-12 * np.var(logits)
+
+
+def check_scores_two_ways(ns, seed=1):
+    """P2: the covariance form of the score equals the logit-moment form."""
+    rng = np.random.default_rng(seed)
+    B, d, C = 32, 16, 6
+    K = rng.normal(size=(C * B, d)) * rng.uniform(0.2, 2.0, size=d)
+    mu, sigma = ns.block_stats(K, B)
+    for beta in (0.0, 0.7, 2.0, 5.0):
+        q = rng.normal(size=d)
+        a = ns.route_scores(q, mu, sigma, beta)
+        b = ns.route_scores_from_logits(q, K, B, C, beta)
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def check_centroid_limit(ns, seed=2):
+    """P3: beta = 0 ranks blocks by the centroid logit mean_j q.k_j alone."""
+    rng = np.random.default_rng(seed)
+    B, d, C = 8, 4, 20
+    K = rng.normal(size=(C * B, d)) * 3
+    mu, sigma = ns.block_stats(K, B)
+    q = rng.normal(size=d)
+    r = ns.route_scores(q, mu, sigma, 0.0)
+    centroid = np.array([np.mean(K[c * B:(c + 1) * B] @ q) for c in range(C)])
+    np.testing.assert_allclose(r, centroid, rtol=1e-12, atol=1e-12)
+    idx, _, _ = ns.select_topk(r, 5)
+    assert sorted(idx.tolist()) == sorted(np.argsort(-centroid, kind="stable")[:5].tolist())
+
+
+def check_topk_brute(ns, seed=3):
+    """P4: top-k equals the first k of Python's stable sort by (-score, index)."""
+    rng = np.random.default_rng(seed)
+    for trial in range(200):
+        E = int(rng.integers(0, 40))
+        k = int(rng.integers(0, 12))
+        r = rng.integers(-3, 4, size=E).astype(float)   # many exact ties
+        idx, r_k, r_k1 = ns.select_topk(r, k)
+        ranked = sorted(range(E), key=lambda c: (-r[c], c))
+        want = sorted(ranked[:k]) + [-1] * max(0, k - E)
+        assert idx.tolist() == want, (r, k)
+        want_k = r[ranked[k - 1]] if 0 < k <= E else math.nan
+        want_k1 = r[ranked[k]] if k < E else math.nan
+        assert (math.isnan(r_k) and math.isnan(want_k)) or r_k == want_k
+        assert (math.isnan(r_k1) and math.isnan(want_k1)) or r_k1 == want_k1
+
+
+def _textbook(q, K, V, mask, scale):
+    """Masked-dense softmax attention, one query row."""
+    s = np.where(mask, scale * (K @ q), -np.inf)
+    m = s.max()
+    p = np.exp(s - m)
+    return (p @ V) / p.sum(), m + math.log(p.sum())
+
+
+def _rand_head(rng, n, d, B):
+    K = rng.normal(size=(n, d)) + np.repeat(rng.normal(size=(-(-n // B), d)), B, 0)[:n]
+    return rng.normal(size=(n, d)), K, rng.normal(size=(n, d))
+
+
+def check_dense_reduction(ns, seed=4):
+    """P5: k >= nb with W >= B-1 is dense causal attention (textbook and torch SDPA)."""
+    rng = np.random.default_rng(seed)
+    for (n, d, B, W) in ((67, 8, 8, 7), (64, 4, 16, 16), (50, 6, 5, 9)):
+        Q, K, V = _rand_head(rng, n, d, B)
+        mu, sigma = ns.block_stats(K, B)
+        nb = n // B
+        scale = 1 / math.sqrt(d)
+        p = O.Params(B, nb + 2, W, 2.0, scale)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(Q)[None, None], torch.tensor(K)[None, None], torch.tensor(V)[None, None],
+            is_causal=True, scale=scale)[0, 0].numpy()
+        for t in range(n):
+            row = ns.prefill_row(Q[t], K, V, mu, sigma, p, t, with_dense=True)
+            assert row["S"].tolist() == list(range(t + 1))
+            tb, tl = _textbook(Q[t], K, V, np.arange(n) <= t, scale)
+            np.testing.assert_allclose(row["O"], tb, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(row["O"], ref[t], rtol=1e-12, atol=1e-12)
+            assert abs(row["lse"] - tl) < 1e-12
+            assert abs(row["eps"]) < 1e-12 and abs(row["eps_direct"]) < 1e-12
+
+
+def check_window_only(ns, seed=5):
+    """P6: k = 0 is sliding-window attention of width W (banded causal mask)."""
+    rng = np.random.default_rng(seed)
+    n, d, B = 45, 5, 8
+    Q, K, V = _rand_head(rng, n, d, B)
+    mu, sigma = ns.block_stats(K, B)
+    for W in (1, 3, 8, 13):
+        p = O.Params(B, 0, W, 2.0, 0.37)
+        for t in range(n):
+            row = ns.prefill_row(Q[t], K, V, mu, sigma, p, t)
+            j = np.arange(n)
+            tb, tl = _textbook(Q[t], K, V, (j <= t) & (j > t - W), 0.37)
+            np.testing.assert_allclose(row["O"], tb, rtol=1e-12, atol=1e-12)
+            assert abs(row["lse"] - tl) < 1e-12
+
+
+def check_gather_equals_mask(ns, seed=6):
+    """P7: attention over the gathered S(t) equals masked-dense attention with M[t,j] = [j in S(t)]."""
+    rng = np.random.default_rng(seed)
+    n, d, B, W = 96, 8, 8, 5
+    Q, K, V = _rand_head(rng, n, d, B)
+    mu, sigma = ns.block_stats(K, B)
+    p = O.Params(B, 3, W, 2.0, 0.3)
+    for t in range(0, n, 7):
+        row = ns.prefill_row(Q[t], K, V, mu, sigma, p, t)
+        j = np.arange(n)
+        blocks = [c for c in row["idx"].tolist() if c >= 0]
+        mask = np.isin(j // B, blocks) | ((j <= t) & (j > t - W))
+        # every selected block is complete and causal, so the mask needs no j <= t clip
+        assert all((c + 1) * B - 1 <= t for c in blocks)
+        tb, tl = _textbook(Q[t], K, V, mask, 0.3)
+        np.testing.assert_allclose(row["O"], tb, rtol=1e-12, atol=1e-12)
+        assert abs(row["lse"] - tl) < 1e-12
+
+
+def check_recovery_law(ns):
+    """P8: target with margin Delta over mu equal distractors gets weight sigma(beta*Delta - log mu)."""
+    d = 3
+    for mu_count in (1, 7, 63, 511):
+        for delta in (-2.0, -0.5, 0.0, 0.3, 1.0, 4.0, 9.0):
+            for beta in (0.125, 1 / math.sqrt(128), 1.0, 2.0):
+                # bare softmax over [target, distractors]: logits beta*(s + Delta), beta*s
+                s0 = 0.7
+                logits = np.array([beta * (s0 + delta)] + [beta * s0] * mu_count)
+                w = np.exp(logits - logits.max())
+                w = w[0] / w.sum()
+                law = ns.recovery_weight(beta, delta, mu_count)
+                assert abs(w - law) < 1e-12
+                # through attention: q.k* = s0+Delta, q.k = s0, V one-hot on the target
+                q = np.array([1.0, 0.0, 0.0])
+                K = np.zeros((mu_count + 1, d))
+                K[0, 0] = s0 + delta
+                K[1:, 0] = s0
+                K[1:, 1] = np.linspace(-1, 1, mu_count)  # orthogonal to q: logits unchanged
+                V = np.zeros((mu_count + 1, d))
+                V[0, 2] = 1.0
+                Oo, _ = ns.attend(q, K, V, np.arange(mu_count + 1), beta)
+                assert abs(Oo[2] - law) < 1e-12
+
+
+def check_recovery_law_pipeline(ns):
+    """P8 through the full row: the planted target and its block-mates as the selected set."""
+    B, d = 8, 4
+    mu_count = 2 * B - 1            # distractors: the other keys of the two selected blocks
+    n = 4 * B
+    beta_soft, delta = 0.5, 3.0
+    q = np.array([1.0, 0, 0, 0])
+    K = np.zeros((n, d))
+    K[:, 0] = -50.0                  # keys outside the selected blocks: far below
+    K[:2 * B, 0] = 1.0               # blocks 0 and 1: distractors at logit 1 (before scale)
+    K[:2 * B, 1] = np.linspace(-3, 3, 2 * B)   # routing spread, orthogonal to q
+    K[5, 0] = 1.0 + delta            # the target in block 0
+    V = np.zeros((n, d))
+    V[5, 3] = 1.0
+    mu, sigma = ns.block_stats(K, B)
+    t = n - 1
+    p = O.Params(B, 2, 1, 2.0, beta_soft)
+    # make the window key (t) a distractor-free position: give it a very low logit
+    row = ns.prefill_row(q, K, V, mu, sigma, p, t, with_dense=False)
+    assert row["idx"].tolist() == [0, 1]
+    # S = blocks 0,1 plus window {t} whose logit is -50: weight ~ e^-25 relative
+    law = ns.recovery_weight(beta_soft, delta, mu_count)
+    assert abs(row["O"][3] - law) < 1e-9
+
+
+def check_dropped_mass(ns, seed=7):
+    """P9: eps two ways agree, lie in [0, 1], and bound ||O_S - O_full||_inf <= 2 eps max|v|."""
+    rng = np.random.default_rng(seed)
+    n, d, B, W = 128, 8, 16, 4
+    Q, K, V = _rand_head(rng, n, d, B)
+    mu, sigma = ns.block_stats(K, B)
+    p = O.Params(B, 2, W, 2.0, 0.4)
+    for t in range(0, n, 5):
+        row = ns.prefill_row(Q[t], K, V, mu, sigma, p, t, with_dense=True)
+        assert -1e-15 <= row["eps"] <= 1 and abs(row["eps"] - row["eps_direct"]) < 1e-12
+        bound = 2 * row["eps"] * np.abs(V[: t + 1]).max()
+        assert np.abs(row["O"] - row["O_full"]).max() <= bound + 1e-12
+
+
+def check_decode_equals_prefill(ns, seed=8):
+    """P10: the decode step at t = L equals prefill row L over the same L+1 keys."""
+    rng = np.random.default_rng(seed)
+    d, B, W = 6, 8, 5
+    for L in (0, 7, 8, 31, 40):
+        Q, K, V = _rand_head(rng, L + 1, d, B)
+        p = O.Params(B, 2, W, 2.0, 0.5)
+        dec = O.decode_step(Q[L], K[L], V[L], K[:L], V[:L], L, p)
+        mu, sigma = ns.block_stats(K, B)
+        pre = ns.prefill_row(Q[L], K, V, mu, sigma, p, L)
+        assert dec["idx"].tolist() == pre["idx"].tolist()
+        np.testing.assert_allclose(dec["O"], pre["O"], rtol=1e-12, atol=1e-14)
+        assert abs(dec["lse"] - pre["lse"]) < 1e-12
+
+
+def check_invariances(ns, seed=9):
+    """P11: permuting keys (with values) inside a block changes nothing; a constant
+    added to every logit leaves O unchanged and shifts LSE by that constant."""
+    rng = np.random.default_rng(seed)
+    n, d, B, W = 80, 6, 16, 6
+    Q, K, V = _rand_head(rng, n, d, B)
+    mu, sigma = ns.block_stats(K, B)
+    perm = np.arange(n)
+    for c in range(n // B):
+        perm[c * B:(c + 1) * B] = c * B + rng.permutation(B)
+    K2, V2 = K[perm], V[perm]
+    mu2, sigma2 = ns.block_stats(K2, B)
+    np.testing.assert_allclose(mu2, mu, atol=1e-13)
+    np.testing.assert_allclose(sigma2, sigma, atol=1e-13)
+    p = O.Params(B, 2, W, 2.0, 0.45)
+    for t in range(B * 2 + 3, n, 9):     # windows away from permuted rows of the tail
+        a = ns.prefill_row(Q[t], K, V, mu, sigma, p, t)
+        # keep the window identical: only permute complete blocks strictly before the window
+        wstart = t - W + 1
+        ok = perm.copy()
+        ok[wstart // B * B:] = np.arange(wstart // B * B, n)
+        b = ns.prefill_row(Q[t], K[ok], V[ok], *ns.block_stats(K[ok], B), p, t)
+        assert a["idx"].tolist() == b["idx"].tolist()
+        np.testing.assert_allclose(a["O"], b["O"], rtol=1e-12, atol=1e-13)
+    # constant logit shift via an extra coordinate: q' = [q, c/scale], k' = [k, 1]
+    cshift = 1.7
+    scale = 0.45
+    Ka = np.concatenate([K, np.ones((n, 1))], 1)
+    t = n - 1
+    S = np.arange(0, n, 3)
+    O1, l1 = ns.attend(Q[t], K, V, S, scale)
+    O2, l2 = ns.attend(np.concatenate([Q[t], [cshift / scale]]), Ka, V, S, scale)
+    np.testing.assert_allclose(O1, O2, rtol=1e-12, atol=1e-13)
+    assert abs((l2 - l1) - cshift) < 1e-12
+
+
+CHECKS = [check_golden, check_stats_vs_library, check_scores_two_ways, check_centroid_limit,
+          check_topk_brute, check_dense_reduction, check_window_only, check_gather_equals_mask,
+          check_recovery_law, check_recovery_law_pipeline, check_dropped_mass,
+          check_decode_equals_prefill, check_invariances]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=lambda f: f.__name__)
+def test_oracle_pin(check):
+    check(_impl())
+
+
+# -- planted mistakes: each must be caught by at least one check ----------------
+
+def _mut_sample_cov(K, B):
+    mu, sigma = OR.block_stats(K, B)
+    return mu, sigma * B / (B - 1)
+
+
+def _mut_full_beta(q, mu, sigma, beta):
+    return OR.route_scores(q, mu, sigma, 2 * beta)
+
+
+def _mut_no_var(q, mu, sigma, beta):
+    return OR.route_scores(q, mu, sigma, 0.0)
+
+
+def _mut_minus_var(q, mu, sigma, beta):
+    return OR.route_scores(q, mu, sigma, -beta)
+
+
+def _mut_topk_high_ties(r, k):
+    r = np.asarray(r, float)
+    E = len(r)
+    order = np.lexsort((-np.arange(E), -r))
+    idx = np.full(k, -1, np.int32)
+    idx[:min(k, E)] = np.sort(order[:min(k, E)])
+    return idx, (r[order[k - 1]] if 0 < k <= E else math.nan), (r[order[k]] if k < E else math.nan)
+
+
+def _mut_routable_partial(t, B, nb):
+    return max(0, min(nb, t // B + 1))
+
+
+def _mut_window_exclusive(t, idx, B, W):
+    S = OR.key_set(t, idx, B, W)
+    return S[S != t] if len(S) > 1 else S
+
+
+def _mut_window_wide(t, idx, B, W):
+    return OR.key_set(t, idx, B, W + 1)
+
+
+def _mut_attend_noscale(q, K, V, S, scale):
+    return OR.attend(q, K, V, S, 1.0)
+
+
+def _mut_attend_transposed_v(q, K, V, S, scale):
+    Oo, lse = OR.attend(q, K, V, S, scale)
+    Vs = np.asarray(V, float)[S]
+    s = scale * (np.asarray(K, float)[S] @ np.asarray(q, float))
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    d = Vs.shape[1]
+    if Vs.shape[0] >= d:
+        Oo = Vs[:d, :].T @ p[:d]   # reads V with its roles swapped on a square slice
+    return Oo, lse
+
+
+def _mut_stats_transposed(K, B):
+    K = np.asarray(K, float)
+    n, d = K.shape
+    nb = n // B
+    mu = np.zeros((nb, d))
+    sigma = np.zeros((nb, d, d))
+    for c in range(nb):
+        blk = K[c * B:(c + 1) * B]
+        mu[c] = blk.mean(0)
+        X = blk - mu[c]
+        sigma[c] = (X.T @ X) / B
+        sigma[c] = np.triu(sigma[c]) + np.triu(sigma[c], 1).T * 0.5   # loses symmetry
+    return mu, sigma
+
+
+def _mut_recovery_sign(beta, delta, mu):
+    return 1 / (1 + math.exp(-(beta * delta + math.log(mu))))
+
+
+def _mut_dropped_swapped(q, K, S, t, scale):
+    a, b = OR.dropped_mass(q, K, S, t, scale)
+    return 1 - a, b
+
+
+MUTANTS = {
+    "sample_covariance": dict(block_stats=_mut_sample_cov),
+    "beta_not_halved": dict(route_scores=_mut_full_beta),
+    "variance_term_dropped": dict(route_scores=_mut_no_var),
+    "variance_sign_flipped": dict(route_scores=_mut_minus_var),
+    "ties_to_higher_index": dict(select_topk=_mut_topk_high_ties),
+    "partial_block_routable": dict(routable_blocks=_mut_routable_partial),
+    "window_excludes_t": dict(key_set=_mut_window_exclusive),
+    "window_off_by_one": dict(key_set=_mut_window_wide),
+    "softmax_scale_dropped": dict(attend=_mut_attend_noscale),
+    "values_transposed": dict(attend=_mut_attend_transposed_v),
+    "covariance_asymmetric": dict(block_stats=_mut_stats_transposed),
+    "recovery_sign": dict(recovery_weight=_mut_recovery_sign),
+    "dropped_mass_complement": dict(dropped_mass=_mut_dropped_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    ns = _impl(**MUTANTS[name])
+    failures = 0
+    for check in CHECKS:
+        try:
+            check(ns)
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures >= 1, f"no pin catches the planted mistake {name!r}"
+
+
+def test_planted_recall_report():
+    """Planted-outlier recall, beta = 2 vs beta = 0 (centroid). PARITY UNPINNED:
+    the write-up reports only that the variance term recovers targets the
+    centroid misses; this checks that direction on the tiny workload."""
+    from synth_inputs import CONFIGS, make_prefill
+    wl = CONFIGS["tiny_prefill_4k"]
+    data = make_prefill(wl, seed=0)
+    orc = O.PrefillOracle(data["Q"], data["K"], data["V"],
+                          O.Params(wl.block, wl.top_k, wl.window, wl.beta, wl.scale))
+    r2 = O.planted_recall(orc, data["plants"])
+    r0 = O.planted_recall(orc, data["plants"], beta=0.0)
+    print(f"planted recall beta=2: {r2:.3f}  beta=0: {r0:.3f}")
+    assert r2 >= r0
