@@ -1,0 +1,18 @@
+"""MI355X-native hot path of Subquadratic Sparse Attention (content-routed block statistics).
+
+The work happens in libssa_mi355x.so (hand-written gfx950 HIP kernels behind a
+C ABI, include/ssa.h).  This package is its build script and a thin ctypes
+binding whose functions carry the C entry points' names.
+"""
+from .binding import (  # noqa: F401
+    SSAError,
+    SSAParams,
+    lib,
+    make_params,
+    ssa_block_stats,
+    ssa_decode_step,
+    ssa_route_topk,
+    ssa_sparse_attn_fwd,
+    ssa_workspace_size,
+    status_string,
+)

@@ -1,0 +1,367 @@
+// Routing scores and top-k block selection (prefill).
+//
+// Write-up "Subquadratic Sparse Attention (SSA)", section "The idea in one
+// screen" (second-cumulant score r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q)
+// and introduction step (i) (keep a small content-dependent set of blocks).
+//
+// Formulation.  With T_c the upper triangle of (beta/2) Sigma_c with doubled
+// off-diagonal (T_ij = beta Sigma_ij for i < j, (beta/2) Sigma_ii on the
+// diagonal, 0 below), q^T T_c q = (beta/2) q^T Sigma_c q for symmetric Sigma_c,
+// so   r_c(q) = sum_j q_j (P_j + mu_cj)   with   P = q T_c.
+// For a tile of query rows that share a KV head, P = Q_tile T_c is a dense
+// contraction on MFMA; its triangular shape lets 32-column tile mt skip
+// every 16-row chunk below the diagonal (20 of 32 chunks computed at d=128).
+// The row-dot with q and the running top-k run on the vector ALUs in the
+// MFMA's own register layout (see frag_k in ssa_common.hpp), so Q is read
+// once per tile and stays in registers for the whole sweep over blocks.
+//
+// Precision.  Q is exact in bfloat16.  T_c (float32) is split into a high
+// and a low bfloat16 part and both are contracted, with float32
+// accumulation, so scores carry ~2^-17 relative error instead of the 2^-9 of
+// a single bfloat16 rounding -- enough to reproduce the exact top-k except
+// where two scores are nearly tied.  float32 inputs use the float32 MFMA.
+//
+// Work split.  A workgroup of 8 waves owns 512 consecutive query rows of one
+// (sequence, KV head), ordered (token, group member), so one Sigma_c tile in
+// LDS serves 512 rows: 64 rows per wave, two 32-row MFMA tiles.  Blocks are
+// streamed in order c = 0, 1, ... through a double-buffered LDS copy of a
+// prepared fragment image; ties in the top-k therefore keep the lower block.
+// Workgroups are issued longest (most routable blocks) first.
+#include "ssa_common.hpp"
+#include "ssa_internal.hpp"
+
+namespace ssa {
+namespace {
+
+constexpr int kRouteThreads = 512;
+constexpr int kRouteRows = 512;
+constexpr int kFragBytes = 2048;   // one 32x16 operand fragment: 64 lanes x 32 bytes
+
+template <int D>
+struct RouteLayout {
+  static constexpr int MT = D / 32;                 // 32-wide output tiles
+  static constexpr int NS = D / 16;                 // 16-wide contraction chunks
+  static constexpr int NF = MT * (MT + 1);          // chunks on or above the diagonal
+  static constexpr int MU_OFF = NF * kFragBytes;
+  static constexpr int MU_BYTES = 2 * MT * 16 * 4;  // mu in accumulator order, both lane halves
+  static constexpr int BLOCK_BYTES = (MU_OFF + MU_BYTES + 255) / 256 * 256;
+  __host__ __device__ static constexpr int frag(int mt, int s) { return mt * (mt + 1) + s; }
+};
+
+// Prepared image of one block (workspace): for every output tile mt and
+// chunk s <= 2mt+1, lane (m, h) of the fragment holds T_c[frag_k(s,h,e)][32mt+m]
+// for e = 0..7 -- as bf16 hi (bytes 0..1023) and lo (1024..2047), or float32;
+// then mu_c in accumulator order: [h][mt][4a+b] = mu_c[32mt + 8a + 4h + b].
+template <bool F32, int D>
+__global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ mu,
+                                                          const float* __restrict__ sigma,
+                                                          uint8_t* __restrict__ prep, int64_t nb,
+                                                          float beta) {
+  using Lay = RouteLayout<D>;
+  const int64_t blk = int64_t(blockIdx.y) * nb + blockIdx.x;
+  const float* S = sigma + blk * int64_t(D) * D;
+  const float* M = mu + blk * D;
+  uint8_t* out = prep + blk * Lay::BLOCK_BYTES;
+  const float half_beta = 0.5f * beta;
+  for (int w = threadIdx.x; w < Lay::NF * 64; w += blockDim.x) {
+    const int f = w / 64, lane = w % 64, m = lane % 32, h = lane / 32;
+    int mt = 0;
+    while ((mt + 1) * (mt + 2) <= f) ++mt;
+    const int s = f - mt * (mt + 1);
+    const int j = 32 * mt + m;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = frag_k(s, h, e);
+      const float sij = S[i * D + j];
+      x[e] = i < j ? beta * sij : (i == j ? half_beta * sij : 0.f);
+    }
+    if constexpr (F32) {
+      floatx8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = x[e];
+      *reinterpret_cast<floatx8*>(out + f * kFragBytes + lane * 32) = v;
+    } else {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const u16 h0 = f32_to_bf16_bits(x[e]), h1 = f32_to_bf16_bits(x[e + 1]);
+        const u16 l0 = f32_to_bf16_bits(x[e] - bf16_bits_to_f32(h0));
+        const u16 l1 = f32_to_bf16_bits(x[e + 1] - bf16_bits_to_f32(h1));
+        hi[e / 2] = uint32_t(h0) | (uint32_t(h1) << 16);
+        lo[e / 2] = uint32_t(l0) | (uint32_t(l1) << 16);
+      }
+      *reinterpret_cast<u32x4*>(out + f * kFragBytes + lane * 16) = hi;
+      *reinterpret_cast<u32x4*>(out + f * kFragBytes + 1024 + lane * 16) = lo;
+    }
+  }
+  for (int w = threadIdx.x; w < 2 * Lay::MT * 16; w += blockDim.x) {
+    const int h = w / (Lay::MT * 16), mt = (w / 16) % Lay::MT, i = w % 16;
+    reinterpret_cast<float*>(out + Lay::MU_OFF)[w] = M[32 * mt + 8 * (i / 4) + 4 * h + (i % 4)];
+  }
+}
+
+template <bool F32>
+struct QFrag;
+template <>
+struct QFrag<false> {
+  using T = bf16x8;
+  using In = bf16_t;
+  __device__ static float elem(const T& v, int e) { return static_cast<float>(v[e]); }
+};
+template <>
+struct QFrag<true> {
+  using T = floatx8;
+  using In = float;
+  __device__ static float elem(const T& v, int e) { return v[e]; }
+};
+
+// Load the B-operand fragment of chunk s for one query row (lane half h).
+template <bool F32>
+__device__ __forceinline__ typename QFrag<F32>::T load_q_frag(const typename QFrag<F32>::In* row,
+                                                              int s, int h, bool valid) {
+  typename QFrag<F32>::T v;
+  if constexpr (F32) {
+    floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+    if (valid) {
+      a = *reinterpret_cast<const floatx4*>(row + 16 * s + 4 * h);
+      b = *reinterpret_cast<const floatx4*>(row + 16 * s + 8 + 4 * h);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[e + 4] = b[e];
+    }
+  } else {
+    u32x2 a = {0u, 0u}, b = a;
+    if (valid) {
+      a = *reinterpret_cast<const u32x2*>(row + 16 * s + 4 * h);
+      b = *reinterpret_cast<const u32x2*>(row + 16 * s + 8 + 4 * h);
+    }
+    u32x4 w = {a[0], a[1], b[0], b[1]};
+    v = __builtin_bit_cast(bf16x8, w);
+  }
+  return v;
+}
+
+template <bool F32, int D, int KMAX>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
+    const typename QFrag<F32>::In* __restrict__ Q, const uint8_t* __restrict__ prep,
+    int32_t* __restrict__ idx, float* __restrict__ kth, int64_t n, int g, int hq, int hkv,
+    int B, int64_t nb, int k, int64_t n_tiles, int64_t n_bkv) {
+  using Lay = RouteLayout<D>;
+  using QT = typename QFrag<F32>::T;
+  constexpr int MT = Lay::MT, NS = Lay::NS, BYTES = Lay::BLOCK_BYTES;
+  constexpr int N16 = BYTES / 16;
+  constexpr int PER_T = (N16 + kRouteThreads - 1) / kRouteThreads;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int64_t wid = blockIdx.x;
+  const int64_t bkv = wid % n_bkv;
+  const int64_t tile = n_tiles - 1 - wid / n_bkv;
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  const int64_t rows_total = n * g;
+  const int64_t rho0 = tile * kRouteRows;
+
+  // query fragments of this lane's two 32-row tiles
+  QT bq[2][NS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t rho = rho0 + 64 * wave + 32 * nt + ln;
+    const bool valid = rho < rows_total;
+    const int64_t t = valid ? rho / g : 0, jg = valid ? rho % g : 0;
+    const auto* row = Q + (((b * hq + kv * g + jg) * n) + t) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) bq[nt][s] = load_q_frag<F32>(row, s, h, valid);
+  }
+  // the row this lane scores and ranks
+  const int64_t my_rho = rho0 + 64 * wave + 32 * h + ln;
+  const bool my_valid = my_rho < rows_total;
+  const int64_t my_t = my_valid ? my_rho / g : 0;
+  const int64_t my_C = my_valid ? min(nb, (my_t + 1) / B) : 0;
+  const int64_t t_max = min(n - 1, (rho0 + kRouteRows - 1) / g);
+  const int64_t C_wg = min(nb, (t_max + 1) / B);
+
+  float ls[KMAX + 1];
+  int li[KMAX + 1];
+#pragma unroll
+  for (int i = 0; i <= KMAX; ++i) {
+    ls[i] = -__builtin_inff();
+    li[i] = -1;
+  }
+
+  const uint8_t* src_base = prep + bkv * nb * int64_t(BYTES);
+  u32x4 stage[PER_T];
+  auto load_stage = [&](int64_t c) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(src_base + c * BYTES);
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int w = tid + i * kRouteThreads;
+      if (w < N16) stage[i] = __builtin_nontemporal_load(src + w);
+    }
+  };
+  auto store_stage = [&](int buf) {
+    u32x4* dst = reinterpret_cast<u32x4*>(lds + buf * BYTES);
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int w = tid + i * kRouteThreads;
+      if (w < N16) dst[w] = stage[i];
+    }
+  };
+
+  if (C_wg > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+
+  for (int64_t c = 0; c < C_wg; ++c) {
+    const bool more = c + 1 < C_wg;
+    if (more) load_stage(c + 1);
+    const uint8_t* L = lds + (c & 1) * BYTES;
+
+    floatx16 acc[2][MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const floatx16 m = *reinterpret_cast<const floatx16*>(L + Lay::MU_OFF + (h * MT + mt) * 64);
+      acc[0][mt] = m;
+      acc[1][mt] = m;
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int s = 0; s <= 2 * mt + 1; ++s) {
+        const uint8_t* F = L + Lay::frag(mt, s) * kFragBytes;
+        if constexpr (F32) {
+          const floatx8 a = *reinterpret_cast<const floatx8*>(F + lane * 32);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma16(a, bq[nt][s], acc[nt][mt]);
+        } else {
+          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(F + lane * 16);
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(F + 1024 + lane * 16);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            acc[nt][mt] = mma16(ahi, bq[nt][s], acc[nt][mt]);
+            acc[nt][mt] = mma16(alo, bq[nt][s], acc[nt][mt]);
+          }
+        }
+      }
+    }
+    // row-dot: lane (ln, h) holds P_j + mu_j for j = 32mt + 8a + 4h + b of both tiles
+    float part[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+            sacc = fmaf(acc[nt][mt][4 * a + bb],
+                        QFrag<F32>::elem(bq[nt][2 * mt + (a >> 1)], 4 * (a & 1) + bb), sacc);
+      part[nt] = sacc + wave_shfl_xor(sacc, 32);
+    }
+    if (more) store_stage((c + 1) & 1);
+
+    float sc = h ? part[1] : part[0];
+    if (c < my_C && sc > ls[KMAX]) {
+      int ci = int(c);
+#pragma unroll
+      for (int i = 0; i <= KMAX; ++i) {
+        const bool gt = sc > ls[i];
+        const float ts = ls[i];
+        const int ti = li[i];
+        ls[i] = gt ? sc : ts;
+        li[i] = gt ? ci : ti;
+        sc = gt ? ts : sc;
+        ci = gt ? ti : ci;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!my_valid) return;
+  const int64_t jg = my_rho % g;
+  const int64_t orow = (b * hq + kv * g + jg) * n + my_t;
+  if (k > 0) {
+    int32_t* out = idx + orow * k;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if (i < k) {
+        // ascending block index, -1 (absent) last; equal keys (only -1) keep slot order
+        const unsigned key_i = unsigned(li[i]);
+        int rank = 0;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (j < k) {
+            const unsigned key_j = unsigned(li[j]);
+            rank += (key_j < key_i || (key_j == key_i && j < i)) ? 1 : 0;
+          }
+        out[rank] = li[i];
+      }
+    }
+  }
+  if (kth != nullptr) {
+    float r_k = -__builtin_inff(), r_k1 = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i <= KMAX; ++i) {
+      if (i == k - 1) r_k = ls[i];
+      if (i == k) r_k1 = ls[i];
+    }
+    kth[orow * 2] = r_k;
+    kth[orow * 2 + 1] = r_k1;
+  }
+}
+
+template <bool F32, int D, int KMAX>
+hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const float* sigma,
+                          int32_t* idx, float* kth, void* ws, hipStream_t st) {
+  using Lay = RouteLayout<D>;
+  const int64_t n_bkv = int64_t(s.b) * s.hkv;
+  uint8_t* prep = static_cast<uint8_t*>(ws);
+  if (s.nb > 0) {
+    hipLaunchKernelGGL((route_prep_kernel<F32, D>), dim3(unsigned(s.nb), unsigned(n_bkv)),
+                       dim3(256), 0, st, mu, sigma, prep, s.nb, s.beta);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n_tiles = (s.n * s.g + kRouteRows - 1) / kRouteRows;
+  const size_t shmem = 2 * size_t(Lay::BLOCK_BYTES);
+  auto kern = route_topk_kernel<F32, D, KMAX>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
+  if (e != hipSuccess) return e;
+  using In = typename QFrag<F32>::In;
+  hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles * n_bkv)), dim3(kRouteThreads), shmem, st,
+                     static_cast<const In*>(Q), prep, idx, kth, s.n, s.g, s.hq, s.hkv, s.B, s.nb,
+                     s.k, n_tiles, n_bkv);
+  return hipGetLastError();
+}
+
+template <bool F32, int D>
+hipError_t launch_route_d(const Shape& s, const void* Q, const float* mu, const float* sigma,
+                          int32_t* idx, float* kth, void* ws, hipStream_t st) {
+  if (s.k <= 8) return launch_route_t<F32, D, 8>(s, Q, mu, sigma, idx, kth, ws, st);
+  if (s.k <= 16) return launch_route_t<F32, D, 16>(s, Q, mu, sigma, idx, kth, ws, st);
+  return launch_route_t<F32, D, 32>(s, Q, mu, sigma, idx, kth, ws, st);
+}
+
+}  // namespace
+
+size_t route_workspace_bytes(const Shape& s) {
+  const size_t per = s.d == 64 ? RouteLayout<64>::BLOCK_BYTES : RouteLayout<128>::BLOCK_BYTES;
+  return align_up(size_t(s.b) * s.hkv * size_t(s.nb) * per);
+}
+
+hipError_t launch_route_topk(const Shape& s, const void* Q, const float* mu, const float* sigma,
+                             int32_t* idx, float* kth, void* ws, hipStream_t st) {
+  if (s.in_bf16)
+    return s.d == 64 ? launch_route_d<false, 64>(s, Q, mu, sigma, idx, kth, ws, st)
+                     : launch_route_d<false, 128>(s, Q, mu, sigma, idx, kth, ws, st);
+  return s.d == 64 ? launch_route_d<true, 64>(s, Q, mu, sigma, idx, kth, ws, st)
+                   : launch_route_d<true, 128>(s, Q, mu, sigma, idx, kth, ws, st);
+}
+
+}  // namespace ssa

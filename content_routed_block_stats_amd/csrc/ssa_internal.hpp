@@ -1,0 +1,47 @@
+// Host-side contract between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssa {
+
+// Validated shapes and parameters of one call (see include/ssa.h).
+struct Shape {
+  int b, hq, hkv, g, d;
+  int64_t n;      // prefill length, or decode cache capacity
+  int B, k, W;
+  int64_t nb;     // complete blocks of n (stat slots per (sequence, KV head))
+  float beta, scale;
+  bool in_bf16, out_bf16;
+};
+
+constexpr size_t kWsAlign = 256;
+inline size_t align_up(size_t x, size_t a = kWsAlign) { return (x + a - 1) / a * a; }
+
+// block statistics.  cache_len == nullptr: every block c < s.nb of every
+// (sequence, KV head), keys read from K [b, hkv, s.n, d].  Otherwise decode
+// mode: only the block completed by the key at position cache_len[b]
+// (if any), with K the caches [b, hkv, s.n, d].
+hipError_t launch_block_stats(const Shape& s, const void* K, float* mu, float* sigma,
+                              const int32_t* cache_len, hipStream_t st);
+
+// routing + top-k (prefill)
+size_t route_workspace_bytes(const Shape& s);
+hipError_t launch_route_topk(const Shape& s, const void* Q, const float* mu, const float* sigma,
+                             int32_t* idx, float* kth, void* ws, hipStream_t st);
+
+// sparse attention (prefill)
+size_t attn_workspace_bytes(const Shape& s);
+hipError_t launch_sparse_attn(const Shape& s, const void* Q, const void* K, const void* V,
+                              const int32_t* idx, void* O, float* lse, void* ws, hipStream_t st);
+
+// decode step
+size_t decode_workspace_bytes(const Shape& s);
+hipError_t launch_decode_step(const Shape& s, const void* q, const void* k_new, const void* v_new,
+                              void* K_cache, void* V_cache, int32_t* cache_len, float* mu,
+                              float* sigma, int32_t* idx, void* o, float* lse, void* ws,
+                              hipStream_t st);
+
+}  // namespace ssa

@@ -1,0 +1,177 @@
+/*
+ * ssa.h -- C ABI of the MI355X (gfx950) hot path of Subquadratic Sparse
+ * Attention (SSA), content-routed block statistics.
+ *
+ * The method (write-up "Subquadratic Sparse Attention (SSA)",
+ * git.hmmc.top/jonsmirl/ssa, introduction paragraph, steps i-iii, and section
+ * "The idea in one screen"): for each query, route to a small set of key
+ * blocks using only per-block summary statistics, scored by the
+ * second-cumulant score r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q; keep the
+ * top-k blocks under causal masking; add a local window; compute exact
+ * softmax attention over the selected keys.
+ *
+ * Conventions shared by every call
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous
+ *    row-major in the layout stated at each call, aligned to 16 bytes.  The
+ *    library never allocates, frees or retains device memory; scratch space
+ *    is the caller's workspace.  It keeps no global mutable state, so calls
+ *    on different streams may run concurrently.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns; results are ready when the stream is.
+ *  - Validation is synchronous and on the host, before anything is enqueued:
+ *    on an error nothing is launched and a status other than SSA_OK is
+ *    returned; ssa_last_error() then holds a message (per thread).  A launch
+ *    failure reported by the runtime returns SSA_ERR_HIP.  Faults inside a
+ *    kernel surface at the caller's next synchronisation.  No C++ exception
+ *    crosses this interface.
+ *  - Row r of a tensor [b, H, n, x] is (sequence, head, position).  q-head h
+ *    reads KV head h / (n_q_heads / n_kv_heads) (contiguous groups).
+ *  - Tokens: b = batch, Hq / Hkv = query / KV heads, n = seq_len, d = head_dim,
+ *    B = block_size, nb = n / B complete blocks, k = top_k, W = window.
+ */
+#ifndef SSA_MI355X_SSA_H
+#define SSA_MI355X_SSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssa_status {
+  SSA_OK = 0,
+  SSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, out-of-range size or parameter */
+  SSA_ERR_UNSUPPORTED = 2,        /* valid in principle, not built (e.g. d not in {64,128}) */
+  SSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  SSA_ERR_HIP = 4                 /* the HIP runtime reported an error */
+} ssa_status;
+
+typedef enum ssa_dtype { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
+
+typedef enum ssa_op {
+  SSA_OP_ROUTE = 1,   /* workspace of ssa_route_topk */
+  SSA_OP_ATTN = 2,    /* workspace of ssa_sparse_attn_fwd */
+  SSA_OP_DECODE = 3   /* workspace of ssa_decode_step */
+} ssa_op;
+
+/* Shapes and method parameters.  Limits checked by every call:
+ *   batch >= 1; n_kv_heads >= 1; n_q_heads a positive multiple of n_kv_heads;
+ *   head_dim in {64, 128};
+ *   seq_len >= 1 (prefill: n; decode: the cache capacity in tokens);
+ *   block_size a multiple of 64 in [64, 1024];
+ *   top_k in [0, 32];  window >= 1;
+ *   beta finite; scale finite and > 0;
+ *   in_dtype in {SSA_F32, SSA_BF16} (Q, K, V and caches);
+ *   out_dtype in {SSA_F32, SSA_BF16} (O). */
+typedef struct ssa_params {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int64_t seq_len;
+  int32_t block_size;
+  int32_t top_k;
+  int32_t window;
+  float beta;    /* routing inverse temperature on raw q (the write-up tunes ~2) */
+  float scale;   /* softmax scale on raw logits, normally the float32 of 1/sqrt(d) */
+  int32_t in_dtype;
+  int32_t out_dtype;
+} ssa_params;
+
+/* Per-block statistics (write-up, "The idea in one screen": the block mean
+ * mu_c and covariance Sigma_c, whose quadratic form is the variance of the
+ * logit across the block).  For every complete block c < nb of every
+ * (sequence, KV head):
+ *   mu_c    = (1/B) sum_j k_j
+ *   Sigma_c = (1/B) sum_j (k_j - mu_c)(k_j - mu_c)^T   (population covariance)
+ * accumulated in float32.
+ *   K     [b, Hkv, n, d]      in_dtype
+ *   mu    [b, Hkv, nb, d]     float32, written
+ *   sigma [b, Hkv, nb, d, d]  float32, written (full symmetric matrix)
+ * A trailing partial block is ignored. */
+ssa_status ssa_block_stats(const ssa_params* p, const void* K, float* mu, float* sigma,
+                           void* stream);
+
+/* Bytes of workspace an operation needs for these parameters (0 is valid). */
+ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes);
+
+/* Routing and top-k (write-up, introduction step i, and the routing score of
+ * "The idea in one screen").  For every query row (b, h, t) the routable
+ * blocks are the complete blocks c with (c+1)B-1 <= t; each gets
+ *   r_c = <q, mu_c> + (beta/2) q^T Sigma_c q      (raw q, KV head of h)
+ * and the min(k, #routable) highest scores are kept, ties to the lower c.
+ *   Q          [b, Hq, n, d]   in_dtype
+ *   mu, sigma  as written by ssa_block_stats
+ *   idx        [b, Hq, n, k]   int32, written: selected block indices in
+ *                              ascending order, padded with -1
+ *   kth        [b, Hq, n, 2]   float32, written if not NULL: the k-th and
+ *                              (k+1)-th largest scores (-inf where absent)
+ *   workspace  >= ssa_workspace_size(p, SSA_OP_ROUTE) bytes of device memory
+ * The scores are evaluated on MFMA in bfloat16 with float32 accumulation,
+ * Sigma split into a high and a low bfloat16 part (float32 MFMA for
+ * float32 inputs), so a selection can differ from an exact one only where
+ * two scores are within a few 1e-6 relative of each other. */
+ssa_status ssa_route_topk(const ssa_params* p, const void* Q, const float* mu,
+                          const float* sigma, int32_t* idx, float* kth, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Sparse attention forward (write-up, introduction steps ii-iii).  For every
+ * query row (b, h, t):
+ *   S(t) = union of the keys of the blocks in idx(b,h,t) (entries < 0 are
+ *          ignored) and the window [max(0, t-W+1), t], each key once;
+ *   s_j  = scale * q.k_j for j in S(t);
+ *   O    = sum_j softmax(s)_j v_j,   LSE = ln sum_j exp(s_j).
+ *   Q    [b, Hq, n, d] in_dtype;  K, V [b, Hkv, n, d] in_dtype
+ *   idx  [b, Hq, n, k] int32 as written by ssa_route_topk: every entry is -1
+ *        or a complete block routable for t, entries distinct and ascending
+ *        (other contents are undefined behaviour)
+ *   O    [b, Hq, n, d] out_dtype, written;  lse [b, Hq, n] float32, written
+ *   workspace >= ssa_workspace_size(p, SSA_OP_ATTN) bytes
+ * Arithmetic: MFMA products with float32 accumulation and an online softmax
+ * in float32. */
+ssa_status ssa_sparse_attn_fwd(const ssa_params* p, const void* Q, const void* K,
+                               const void* V, const int32_t* idx, void* O, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step per sequence (write-up, module table: the decode path routes
+ * and attends one new query per step against the cache).  With
+ * L = cache_len[b] tokens already cached, for every sequence b:
+ *   1. writes k_new, v_new at position L of the caches;
+ *   2. if (L+1) % B == 0, writes mu/sigma of the block (L+1)/B - 1 just completed;
+ *   3. for every q-head, routes over the complete blocks c < (L+1)/B, keeps
+ *      the top k, and attends over the selected blocks and the window
+ *      [max(0, L-W+1), L] exactly as ssa_route_topk + ssa_sparse_attn_fwd
+ *      would for query position t = L;
+ *   4. increments cache_len[b].
+ * p->seq_len is the cache capacity C (tokens); the caller guarantees
+ * cache_len[b] < C (not checked on the device).
+ *   q        [b, Hq, d] in_dtype;  k_new, v_new [b, Hkv, d] in_dtype
+ *   K_cache, V_cache [b, Hkv, C, d] in_dtype (read and written)
+ *   cache_len [b] int32 on the device (read and incremented)
+ *   mu [b, Hkv, C/B, d], sigma [b, Hkv, C/B, d, d] float32 (read, and written
+ *      for a completed block); entries of complete blocks must hold the
+ *      statistics ssa_block_stats would write
+ *   idx [b, Hq, k] int32, written if not NULL (as ssa_route_topk)
+ *   o [b, Hq, d] out_dtype, written;  lse [b, Hq] float32, written
+ *   workspace >= ssa_workspace_size(p, SSA_OP_DECODE) bytes
+ * Routing here reads sigma in float32 on the vector units. */
+ssa_status ssa_decode_step(const ssa_params* p, const void* q, const void* k_new,
+                           const void* v_new, void* K_cache, void* V_cache, int32_t* cache_len,
+                           float* mu, float* sigma, int32_t* idx, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* ssa_status_string(ssa_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* ssa_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t ssa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_MI355X_SSA_H */

@@ -1,0 +1,101 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+include/ssa.h declares, and rejects invalid arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import content_routed_block_stats_amd as ssa
+from content_routed_block_stats_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssa.lib()
+    names = _declared_functions()
+    assert {"ssa_block_stats", "ssa_route_topk", "ssa_sparse_attn_fwd", "ssa_decode_step"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in ssa.h but not exported"
+    assert lib.ssa_version() >= 100
+
+
+def test_params_struct_matches_header_layout():
+    # int32 x4, int64, int32 x3, float x2, int32 x2 with natural alignment
+    assert ctypes.sizeof(B.SSAParams) == 56
+    assert B.SSAParams.seq_len.offset == 16 and B.SSAParams.beta.offset == 36
+
+
+def _p(**kw):
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, seq_len=4096, block_size=128,
+                top_k=8, window=128, beta=2.0)
+    base.update(kw)
+    return B.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), B.SSA_ERR_UNSUPPORTED),
+    (dict(n_q_heads=3), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(block_size=48), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(block_size=2048), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(top_k=33), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(top_k=-1), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(window=0), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=0), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(beta=float("nan")), B.SSA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), B.SSA_ERR_INVALID_ARGUMENT),
+])
+def test_invalid_params_rejected_on_host(kw, status):
+    p = _p(**kw)
+    n = ctypes.c_size_t(0)
+    got = ssa.lib().ssa_workspace_size(ctypes.byref(p), B.SSA_OP_ATTN, ctypes.byref(n))
+    assert got == status, B.status_string(got)
+    assert ssa.lib().ssa_last_error().decode() != ""
+    # the compute entry points reject the same parameters before any launch
+    got = ssa.lib().ssa_block_stats(ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20, None)
+    assert got == status
+
+
+def test_null_pointers_and_workspace_checked_on_host():
+    p = _p()
+    L = ssa.lib()
+    assert L.ssa_block_stats(None, 1, 1, 1, None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert L.ssa_block_stats(ctypes.byref(p), None, 1, 1, None) == B.SSA_ERR_INVALID_ARGUMENT
+    need = B.ssa_workspace_size(p, B.SSA_OP_ROUTE)
+    assert need > 0
+    got = L.ssa_route_topk(ctypes.byref(p), 256, 256, 256, 256, None, 256, need - 1, None)
+    assert got == B.SSA_ERR_WORKSPACE_TOO_SMALL
+    got = L.ssa_route_topk(ctypes.byref(p), 256, 256, 256, 256, None, 128, need, None)
+    assert got == B.SSA_ERR_INVALID_ARGUMENT          # workspace not 256-byte aligned
+    need_a = B.ssa_workspace_size(p, B.SSA_OP_ATTN)
+    got = L.ssa_sparse_attn_fwd(ctypes.byref(p), 256, 256, 256, None, 256, 256, 256, need_a, None)
+    assert got == B.SSA_ERR_INVALID_ARGUMENT          # idx NULL with top_k > 0
+    need_d = B.ssa_workspace_size(p, B.SSA_OP_DECODE)
+    got = L.ssa_decode_step(ctypes.byref(p), 256, 256, 256, 256, 256, None, 256, 256, None, 256,
+                            256, 256, need_d, None)
+    assert got == B.SSA_ERR_INVALID_ARGUMENT          # cache_len NULL
+    assert L.ssa_workspace_size(ctypes.byref(p), 99, ctypes.byref(ctypes.c_size_t())) == \
+        B.SSA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes_scale_with_problem():
+    small = B.ssa_workspace_size(_p(seq_len=4096), B.SSA_OP_ATTN)
+    big = B.ssa_workspace_size(_p(seq_len=8192), B.SSA_OP_ATTN)
+    assert big > small > 0
+    assert B.ssa_workspace_size(_p(top_k=0), B.SSA_OP_ATTN) < small
+    # decode workspace: scores, selections and per-(row, item) partials
+    assert B.ssa_workspace_size(_p(), B.SSA_OP_DECODE) > 0
+
+
+def test_status_strings():
+    for code in range(5):
+        assert B.status_string(code).startswith("SSA_")
