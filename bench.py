@@ -1,0 +1,301 @@
+#!/usr/bin/env python
+"""Throughput of the SSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the prefill hot path over one batch of seeded synthetic
+input already resident in HBM: ssa_block_stats -> ssa_route_topk ->
+ssa_sparse_attn_fwd.  The default workload is the n = 131072 GQA prefill
+(32 q-heads / 8 KV heads, d = 128, bf16, B = 256, k = 16, W = 256, beta = 2).
+Prints ONE JSON line: query-tokens/s, per-stage times from HIP events on the
+launch stream, the routing kernel against the bf16 MFMA roofline, the gather
+against the HBM roofline, a decode step on the 32 x 256K-token cache, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def route_flops(wl) -> float:
+    """Algorithmic routing flops: (2d^2 + 4d) per (query row, routable block)."""
+    n, B, d = wl.seq_len, wl.block, wl.head_dim
+    nb = n // B
+    # sum over t of min(nb, floor((t+1)/B)), in closed form
+    pairs_per_head = B * nb * (nb - 1) // 2 + (n - nb * B + 1) * nb
+    return float(wl.batch * wl.n_q_heads * pairs_per_head) * (2 * d * d + 4 * d)
+
+
+def gather_bytes(wl) -> float:
+    """Algorithmic HBM bytes of ssa_sparse_attn_fwd with block-major dispatch.
+
+    Per selected (row, block): the query row (2d bytes, bf16) read by the
+    block's task, the fp16 partial written and read back (2 * (2d + 8)), the
+    idx entry read twice by the dispatch (8) and its sorted entry written and
+    read (8).  Per row: the query row for the window pass (2d), the idx row
+    (4k), O written (2d) and LSE (4).  Per (sequence, KV head): K and V read
+    once for the blocks and once for the windows (4 * n * d * 2).
+    """
+    n, B, d, k = wl.seq_len, wl.block, wl.head_dim, wl.top_k
+    nb = n // B
+    sel_per_head = sum(min(k, min(nb, (t + 1) // B)) for t in range(n))
+    rows = wl.batch * wl.n_q_heads * n
+    sel = wl.batch * wl.n_q_heads * sel_per_head
+    per_sel = 2 * d + 2 * (2 * d + 8) + 8 + 8
+    per_row = 2 * d + 4 * k + 2 * d + 4
+    kv = wl.batch * wl.n_kv_heads * 4 * n * d * 2
+    return float(sel * per_sel + rows * per_row + kv)
+
+
+def kernel_source_digest(*names: str) -> str:
+    h = hashlib.sha256()
+    for nm in names:
+        with open(os.path.join(ROOT, "content_routed_block_stats_amd", "csrc", nm), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None."""
+    path = os.path.join(PROFILES, f"{kernel}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != digest:
+        return None          # the kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, data, seconds: float) -> dict:
+    """Time the CPU oracle on a bounded sample of the workload (one thread)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    p = O.Params(wl.block, wl.top_k, wl.window, wl.beta, wl.scale)
+    rng = np.random.default_rng(0)
+    kv = 0
+    g = wl.group
+    Kh = O.as_f64(data["K"][0, kv].cpu())
+    Vh = O.as_f64(data["V"][0, kv].cpu())
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        mu, sigma = O.block_stats(Kh, wl.block)
+        t_stats = time.perf_counter() - t0
+        rows = 0
+        t_rows = 0.0
+        while t_rows < seconds and rows < 4096:
+            t = int(rng.integers(0, wl.seq_len))
+            h = kv * g + int(rng.integers(0, g))
+            q = O.as_f64(data["Q"][0, h, t].cpu())
+            t1 = time.perf_counter()
+            O.prefill_row(q, Kh, Vh, mu, sigma, p, t)
+            t_rows += time.perf_counter() - t1
+            rows += 1
+    per_row = t_rows / rows
+    total = wl.batch * wl.n_kv_heads * t_stats + wl.batch * wl.n_q_heads * wl.seq_len * per_row
+    return {
+        "value": wl.batch * wl.seq_len / total,
+        "unit": "query-tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"block statistics of 1 of {wl.batch * wl.n_kv_heads} KV heads "
+                   f"({t_stats:.2f} s) + {rows} query rows at uniform positions "
+                   f"({t_rows:.2f} s, {per_row * 1e3:.2f} ms/row), NumPy float64 on one "
+                   f"thread of {platform.processor() or platform.machine()}; full-job time "
+                   f"extrapolated to {total:.0f} s"),
+    }
+
+
+def bench_decode(steps: int, warmup: int) -> dict:
+    """ssa_decode_step on the 32-sequence x 262144-token cache workload."""
+    import torch
+
+    import content_routed_block_stats_amd as ssa
+    from synth_inputs import CONFIGS, make_decode
+
+    wl = CONFIGS["decode_256k"]
+    L = wl.seq_len
+    cap = L + 1024
+    data = make_decode(wl, seed=0, device="cuda", capacity=cap)
+    Kc, Vc = data["K_cache"], data["V_cache"]
+    mu, sigma = ssa.ssa_block_stats(Kc, wl.block)
+    cache_len = torch.full((wl.batch,), L, dtype=torch.int32, device="cuda")
+    q, kn, vn = data["q"], data["k_new"], data["v_new"]
+    p = ssa.make_params(batch=wl.batch, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                        head_dim=wl.head_dim, seq_len=cap, block_size=wl.block, top_k=wl.top_k,
+                        window=wl.window, beta=wl.beta, scale=wl.scale, in_dtype=q.dtype)
+    ws = torch.empty(ssa.ssa_workspace_size(p, 3), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ssa.ssa_decode_step(q, kn, vn, Kc, Vc, cache_len, mu, sigma, block_size=wl.block,
+                            top_k=wl.top_k, window=wl.window, beta=wl.beta, scale=wl.scale,
+                            workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # HBM bytes a step must read: Sigma upper 32x32 tiles (10 of 16 at d=128) and mu of
+    # every complete block, plus K and V of the selected blocks and the window
+    nbc = (L + 1) // wl.block
+    d = wl.head_dim
+    tiles = (d // 32) * (d // 32 + 1) // 2
+    sig = wl.batch * wl.n_kv_heads * nbc * (tiles * 32 * 32 * 4 + d * 4)
+    gat = wl.batch * wl.n_q_heads * (wl.top_k * wl.block + wl.window) * d * 2 * 2
+    del data
+    return {"workload": wl.name, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
+            "hbm_gbs_algorithmic": round((sig + gat) / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round((sig + gat) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "steps": steps}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa_prefill_128k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by independent KV heads and sequences, see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import content_routed_block_stats_amd as ssa
+    from synth_inputs import CONFIGS, make_prefill
+
+    wl = CONFIGS[args.workload]
+    if wl.decode:
+        print("choose a prefill workload", file=sys.stderr)
+        return 2
+    dev = "cuda"
+    print(f"[bench] generating {wl.name} on {torch.cuda.get_device_name(0)}", file=sys.stderr,
+          flush=True)
+    data = make_prefill(wl, seed=args.seed, device=dev)
+    Q, K, V = data["Q"], data["K"], data["V"]
+    b, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    nb = n // wl.block
+    mu = torch.empty((b, hkv, nb, d), dtype=torch.float32, device=dev)
+    sigma = torch.empty((b, hkv, nb, d, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((b, hq, n, wl.top_k), dtype=torch.int32, device=dev)
+    O = torch.empty((b, hq, n, d), dtype=Q.dtype, device=dev)
+    lse = torch.empty((b, hq, n), dtype=torch.float32, device=dev)
+    p = ssa.make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=n,
+                        block_size=wl.block, top_k=wl.top_k, window=wl.window, beta=wl.beta,
+                        scale=wl.scale, in_dtype=Q.dtype)
+    ws_r = torch.empty(ssa.ssa_workspace_size(p, 1), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(ssa.ssa_workspace_size(p, 2), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        ssa.ssa_block_stats(K, wl.block, mu=mu, sigma=sigma)
+        if ev:
+            ev[1].record()
+        ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta,
+                           idx=idx, workspace=ws_r)
+        if ev:
+            ev[2].record()
+        ssa.ssa_sparse_attn_fwd(Q, K, V, idx, block_size=wl.block, window=wl.window,
+                                scale=wl.scale, out=O, lse=lse, workspace=ws_a)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    st = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
+    t_stats, t_route, t_attn = st
+
+    rf = route_flops(wl)
+    achieved = rf / (t_route * 1e-3) / 1e12
+    gb = gather_bytes(wl)
+    gbs = gb / (t_attn * 1e-3) / 1e9
+    route_digest = kernel_source_digest("route_topk.hip", "ssa_common.hpp")
+    attn_digest = kernel_source_digest("sparse_attn.hip", "ssa_common.hpp")
+    tokens = b * n
+    res = {
+        "metric": "SSA prefill query-tokens/s at n=128K + % of MFMA/HBM roofline",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": b, "q_heads": hq, "kv_heads": hkv,
+                   "seq_len": n, "head_dim": d, "block": wl.block, "top_k": wl.top_k,
+                   "window": wl.window, "beta": wl.beta, "seed": args.seed},
+        "stages_ms": {"block_stats": round(t_stats, 4), "route_topk": round(t_route, 4),
+                      "sparse_attn_fwd": round(t_attn, 4)},
+        "roofline": {"kernel": "route_topk", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": counted_traffic("route_topk", route_digest),
+                     "algorithmic_flops_per_launch": rf},
+        "roofline_gather": {"kernel": "sparse_attn_fwd", "bound": "hbm", "achieved": round(gbs, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "traffic": counted_traffic("sparse_attn_fwd", attn_digest),
+                            "algorithmic_bytes_per_launch": gb},
+    }
+    del O, lse, ws_a, ws_r
+    if not args.no_decode:
+        print("[bench] decode step", file=sys.stderr, flush=True)
+        res["decode"] = bench_decode(steps=max(5, args.steps), warmup=2)
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

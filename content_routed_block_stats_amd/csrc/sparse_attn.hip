@@ -36,7 +36,8 @@ namespace ssa {
 namespace {
 
 constexpr int kAttnThreads = 256;          // 4 waves, 32 query rows each
-constexpr int kTaskRows = 128;             // rows per block-attention task
+constexpr int kTaskTiles = 1;              // 32-row MFMA tiles per wave in a task
+constexpr int kTaskRows = 4 * 32 * kTaskTiles;   // rows per block-attention task
 constexpr int kWinRows = 128;              // rows per window/merge tile
 constexpr int kKeyChunk = 64;              // keys per LDS chunk
 constexpr int kHistTokens = 2048;          // tokens per dispatch workgroup
@@ -47,8 +48,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 template <bool F32, int D>
 struct AT {
   using In = typename std::conditional<F32, float, bf16_t>::type;
-  using Frag = typename std::conditional<F32, floatx8, bf16x8>::type;
+  using Frag = typename std::conditional<F32, floatx8, bf16x8>::type;    // Q, K operands
+  using VFrag = typename std::conditional<F32, floatx8, f16x8>::type;    // P, V operands
   static constexpr int ES = F32 ? 4 : 2;          // element bytes
+  static constexpr int LOG_NS = D == 128 ? 3 : 2;
   static constexpr int FRAG = 64 * 8 * ES;         // one operand fragment
   static constexpr int NS = D / 16;                // 16-wide chunks of d
   static constexpr int MTD = D / 32;               // 32-wide tiles of d
@@ -87,68 +90,133 @@ __device__ __forceinline__ typename AT<F32, D>::Frag load_row_frag(const typenam
   return v;
 }
 
-// Stage keys [key0, key0 + 64) of one head (rows >= n_keys read as zero) into
+// Keys [key0, key0 + 64) of one head (rows >= n_keys read as zero), staged in
 // LDS as MFMA A-operand fragments:
 //   K part: fragment (mt, s), lane (m, h), element e = K[key0 + 32mt + m][frag_k(s,h,e)]
 //   V part: fragment (mt, s), lane (m, h), element e = V[key0 + frag_k(s,h,e)][32mt + m]
-// Both are moved in 4-element pieces; V is transposed through registers in
-// 4-key x 4-column tiles.
+// K moves in 4-element pieces, assigned so that the 64 lanes of one LDS store
+// fill 512 contiguous bytes (no bank conflicts).  V is transposed through
+// registers in 4-key x 4-column tiles and, for bfloat16 inputs, converted to
+// float16 after scaling by an exact power of two (vscale) that keeps every
+// value of the head inside the float16 range: bf16 values then convert
+// exactly, so P V runs as one float16 MFMA with P carrying 11 fraction bits.
+// load() issues the global reads into registers and store() writes them to
+// LDS, so a chunk's reads are in flight while the previous chunk is computed.
 template <bool F32, int D>
-__device__ __forceinline__ void stage_chunk(uint8_t* lds, const typename AT<F32, D>::In* Kh,
-                                            const typename AT<F32, D>::In* Vh, int64_t key0,
-                                            int64_t n_keys, int tid) {
+struct ChunkRegs {
   using A = AT<F32, D>;
+  using In = typename A::In;
   using PieceT = typename std::conditional<F32, floatx4, u32x2>::type;
-  constexpr int PPR = D / 4;                 // pieces per key row
-  constexpr int KP = kKeyChunk * PPR;        // K pieces in the chunk
-  for (int w = tid; w < KP; w += kAttnThreads) {
-    const int r = w / PPR, p = w % PPR;
-    PieceT v = {};
-    if (key0 + r < n_keys) v = *reinterpret_cast<const PieceT*>(Kh + (key0 + r) * D + 4 * p);
-    const int mt = r / 32, m = r % 32, s = p / 4, h = p & 1, sel = (p >> 1) & 1;
-    *reinterpret_cast<PieceT*>(lds + (mt * A::NS + s) * A::FRAG + (h * 32 + m) * 8 * A::ES +
-                               sel * A::PIECE) = v;
+  static constexpr int KPT = kKeyChunk * (D / 4) / kAttnThreads;         // K pieces per thread
+  static constexpr int VPT = (kKeyChunk / 4) * (D / 4) / kAttnThreads;   // V tiles per thread
+  PieceT k[KPT];
+  PieceT v[VPT][4];
+
+  // piece w of the K chunk: lanes vary (m, sel) fastest, then h, s, mt
+  __device__ static __forceinline__ void kpiece(int w, int& mt, int& m, int& s, int& h, int& sel) {
+    m = w & 31;
+    sel = (w >> 5) & 1;
+    h = (w >> 6) & 1;
+    s = (w >> 7) & (A::NS - 1);
+    mt = w >> (7 + A::LOG_NS);
   }
-  constexpr int VT = (kKeyChunk / 4) * (D / 4);   // 4x4 tiles
-  uint8_t* vl = lds + A::KBYTES;
-  for (int w = tid; w < VT; w += kAttnThreads) {
-    const int kq = w / (D / 4), dq = w % (D / 4);
-    if constexpr (F32) {
-      floatx4 rows[4];
+
+  __device__ __forceinline__ void load(const In* Kh, const In* Vh, int64_t key0, int64_t n_keys,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      int mt, m, s, h, sel;
+      kpiece(tid + i * kAttnThreads, mt, m, s, h, sel);
+      const int r = 32 * mt + m;
+      k[i] = PieceT{};
+      if (key0 + r < n_keys)
+        k[i] = *reinterpret_cast<const PieceT*>(Kh + (key0 + r) * D + 16 * s + 8 * sel + 4 * h);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int w = tid + i * kAttnThreads, kq = w / (D / 4), dq = w % (D / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        rows[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+        v[i][r] = PieceT{};
         if (key0 + 4 * kq + r < n_keys)
-          rows[r] = *reinterpret_cast<const floatx4*>(Vh + (key0 + 4 * kq + r) * D + 4 * dq);
-      }
-      const int s = kq / 4, kg = kq % 4, sel = kg >> 1, h = kg & 1;
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        const int d = 4 * dq + dd, mt = d / 32, m = d % 32;
-        floatx4 col = {rows[0][dd], rows[1][dd], rows[2][dd], rows[3][dd]};
-        *reinterpret_cast<floatx4*>(vl + (mt * 4 + s) * A::FRAG + (h * 32 + m) * 8 * A::ES +
-                                    sel * A::PIECE) = col;
-      }
-    } else {
-      u32x2 rows[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rows[r] = u32x2{0u, 0u};
-        if (key0 + 4 * kq + r < n_keys)
-          rows[r] = *reinterpret_cast<const u32x2*>(Vh + (key0 + 4 * kq + r) * D + 4 * dq);
-      }
-      const int s = kq / 4, kg = kq % 4, sel = kg >> 1, h = kg & 1;
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        const int d = 4 * dq + dd, mt = d / 32, m = d % 32;
-        const int word = dd >> 1, shift = (dd & 1) * 16;
-        const uint32_t e0 = (rows[0][word] >> shift) & 0xFFFFu, e1 = (rows[1][word] >> shift) & 0xFFFFu;
-        const uint32_t e2 = (rows[2][word] >> shift) & 0xFFFFu, e3 = (rows[3][word] >> shift) & 0xFFFFu;
-        u32x2 col = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        *reinterpret_cast<u32x2*>(vl + (mt * 4 + s) * A::FRAG + (h * 32 + m) * 8 * A::ES +
-                                  sel * A::PIECE) = col;
+          v[i][r] = *reinterpret_cast<const PieceT*>(Vh + (key0 + 4 * kq + r) * D + 4 * dq);
       }
     }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* lds, int tid, float vscale) const {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      int mt, m, s, h, sel;
+      kpiece(tid + i * kAttnThreads, mt, m, s, h, sel);
+      *reinterpret_cast<PieceT*>(lds + (mt * A::NS + s) * A::FRAG + (h * 32 + m) * 8 * A::ES +
+                                 sel * A::PIECE) = k[i];
+    }
+    uint8_t* vl = lds + A::KBYTES;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int w = tid + i * kAttnThreads, kq = w / (D / 4), dq = w % (D / 4);
+      const int s = kq / 4, kg = kq % 4, sel = kg >> 1, h = kg & 1;
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        const int d = 4 * dq + dd, mt = d / 32, m = d % 32;
+        PieceT col;
+        if constexpr (F32) {
+          col = floatx4{v[i][0][dd], v[i][1][dd], v[i][2][dd], v[i][3][dd]};
+        } else {
+          const int word = dd >> 1, shift = (dd & 1) * 16;
+          uint32_t e[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = bf16_bits_to_f32((v[i][r][word] >> shift) & 0xFFFFu) * vscale;
+            e[r] = __builtin_bit_cast(u16, static_cast<_Float16>(x));
+          }
+          col = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+        }
+        *reinterpret_cast<PieceT*>(vl + (mt * 4 + s) * A::FRAG + (h * 32 + m) * 8 * A::ES +
+                                   sel * A::PIECE) = col;
+      }
+    }
+  }
+};
+
+// Power-of-two scale for the float16 value operand of one head: vexp_bits is
+// the largest |v| of the head as bfloat16 bits; returns e >= 0 with
+// max|v| * 2^-e < 2^15.
+__device__ __forceinline__ int value_exponent(uint32_t vmax_bits) {
+  const float vmax = bf16_bits_to_f32(vmax_bits & 0x7FFFu);
+  int E = 0;
+  if (vmax > 0.f) (void)frexpf(vmax, &E);   // vmax < 2^E
+  return E > 15 ? E - 15 : 0;
+}
+
+// Chunk images: every 64-key chunk of every head, already in the LDS layout
+// above (K fragments, then V transposed and, for bfloat16 inputs, converted to
+// float16).  Written once per call; the attention kernels then stage a chunk
+// with straight 16-byte global->LDS DMA loads, no registers and no transposes.
+template <bool F32, int D>
+__global__ __launch_bounds__(kAttnThreads) void kv_image_kernel(
+    const typename AT<F32, D>::In* __restrict__ K, const typename AT<F32, D>::In* __restrict__ V,
+    const uint32_t* __restrict__ vmax, uint8_t* __restrict__ img, int64_t n, int64_t n_chunks) {
+  using A = AT<F32, D>;
+  const int64_t ci = blockIdx.x, bkv = blockIdx.y;
+  const float vscale = F32 ? 1.f : ldexpf(1.f, -value_exponent(vmax[bkv]));
+  ChunkRegs<F32, D> cr;
+  cr.load(K + bkv * n * D, V + bkv * n * D, ci * kKeyChunk, n, threadIdx.x);
+  cr.store(img + (bkv * n_chunks + ci) * A::CHUNK, threadIdx.x, vscale);
+}
+
+// Copy one chunk image (A::CHUNK bytes) into LDS: each wave moves a quarter,
+// 1 KB per instruction, global -> LDS directly.
+template <bool F32, int D>
+__device__ __forceinline__ void stage_chunk_dma(uint8_t* lds, const uint8_t* src, int tid) {
+  constexpr int PER_WAVE = AT<F32, D>::CHUNK / (kAttnThreads / 64);
+  const int wave = tid / 64, lane = tid % 64;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE / 1024; ++i) {
+    const int off = wave * PER_WAVE + i * 1024;
+    __builtin_amdgcn_global_load_lds(src + off + lane * 16,
+                                     (__attribute__((address_space(3))) void*)(lds + off), 16, 0, 0);
   }
 }
 
@@ -170,81 +238,163 @@ __device__ __forceinline__ void row_state_init(RowState<D>& st) {
   st.l = 0.f;
 }
 
-// One 64-key chunk for the 32 rows of this wave.  mask(mt, a, b) says whether
-// key 32mt + 8a + 4h + b of the chunk counts for this lane's row.
-template <bool F32, int D, typename Mask>
+// One 64-key chunk for the NT 32-row tiles of this wave; every fragment read
+// from LDS feeds NT MFMAs.  mask(nt, mt, a, b) says whether key
+// 32mt + 8a + 4h + b of the chunk counts for this lane's row of tile nt.
+// Probabilities are exp2(s * scale2 - m) with the running row max m in the
+// same base-2 units; for bfloat16 inputs they enter P V as float16.
+template <bool F32, int D, int NT, typename Mask>
 __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
-                                             const typename AT<F32, D>::Frag (&bq)[D / 16],
-                                             float scale2, int lane, RowState<D>& st, Mask mask) {
+                                             const typename AT<F32, D>::Frag (&bq)[NT][D / 16],
+                                             float scale2, int lane, RowState<D> (&st)[NT],
+                                             Mask mask) {
   using A = AT<F32, D>;
   using Frag = typename A::Frag;
-  const int h = lane / 32;
-  floatx16 sacc[2];
+  using VFrag = typename A::VFrag;
+  floatx16 sacc[NT][2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[mt][j] = 0.f;
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[nt][mt][j] = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int s = 0; s < A::NS; ++s) {
       const Frag a = *reinterpret_cast<const Frag*>(lds + (mt * A::NS + s) * A::FRAG + lane * 8 * A::ES);
-      sacc[mt] = mma16(a, bq[s], sacc[mt]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[nt][mt] = mma16(a, bq[nt][s], sacc[nt][mt]);
     }
-  }
-  float mloc = -__builtin_inff();
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int nt = 0; nt < NT; ++nt) {
+    float mloc = -__builtin_inff();
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float v = sacc[mt][4 * a + b] * scale2;
-        if (!mask(mt, a, b)) v = -__builtin_inff();
-        sacc[mt][4 * a + b] = v;
-        mloc = fmaxf(mloc, v);
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float v = sacc[nt][mt][4 * a + b];
+          if (!mask(nt, mt, a, b)) v = -__builtin_inff();
+          sacc[nt][mt][4 * a + b] = v;
+          mloc = fmaxf(mloc, v);
+        }
+    mloc = fmaxf(mloc, wave_shfl_xor(mloc, 32)) * scale2;
+    const float mnew = fmaxf(st[nt].m2, mloc);
+    const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(st[nt].m2 - mref);
+    st[nt].m2 = mnew;
+    float lsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][j], scale2, -mref));
+        sacc[nt][mt][j] = p;
+        lsum += p;
       }
-  mloc = fmaxf(mloc, wave_shfl_xor(mloc, 32));
-  const float mnew = fmaxf(st.m2, mloc);
-  const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f(st.m2 - mref);
-  st.m2 = mnew;
-  float lsum = 0.f;
+    st[nt].l = st[nt].l * alpha + lsum;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float p = __builtin_amdgcn_exp2f(sacc[mt][j] - mref);
-      sacc[mt][j] = p;
-      lsum += p;
-    }
-  st.l = st.l * alpha + lsum;
-#pragma unroll
-  for (int i = 0; i < A::MTD; ++i) st.o[i] *= alpha;
+    for (int i = 0; i < A::MTD; ++i) st[nt].o[i] *= alpha;
+  }
   // P as the B operand of O^T += V^T P^T: chunk s' covers keys 16s'..16s'+15
   const uint8_t* vl = lds + A::KBYTES;
 #pragma unroll
   for (int sp = 0; sp < 4; ++sp) {
-    // bfloat16 inputs: P = P_hi + P_lo, both contracted with the exact bf16 V,
-    // so the product keeps ~2^-17 relative accuracy instead of 2^-9
-    Frag pf, pl;
+    VFrag pf[NT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pv = sacc[sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)];
-      if constexpr (F32) {
-        pf[e] = pv;
-      } else {
-        const __bf16 hi = static_cast<__bf16>(pv);
-        pf[e] = hi;
-        pl[e] = static_cast<__bf16>(pv - static_cast<float>(hi));
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = sacc[nt][sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)];
+        if constexpr (F32) pf[nt][e] = pv; else pf[nt][e] = static_cast<_Float16>(pv);
       }
-    }
 #pragma unroll
     for (int mt = 0; mt < A::MTD; ++mt) {
-      const Frag a = *reinterpret_cast<const Frag*>(vl + (mt * 4 + sp) * A::FRAG + lane * 8 * A::ES);
-      st.o[mt] = mma16(a, pf, st.o[mt]);
-      if constexpr (!F32) st.o[mt] = mma16(a, pl, st.o[mt]);
+      const VFrag a = *reinterpret_cast<const VFrag*>(vl + (mt * 4 + sp) * A::FRAG + lane * 8 * A::ES);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) st[nt].o[mt] = mma16(a, pf[nt], st[nt].o[mt]);
     }
   }
-  (void)h;
+}
+
+// A lane's half of one partial: the D/2 values of the lane half's columns,
+// in accumulator order, written / read as 16-byte vectors.
+template <typename PartT, int MTD>
+__device__ __forceinline__ void store_partial(PartT* dst, const floatx16 (&o)[MTD], float sc) {
+  if constexpr (sizeof(PartT) == 4) {
+#pragma unroll
+    for (int mt = 0; mt < MTD; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        reinterpret_cast<floatx4*>(dst)[mt * 4 + q] =
+            floatx4{o[mt][4 * q] * sc, o[mt][4 * q + 1] * sc, o[mt][4 * q + 2] * sc,
+                    o[mt][4 * q + 3] * sc};
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MTD; ++mt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = o[mt][8 * q + 2 * i] * sc, b2 = o[mt][8 * q + 2 * i + 1] * sc;
+          w[i] = uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(a))) |
+                 (uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(b2))) << 16);
+        }
+        reinterpret_cast<u32x4*>(dst)[mt * 2 + q] = w;
+      }
+  }
+}
+
+// o += w * partial (the lane half's values, same order as store_partial).
+template <typename PartT, int MTD>
+__device__ __forceinline__ void accumulate_partial(floatx16 (&o)[MTD], const PartT* src, float w) {
+  if constexpr (sizeof(PartT) == 4) {
+#pragma unroll
+    for (int mt = 0; mt < MTD; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 v = reinterpret_cast<const floatx4*>(src)[mt * 4 + q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[mt][4 * q + i] = fmaf(w, v[i], o[mt][4 * q + i]);
+      }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MTD; ++mt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(src)[mt * 2 + q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = static_cast<float>(__builtin_bit_cast(_Float16, u16(v[i] & 0xFFFFu)));
+          const float b2 = static_cast<float>(__builtin_bit_cast(_Float16, u16(v[i] >> 16)));
+          o[mt][8 * q + 2 * i] = fmaf(w, a, o[mt][8 * q + 2 * i]);
+          o[mt][8 * q + 2 * i + 1] = fmaf(w, b2, o[mt][8 * q + 2 * i + 1]);
+        }
+      }
+  }
+}
+
+// Largest |v| of every (sequence, KV head), as bfloat16 bits (order-preserving
+// for non-negative values), for the float16 value scale.
+__global__ __launch_bounds__(256) void value_max_kernel(const bf16_t* __restrict__ V,
+                                                        uint32_t* __restrict__ vmax,
+                                                        int64_t per_head) {
+  const int64_t bkv = blockIdx.y;
+  const u32x4* src = reinterpret_cast<const u32x4*>(V + bkv * per_head);
+  const int64_t n16 = per_head / 8;
+  uint32_t m = 0;
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n16;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const u32x4 w = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, uint32_t(__shfl_xor(int(m), o, 64)));
+  if ((threadIdx.x & 63) == 0) atomicMax(&vmax[bkv], m);
 }
 
 // ---------------------------------------------------------------- dispatch --
@@ -364,13 +514,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
 // ---------------------------------------------------------- block attention --
 
 template <bool F32, int D, typename PartT>
-__global__ __launch_bounds__(kAttnThreads) void block_attn_kernel(
-    const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ K,
-    const typename AT<F32, D>::In* __restrict__ V, const int4* __restrict__ tasks,
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void block_attn_kernel(
+    const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
+    int64_t n_chunks, const int4* __restrict__ tasks,
     const int32_t* __restrict__ task_count, const uint32_t* __restrict__ entries,
-    PartT* __restrict__ o_part, float2* __restrict__ lse_part, int64_t n, int g, int hq, int hkv,
-    int B, int64_t nb, int k, float scale2) {
+    const uint32_t* __restrict__ vmax, PartT* __restrict__ o_part, float2* __restrict__ lse_part,
+    int64_t n, int g, int hq, int hkv, int B, int64_t nb, int k, float scale2) {
   using A = AT<F32, D>;
+  constexpr int NT = kTaskTiles;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int32_t T = *task_count;
   // XCD-aware order: consecutive tasks (same block) land on the same XCD.
@@ -383,73 +534,77 @@ __global__ __launch_bounds__(kAttnThreads) void block_attn_kernel(
   const int64_t b = bkv / hkv, kv = bkv % hkv;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
 
-  const int r = 32 * wave + ln;
-  const bool valid = r < task.z;
-  int64_t orow = 0;
-  int slot = 0;
-  typename A::Frag bq[A::NS];
-  {
+  int64_t orow[NT];
+  int slot[NT];
+  bool valid[NT];
+  typename A::Frag bq[NT][A::NS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = 32 * (NT * wave + nt) + ln;
+    valid[nt] = r < task.z;
     int64_t t = 0, j = 0;
-    if (valid) {
+    slot[nt] = 0;
+    if (valid[nt]) {
       const uint32_t code = entries[task.y + r];
       const int64_t rho = code >> 5;
-      slot = int(code & 31u);
+      slot[nt] = int(code & 31u);
       t = rho / g;
       j = rho % g;
     }
-    orow = (b * hq + kv * g + j) * n + t;
-    const auto* qrow = Q + orow * D;
+    orow[nt] = (b * hq + kv * g + j) * n + t;
+    const auto* qrow = Q + orow[nt] * D;
 #pragma unroll
-    for (int s = 0; s < A::NS; ++s) bq[s] = load_row_frag<F32, D>(qrow, s, h, valid);
+    for (int s = 0; s < A::NS; ++s) bq[nt][s] = load_row_frag<F32, D>(qrow, s, h, valid[nt]);
   }
-  const bool wave_active = 32 * wave < task.z;
+  const bool wave_active = 32 * NT * wave < task.z;
 
-  const auto* Kh = K + (bkv * n + c * B) * D;
-  const auto* Vh = V + (bkv * n + c * B) * D;
-  RowState<D> st;
-  row_state_init(st);
+  const uint8_t* src = img + (bkv * n_chunks + c * (B / kKeyChunk)) * A::CHUNK;
+  const int ev = F32 ? 0 : value_exponent(vmax[bkv]);
+  RowState<D> st[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) row_state_init(st[nt]);
   const int nchunks = B / kKeyChunk;
-  stage_chunk<F32, D>(lds, Kh, Vh, 0, B, tid);
+  stage_chunk_dma<F32, D>(lds, src, tid);
   __syncthreads();
   for (int ch = 0; ch < nchunks; ++ch) {
-    if (ch + 1 < nchunks)
-      stage_chunk<F32, D>(lds + ((ch + 1) & 1) * A::CHUNK, Kh, Vh, int64_t(ch + 1) * kKeyChunk, B, tid);
+    const bool more = ch + 1 < nchunks;
+    if (more) stage_chunk_dma<F32, D>(lds + ((ch + 1) & 1) * A::CHUNK, src + (ch + 1) * A::CHUNK, tid);
     if (wave_active)
-      attend_chunk<F32, D>(lds + (ch & 1) * A::CHUNK, bq, scale2, lane, st,
-                           [](int, int, int) { return true; });
+      attend_chunk<F32, D, NT>(lds + (ch & 1) * A::CHUNK, bq, scale2, lane, st,
+                               [](int, int, int, int) { return true; });
     __syncthreads();
   }
-  if (!valid) return;
-  const float l = st.l + wave_shfl_xor(st.l, 32);
-  const float inv = 1.f / l;
-  // the partial is a convex combination of value rows; half-precision partials
-  // are stored scaled by 2^-e with |o| < 2^e, so every entry keeps ~2^-12
-  // relative accuracy of max|o| whatever the value range
-  float mx = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < A::MTD; ++mt)
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!valid[nt]) continue;
+    const float l = st[nt].l + wave_shfl_xor(st[nt].l, 32);
+    const float inv = 1.f / l;
+    // the partial is a convex combination of value rows; half-precision
+    // partials are stored scaled by 2^-e with |o| < 2^e, so every entry keeps
+    // ~2^-12 relative accuracy of max|o| whatever the value range
+    float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(st.o[mt][j]));
-  mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * inv;
-  int e = 0;
-  if (!F32 && mx > 0.f) (void)frexpf(mx, &e);
-  const float sc = ldexpf(inv, -e);
-  const int64_t pidx = orow * k + slot;
-  PartT* dst = o_part + pidx * D + h * (D / 2);
+    for (int mt = 0; mt < A::MTD; ++mt)
 #pragma unroll
-  for (int mt = 0; mt < A::MTD; ++mt)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) store_from_f32(dst, mt * 16 + j, st.o[mt][j] * sc);
-  if (h == 0) lse_part[pidx] = float2{st.m2 + __log2f(l), float(e)};
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(st[nt].o[mt][j]));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * inv;
+    int e = 0;
+    if (!F32 && mx > 0.f) (void)frexpf(mx, &e);
+    const float sc = ldexpf(inv, -e);
+    const int64_t pidx = orow[nt] * k + slot[nt];
+    PartT* dst = o_part + pidx * D + h * (D / 2);
+    store_partial<PartT>(dst, st[nt].o, sc);
+    if (h == 0) lse_part[pidx] = float2{st[nt].m2 + __log2f(l), float(e + ev)};
+  }
 }
 
 // ----------------------------------------------------------- window + merge --
 
 template <bool F32, int D, typename PartT, typename OutT>
-__global__ __launch_bounds__(kAttnThreads) void window_merge_kernel(
-    const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ K,
-    const typename AT<F32, D>::In* __restrict__ V, const int32_t* __restrict__ idx,
-    const PartT* __restrict__ o_part, const float2* __restrict__ lse_part, OutT* __restrict__ O,
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void window_merge_kernel(
+    const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
+    int64_t n_chunks, const int32_t* __restrict__ idx, const uint32_t* __restrict__ vmax, const PartT* __restrict__ o_part,
+    const float2* __restrict__ lse_part, OutT* __restrict__ O,
     float* __restrict__ lse, int64_t n, int g, int hq, int hkv, int B, int k, int W,
     float scale2, int64_t n_tiles) {
   using A = AT<F32, D>;
@@ -467,6 +622,13 @@ __global__ __launch_bounds__(kAttnThreads) void window_merge_kernel(
   const int64_t t = valid ? rho / g : 0, jg = valid ? rho % g : 0;
   const int64_t orow = (b * hq + kv * g + jg) * n + t;
 
+  const int64_t t_lo = rho0 / g, t_hi = min(n - 1, (rho0 + kWinRows - 1) / g);
+  const int64_t key_lo = max(int64_t(0), t_lo - W + 1);
+  const int64_t ch0 = key_lo / kKeyChunk, ch1 = t_hi / kKeyChunk;
+  const uint8_t* src = img + bkv * n_chunks * A::CHUNK;
+  const int ev = F32 ? 0 : value_exponent(vmax[bkv]);
+  stage_chunk_dma<F32, D>(lds, src + ch0 * A::CHUNK, tid);
+
   for (int w = tid; w < kWinRows * k; w += kAttnThreads) {
     const int rr = w / k, i = w % k;
     const int64_t rh = rho0 + rr;
@@ -477,29 +639,23 @@ __global__ __launch_bounds__(kAttnThreads) void window_merge_kernel(
     }
     sidx[w] = v;
   }
-  typename A::Frag bq[A::NS];
+  typename A::Frag bq[1][A::NS];
   {
     const auto* qrow = Q + orow * D;
 #pragma unroll
-    for (int s = 0; s < A::NS; ++s) bq[s] = load_row_frag<F32, D>(qrow, s, h, valid);
+    for (int s = 0; s < A::NS; ++s) bq[0][s] = load_row_frag<F32, D>(qrow, s, h, valid);
   }
-  const int64_t t_lo = rho0 / g, t_hi = min(n - 1, (rho0 + kWinRows - 1) / g);
-  const int64_t key_lo = max(int64_t(0), t_lo - W + 1);
-  const int64_t ch0 = key_lo / kKeyChunk, ch1 = t_hi / kKeyChunk;
   const int64_t wave_t_lo = min(n - 1, (rho0 + 32 * wave) / g);
   const int64_t wave_t_hi = min(n - 1, (rho0 + 32 * wave + 31) / g);
   const bool wave_active = rho0 + 32 * wave < rows_total;
 
-  const auto* Kh = K + bkv * n * D;
-  const auto* Vh = V + bkv * n * D;
-  RowState<D> st;
-  row_state_init(st);
-  stage_chunk<F32, D>(lds, Kh, Vh, ch0 * kKeyChunk, n, tid);
+  RowState<D> st[1];
+  row_state_init(st[0]);
   __syncthreads();
   for (int64_t ch = ch0; ch <= ch1; ++ch) {
     const int buf = int((ch - ch0) & 1);
-    if (ch + 1 <= ch1)
-      stage_chunk<F32, D>(lds + (buf ^ 1) * A::CHUNK, Kh, Vh, (ch + 1) * kKeyChunk, n, tid);
+    const bool more = ch + 1 <= ch1;
+    if (more) stage_chunk_dma<F32, D>(lds + (buf ^ 1) * A::CHUNK, src + (ch + 1) * A::CHUNK, tid);
     const int64_t key0 = ch * kKeyChunk;
     // does this wave's token range touch the chunk at all?
     const bool touch = wave_active && key0 <= wave_t_hi && key0 + kKeyChunk - 1 > wave_t_lo - W;
@@ -509,36 +665,33 @@ __global__ __launch_bounds__(kAttnThreads) void window_merge_kernel(
       bool excl = false;
       for (int i = 0; i < k; ++i) excl |= sidx[r * k + i] == blk;
       const int64_t tv = valid ? t : -(int64_t(1) << 40);
-      attend_chunk<F32, D>(lds + buf * A::CHUNK, bq, scale2, lane, st,
-                           [&](int mt, int a, int bb) {
-                             const int64_t j = key0 + 32 * mt + 8 * a + 4 * h + bb;
-                             return !excl && j <= tv && j > tv - W;
-                           });
+      attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
+                              [&](int, int mt, int a, int bb) {
+                                const int64_t j = key0 + 32 * mt + 8 * a + 4 * h + bb;
+                                return !excl && j <= tv && j > tv - W;
+                              });
     }
     __syncthreads();
   }
   if (!valid) return;
   // merge: window part (m2, l, o unnormalised) with the routed partials
-  const float lw = st.l + wave_shfl_xor(st.l, 32);
-  float M = lw > 0.f ? st.m2 + __log2f(lw) : -__builtin_inff();
+  RowState<D>& ws = st[0];
+  const float lw = ws.l + wave_shfl_xor(ws.l, 32);
+  float M = lw > 0.f ? ws.m2 + __log2f(lw) : -__builtin_inff();
   for (int i = 0; i < k; ++i)
     if (sidx[r * k + i] >= 0) M = fmaxf(M, lse_part[orow * k + i].x);
-  const float ww = lw > 0.f ? __builtin_amdgcn_exp2f(st.m2 - M) : 0.f;
+  const float ww = lw > 0.f ? __builtin_amdgcn_exp2f(ws.m2 - M) : 0.f;
   float den = ww * lw;
+  const float wws = ldexpf(ww, ev);   // the window's values were scaled by 2^-ev
 #pragma unroll
-  for (int mt = 0; mt < A::MTD; ++mt) st.o[mt] *= ww;
+  for (int mt = 0; mt < A::MTD; ++mt) ws.o[mt] *= wws;
   for (int i = 0; i < k; ++i) {
     if (sidx[r * k + i] < 0) continue;
     const int64_t pidx = orow * k + i;
     const float2 le = lse_part[pidx];
     const float wi = __builtin_amdgcn_exp2f(le.x - M);
     den += wi;
-    const float ws = ldexpf(wi, int(le.y));
-    const PartT* src = o_part + pidx * D + h * (D / 2);
-#pragma unroll
-    for (int mt = 0; mt < A::MTD; ++mt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) st.o[mt][j] = fmaf(ws, load_f32(src, mt * 16 + j), st.o[mt][j]);
+    accumulate_partial<PartT>(ws.o, o_part + pidx * D + h * (D / 2), ldexpf(wi, int(le.y)));
   }
   const float inv = 1.f / den;
   OutT* out = O + orow * D;
@@ -548,13 +701,16 @@ __global__ __launch_bounds__(kAttnThreads) void window_merge_kernel(
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb)
-        store_from_f32(out, 32 * mt + 8 * a + 4 * h + bb, st.o[mt][4 * a + bb] * inv);
+        store_from_f32(out, 32 * mt + 8 * a + 4 * h + bb, ws.o[mt][4 * a + bb] * inv);
   if (h == 0) lse[orow] = (M + __log2f(den)) * kLn2;
 }
 
 // ------------------------------------------------------------------ launch --
 
 struct AttnWs {
+  uint32_t* vmax;
+  uint8_t* img;
+  int64_t n_chunks;
   int32_t* counts;
   int32_t* cursor;
   int32_t* task_count;
@@ -578,6 +734,10 @@ AttnWs attn_ws_layout(const Shape& s, void* base) {
     off += align_up(bytes);
     return o;
   };
+  const size_t o_vmax = take(size_t(s.b) * s.hkv * 4);
+  w.n_chunks = (s.n + kKeyChunk - 1) / kKeyChunk;
+  const size_t chunk_bytes = size_t(kKeyChunk) * s.d * 2 * es;
+  const size_t o_img = take(size_t(s.b) * s.hkv * size_t(w.n_chunks) * chunk_bytes);
   const size_t o_counts = take(size_t(nseg) * 4), o_cursor = take(size_t(nseg) * 4);
   const size_t o_tc = take(4), o_tasks = take(size_t(w.max_tasks) * 16);
   const size_t o_entries = take(size_t(pairs) * 4), o_lse = take(size_t(pairs) * 8);
@@ -585,6 +745,8 @@ AttnWs attn_ws_layout(const Shape& s, void* base) {
   w.bytes = off;
   if (base != nullptr) {
     uint8_t* p = static_cast<uint8_t*>(base);
+    w.vmax = reinterpret_cast<uint32_t*>(p + o_vmax);
+    w.img = p + o_img;
     w.counts = reinterpret_cast<int32_t*>(p + o_counts);
     w.cursor = reinterpret_cast<int32_t*>(p + o_cursor);
     w.task_count = reinterpret_cast<int32_t*>(p + o_tc);
@@ -610,6 +772,16 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
   const int64_t nseg = n_bkv * s.nb;
   const float scale2 = s.scale * kLog2e;
   hipError_t e;
+  if (!F32) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st,
+                       reinterpret_cast<int32_t*>(w.vmax), n_bkv, 0);
+    const int64_t per_head = s.n * D;
+    const unsigned gx = unsigned(std::min<int64_t>((per_head / 8 + 255) / 256, 64));
+    hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
+                       reinterpret_cast<const bf16_t*>(Vv), w.vmax, per_head);
+  }
+  hipLaunchKernelGGL((kv_image_kernel<F32, D>), dim3(unsigned(w.n_chunks), unsigned(n_bkv)),
+                     dim3(kAttnThreads), 0, st, K, V, w.vmax, w.img, s.n, w.n_chunks);
   if (s.k > 0 && nseg > 0) {
     hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((nseg + 255) / 256, 4096))),
                        dim3(256), 0, st, w.counts, nseg, 0);
@@ -633,8 +805,9 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(bshm))) != hipSuccess)
       return e;
     const int64_t grid = (w.max_tasks + 7) / 8 * 8;
-    hipLaunchKernelGGL(bk, dim3(unsigned(grid)), dim3(kAttnThreads), bshm, st, Q, K, V, w.tasks,
-                       w.task_count, w.entries, static_cast<PartT*>(w.o_part), w.lse_part, s.n,
+    hipLaunchKernelGGL(bk, dim3(unsigned(grid)), dim3(kAttnThreads), bshm, st, Q, w.img, w.n_chunks,
+                       w.tasks,
+                       w.task_count, w.entries, w.vmax, static_cast<PartT*>(w.o_part), w.lse_part, s.n,
                        s.g, s.hq, s.hkv, s.B, s.nb, s.k, scale2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -644,8 +817,8 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
                                hipFuncAttributeMaxDynamicSharedMemorySize, int(wshm))) != hipSuccess)
     return e;
   const int64_t n_tiles = (s.n * s.g + kWinRows - 1) / kWinRows;
-  hipLaunchKernelGGL(wk, dim3(unsigned(n_tiles * n_bkv)), dim3(kAttnThreads), wshm, st, Q, K, V,
-                     idx, static_cast<const PartT*>(w.o_part), w.lse_part, static_cast<OutT*>(Ov),
+  hipLaunchKernelGGL(wk, dim3(unsigned(n_tiles * n_bkv)), dim3(kAttnThreads), wshm, st, Q, w.img,
+                     w.n_chunks, idx, w.vmax, static_cast<const PartT*>(w.o_part), w.lse_part, static_cast<OutT*>(Ov),
                      lse, s.n, s.g, s.hq, s.hkv, s.B, s.k, s.W, scale2, n_tiles);
   return hipGetLastError();
 }

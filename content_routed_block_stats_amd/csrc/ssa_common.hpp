@@ -7,6 +7,7 @@
 namespace ssa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -75,6 +76,10 @@ __host__ __device__ __forceinline__ constexpr int frag_k(int s, int h, int e) {
 // One MFMA step contracting a 16-wide chunk: bf16 inputs (one instruction)...
 __device__ __forceinline__ floatx16 mma16(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// ...or float16 inputs (one instruction)...
+__device__ __forceinline__ floatx16 mma16(const f16x8& a, const f16x8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 // ...or float32 inputs (eight 32x32x2 instructions, element e on slot 2e + h).
 __device__ __forceinline__ floatx16 mma16(const floatx8& a, const floatx8& b, floatx16 c) {
