@@ -33,8 +33,8 @@
 namespace ssa {
 namespace {
 
-constexpr int kRouteThreads = 512;
-constexpr int kRouteRows = 512;
+constexpr int kRouteThreads = 512;   // 8 waves, two per SIMD
+constexpr int kRouteRows = 512;      // 64 query rows per wave
 constexpr int kFragBytes = 2048;   // one 32x16 operand fragment: 64 lanes x 32 bytes
 
 template <int D>
@@ -45,6 +45,9 @@ struct RouteLayout {
   static constexpr int MU_OFF = NF * kFragBytes;
   static constexpr int MU_BYTES = 2 * MT * 16 * 4;  // mu in accumulator order, both lane halves
   static constexpr int BLOCK_BYTES = (MU_OFF + MU_BYTES + 255) / 256 * 256;
+  // LDS copy of one image, whole 1 KB DMA rows (the last row reads past the image)
+  static constexpr int DMA_ROWS = (BLOCK_BYTES + 1023) / 1024;
+  static constexpr int LDS_BYTES = DMA_ROWS * 1024;
   __host__ __device__ static constexpr int frag(int mt, int s) { return mt * (mt + 1) + s; }
 };
 
@@ -152,8 +155,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   using Lay = RouteLayout<D>;
   using QT = typename QFrag<F32>::T;
   constexpr int MT = Lay::MT, NS = Lay::NS, BYTES = Lay::BLOCK_BYTES;
-  constexpr int N16 = BYTES / 16;
-  constexpr int PER_T = (N16 + kRouteThreads - 1) / kRouteThreads;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
@@ -191,83 +192,67 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     li[i] = -1;
   }
 
+  // block c's image -> LDS buffer c&1 by direct global->LDS loads (1 KB per
+  // wave instruction); the barrier that ends an iteration waits for them
   const uint8_t* src_base = prep + bkv * nb * int64_t(BYTES);
-  u32x4 stage[PER_T];
-  auto load_stage = [&](int64_t c) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(src_base + c * BYTES);
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int w = tid + i * kRouteThreads;
-      if (w < N16) stage[i] = __builtin_nontemporal_load(src + w);
-    }
+  auto stage = [&](int64_t c) {
+    const uint8_t* src = src_base + c * BYTES;
+    uint8_t* dst = lds + (c & 1) * Lay::LDS_BYTES;
+    for (int r = wave; r < Lay::DMA_ROWS; r += kRouteThreads / 64)
+      __builtin_amdgcn_global_load_lds(src + r * 1024 + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + r * 1024),
+                                       16, 0, 0);
   };
-  auto store_stage = [&](int buf) {
-    u32x4* dst = reinterpret_cast<u32x4*>(lds + buf * BYTES);
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int w = tid + i * kRouteThreads;
-      if (w < N16) dst[w] = stage[i];
-    }
-  };
-
-  if (C_wg > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
+  if (C_wg > 0) stage(0);
   __syncthreads();
 
-  for (int64_t c = 0; c < C_wg; ++c) {
-    const bool more = c + 1 < C_wg;
-    if (more) load_stage(c + 1);
-    const uint8_t* L = lds + (c & 1) * BYTES;
-
-    floatx16 acc[2][MT];
+  // Output tiles are contracted one at a time (both row tiles, high then low
+  // part per chunk) and each finished tile is folded into the row-dot (lane
+  // (ln, h) holds P_j + mu_j for j = 32mt + 8a + 4h + b) while the next tile's
+  // MFMAs run.  The last tile's dot and the top-k insert of a block are
+  // deferred to the start of the next block's iteration, where they overlap
+  // that block's first MFMAs; blocks still enter the top-k in order.
+  floatx16 acc[2][MT];
+  float part[2] = {0.f, 0.f}, prev[2] = {0.f, 0.f};
+  auto mfma_tile = [&](const uint8_t* L, int mt) {
+    const floatx16 m = *reinterpret_cast<const floatx16*>(L + Lay::MU_OFF + (h * MT + mt) * 64);
+    acc[0][mt] = m;
+    acc[1][mt] = m;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const floatx16 m = *reinterpret_cast<const floatx16*>(L + Lay::MU_OFF + (h * MT + mt) * 64);
-      acc[0][mt] = m;
-      acc[1][mt] = m;
-    }
+    for (int s = 0; s <= 2 * mt + 1; ++s) {
+      const uint8_t* F = L + Lay::frag(mt, s) * kFragBytes;
+      if constexpr (F32) {
+        const floatx8 a = *reinterpret_cast<const floatx8*>(F + lane * 32);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+        for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma16(a, bq[nt][s], acc[nt][mt]);
+      } else {
+        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(F + lane * 16);
+        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(F + 1024 + lane * 16);
 #pragma unroll
-      for (int s = 0; s <= 2 * mt + 1; ++s) {
-        const uint8_t* F = L + Lay::frag(mt, s) * kFragBytes;
-        if constexpr (F32) {
-          const floatx8 a = *reinterpret_cast<const floatx8*>(F + lane * 32);
+        for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma16(ahi, bq[nt][s], acc[nt][mt]);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma16(a, bq[nt][s], acc[nt][mt]);
-        } else {
-          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(F + lane * 16);
-          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(F + 1024 + lane * 16);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            acc[nt][mt] = mma16(ahi, bq[nt][s], acc[nt][mt]);
-            acc[nt][mt] = mma16(alo, bq[nt][s], acc[nt][mt]);
-          }
-        }
+        for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma16(alo, bq[nt][s], acc[nt][mt]);
       }
     }
-    // row-dot: lane (ln, h) holds P_j + mu_j for j = 32mt + 8a + 4h + b of both tiles
-    float part[2];
+  };
+  auto dot_tile = [&](int mt, float (&pt)[2]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float sacc = 0.f;
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb)
-            sacc = fmaf(acc[nt][mt][4 * a + bb],
-                        QFrag<F32>::elem(bq[nt][2 * mt + (a >> 1)], 4 * (a & 1) + bb), sacc);
-      part[nt] = sacc + wave_shfl_xor(sacc, 32);
-    }
-    if (more) store_stage((c + 1) & 1);
-
-    float sc = h ? part[1] : part[0];
-    if (c < my_C && sc > ls[KMAX]) {
-      int ci = int(c);
+        for (int bb = 0; bb < 4; ++bb)
+          pt[nt] = fmaf(acc[nt][mt][4 * a + bb],
+                        QFrag<F32>::elem(bq[nt][2 * mt + (a >> 1)], 4 * (a & 1) + bb), pt[nt]);
+  };
+  // both lane halves combined, then the running top-k insert of block cb
+  auto insert = [&](float (&pt)[2], int64_t cb) {
+    const float p0 = pt[0] + wave_shfl_xor(pt[0], 32);
+    const float p1 = pt[1] + wave_shfl_xor(pt[1], 32);
+    pt[0] = pt[1] = 0.f;
+    float sc = h ? p1 : p0;
+    if (cb < my_C && sc > ls[KMAX]) {
+      int ci = int(cb);
 #pragma unroll
       for (int i = 0; i <= KMAX; ++i) {
         const bool gt = sc > ls[i];
@@ -279,7 +264,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         ci = gt ? ti : ci;
       }
     }
+  };
+
+  for (int64_t c = 0; c < C_wg; ++c) {
+    if (c + 1 < C_wg) stage(c + 1);
+    const uint8_t* L = lds + (c & 1) * Lay::LDS_BYTES;
+    mfma_tile(L, 0);
+    if (c > 0) {
+      dot_tile(MT - 1, prev);
+      insert(prev, c - 1);
+    }
+#pragma unroll
+    for (int mt = 1; mt < MT; ++mt) {
+      dot_tile(mt - 1, part);
+      mfma_tile(L, mt);
+      // interleave: one MFMA, then three VALU (the previous tile's row-dot)
+      constexpr int kMfmaPerChunk = F32 ? 16 : 4;
+#pragma unroll
+      for (int i = 0; i < (2 * mt + 2) * kMfmaPerChunk; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    }
+    prev[0] = part[0];
+    prev[1] = part[1];
+    part[0] = part[1] = 0.f;
     __syncthreads();
+  }
+  if (C_wg > 0) {
+    dot_tile(MT - 1, prev);
+    insert(prev, C_wg - 1);
   }
 
   if (!my_valid) return;
@@ -328,7 +342,7 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
     if (e != hipSuccess) return e;
   }
   const int64_t n_tiles = (s.n * s.g + kRouteRows - 1) / kRouteRows;
-  const size_t shmem = 2 * size_t(Lay::BLOCK_BYTES);
+  const size_t shmem = 2 * size_t(Lay::LDS_BYTES);
   auto kern = route_topk_kernel<F32, D, KMAX>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
@@ -352,7 +366,8 @@ hipError_t launch_route_d(const Shape& s, const void* Q, const float* mu, const 
 
 size_t route_workspace_bytes(const Shape& s) {
   const size_t per = s.d == 64 ? RouteLayout<64>::BLOCK_BYTES : RouteLayout<128>::BLOCK_BYTES;
-  return align_up(size_t(s.b) * s.hkv * size_t(s.nb) * per);
+  // + 1 KB: the DMA of the last image reads up to one row past its end
+  return align_up(size_t(s.b) * s.hkv * size_t(s.nb) * per + 1024);
 }
 
 hipError_t launch_route_topk(const Shape& s, const void* Q, const float* mu, const float* sigma,

@@ -258,14 +258,27 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) sacc[nt][mt][j] = 0.f;
+  // S^T = K Q^T: the two 32-key tiles are independent accumulator chains,
+  // interleaved; K fragments are read from LDS two steps ahead of use.
+  auto kfrag = [&](int mt, int s) {
+    return *reinterpret_cast<const Frag*>(lds + (mt * A::NS + s) * A::FRAG + lane * 8 * A::ES);
+  };
+  Frag ka[3][2];
+  ka[0][0] = kfrag(0, 0);
+  ka[0][1] = kfrag(1, 0);
+  ka[1][0] = kfrag(0, 1);
+  ka[1][1] = kfrag(1, 1);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int s = 0; s < A::NS; ++s) {
-      const Frag a = *reinterpret_cast<const Frag*>(lds + (mt * A::NS + s) * A::FRAG + lane * 8 * A::ES);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sacc[nt][mt] = mma16(a, bq[nt][s], sacc[nt][mt]);
+  for (int s = 0; s < A::NS; ++s) {
+    if (s + 2 < A::NS) {
+      ka[(s + 2) % 3][0] = kfrag(0, s + 2);
+      ka[(s + 2) % 3][1] = kfrag(1, s + 2);
     }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[nt][mt] = mma16(ka[s % 3][mt], bq[nt][s], sacc[nt][mt]);
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float mloc = -__builtin_inff();
@@ -298,10 +311,22 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
 #pragma unroll
     for (int i = 0; i < A::MTD; ++i) st[nt].o[i] *= alpha;
   }
-  // P as the B operand of O^T += V^T P^T: chunk s' covers keys 16s'..16s'+15
+  // P as the B operand of O^T += V^T P^T: chunk s' covers keys 16s'..16s'+15.
+  // The MTD output tiles are independent chains; V fragments are read one
+  // step ahead of use.
   const uint8_t* vl = lds + A::KBYTES;
+  auto vfrag = [&](int mt, int sp) {
+    return *reinterpret_cast<const VFrag*>(vl + (mt * 4 + sp) * A::FRAG + lane * 8 * A::ES);
+  };
+  VFrag va[2][A::MTD];
+#pragma unroll
+  for (int mt = 0; mt < A::MTD; ++mt) va[0][mt] = vfrag(mt, 0);
 #pragma unroll
   for (int sp = 0; sp < 4; ++sp) {
+    if (sp + 1 < 4) {
+#pragma unroll
+      for (int mt = 0; mt < A::MTD; ++mt) va[(sp + 1) & 1][mt] = vfrag(mt, sp + 1);
+    }
     VFrag pf[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -311,11 +336,9 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
         if constexpr (F32) pf[nt][e] = pv; else pf[nt][e] = static_cast<_Float16>(pv);
       }
 #pragma unroll
-    for (int mt = 0; mt < A::MTD; ++mt) {
-      const VFrag a = *reinterpret_cast<const VFrag*>(vl + (mt * 4 + sp) * A::FRAG + lane * 8 * A::ES);
+    for (int mt = 0; mt < A::MTD; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) st[nt].o[mt] = mma16(a, pf[nt], st[nt].o[mt]);
-    }
+      for (int nt = 0; nt < NT; ++nt) st[nt].o[mt] = mma16(va[sp & 1][mt], pf[nt], st[nt].o[mt]);
   }
 }
 
@@ -513,6 +536,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
 
 // ---------------------------------------------------------- block attention --
 
+// Persistent: the tasks of one XCD form a contiguous range (consecutive tasks
+// share a block, so its images stay in that XCD's L2), dealt round-robin to
+// the XCD's workgroups.  While a task runs, the next task's first chunk is
+// staged during the last chunk, its row entries are fetched during chunk 0
+// and its query rows during chunk 1, so a task's start-up latency hides
+// behind the previous task's compute.
 template <bool F32, int D, typename PartT>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void block_attn_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
@@ -521,80 +550,101 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     const uint32_t* __restrict__ vmax, PartT* __restrict__ o_part, float2* __restrict__ lse_part,
     int64_t n, int g, int hq, int hkv, int B, int64_t nb, int k, float scale2) {
   using A = AT<F32, D>;
-  constexpr int NT = kTaskTiles;
+  using Frag = typename A::Frag;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int32_t T = *task_count;
-  // XCD-aware order: consecutive tasks (same block) land on the same XCD.
-  const int64_t per_xcd = (int64_t(T) + 7) / 8;
+  const int64_t T = *task_count;
+  const int64_t per_xcd = (T + 7) / 8;
   const int64_t x = blockIdx.x;
-  const int64_t ti = (x % 8) * per_xcd + x / 8;
-  if (x / 8 >= per_xcd || ti >= T) return;
-  const int4 task = tasks[ti];
-  const int64_t seg = task.x, bkv = seg / nb, c = seg % nb;
-  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  const int64_t xb = (x % 8) * per_xcd, xe = min(T, xb + per_xcd);
+  const int64_t stride = gridDim.x / 8;
+  int64_t ti = xb + x / 8;
+  if (ti >= xe) return;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
-
-  int64_t orow[NT];
-  int slot[NT];
-  bool valid[NT];
-  typename A::Frag bq[NT][A::NS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = 32 * (NT * wave + nt) + ln;
-    valid[nt] = r < task.z;
-    int64_t t = 0, j = 0;
-    slot[nt] = 0;
-    if (valid[nt]) {
-      const uint32_t code = entries[task.y + r];
-      const int64_t rho = code >> 5;
-      slot[nt] = int(code & 31u);
-      t = rho / g;
-      j = rho % g;
-    }
-    orow[nt] = (b * hq + kv * g + j) * n + t;
-    const auto* qrow = Q + orow[nt] * D;
-#pragma unroll
-    for (int s = 0; s < A::NS; ++s) bq[nt][s] = load_row_frag<F32, D>(qrow, s, h, valid[nt]);
-  }
-  const bool wave_active = 32 * NT * wave < task.z;
-
-  const uint8_t* src = img + (bkv * n_chunks + c * (B / kKeyChunk)) * A::CHUNK;
-  const int ev = F32 ? 0 : value_exponent(vmax[bkv]);
-  RowState<D> st[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) row_state_init(st[nt]);
+  const int r = 32 * wave + ln;             // this lane's row within a task
   const int nchunks = B / kKeyChunk;
-  stage_chunk_dma<F32, D>(lds, src, tid);
+
+  auto image_of = [&](const int4& tk) {
+    const int64_t bkv = tk.x / nb, c = tk.x % nb;
+    return img + (bkv * n_chunks + c * (B / kKeyChunk)) * A::CHUNK;
+  };
+  // the query row of entry code for task tk: global row index and slot
+  auto row_of = [&](const int4& tk, uint32_t code, int64_t& orow, int& slot) {
+    const int64_t bkv = tk.x / nb, b = bkv / hkv, kv = bkv % hkv;
+    const int64_t rho = code >> 5;
+    slot = int(code & 31u);
+    orow = (b * hq + kv * g + rho % g) * n + rho / g;
+  };
+
+  int4 task = tasks[ti];
+  uint32_t code = r < task.z ? entries[task.y + r] : 0u;
+  int64_t orow;
+  int slot;
+  row_of(task, code, orow, slot);
+  Frag bq[1][A::NS];
+#pragma unroll
+  for (int s = 0; s < A::NS; ++s) bq[0][s] = load_row_frag<F32, D>(Q + orow * D, s, h, r < task.z);
+  stage_chunk_dma<F32, D>(lds, image_of(task), tid);
+  int buf = 0;
   __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const bool more = ch + 1 < nchunks;
-    if (more) stage_chunk_dma<F32, D>(lds + ((ch + 1) & 1) * A::CHUNK, src + (ch + 1) * A::CHUNK, tid);
-    if (wave_active)
-      attend_chunk<F32, D, NT>(lds + (ch & 1) * A::CHUNK, bq, scale2, lane, st,
-                               [](int, int, int, int) { return true; });
-    __syncthreads();
-  }
+
+  while (true) {
+    const int64_t tn = ti + stride;
+    const bool has_next = tn < xe;
+    const int4 task_n = has_next ? tasks[tn] : int4{0, 0, 0, 0};
+    const uint8_t* src = image_of(task);
+    const bool valid = r < task.z, wave_active = 32 * wave < task.z;
+    const int ev = F32 ? 0 : value_exponent(vmax[task.x / nb]);
+    uint32_t code_n = 0;
+    int64_t orow_n = 0;
+    int slot_n = 0;
+    Frag bqn[A::NS];
+    RowState<D> st[1];
+    row_state_init(st[0]);
+    for (int ch = 0; ch < nchunks; ++ch) {
+      uint8_t* nbuf = lds + (buf ^ 1) * A::CHUNK;
+      if (ch + 1 < nchunks)
+        stage_chunk_dma<F32, D>(nbuf, src + (ch + 1) * A::CHUNK, tid);
+      else if (has_next)
+        stage_chunk_dma<F32, D>(nbuf, image_of(task_n), tid);
+      if (ch == 0 && has_next && r < task_n.z) code_n = entries[task_n.y + r];
+      if (ch == (nchunks > 1 ? 1 : 0) && has_next) {
+        row_of(task_n, code_n, orow_n, slot_n);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (!valid[nt]) continue;
-    const float l = st[nt].l + wave_shfl_xor(st[nt].l, 32);
-    const float inv = 1.f / l;
-    // the partial is a convex combination of value rows; half-precision
-    // partials are stored scaled by 2^-e with |o| < 2^e, so every entry keeps
-    // ~2^-12 relative accuracy of max|o| whatever the value range
-    float mx = 0.f;
+        for (int s = 0; s < A::NS; ++s)
+          bqn[s] = load_row_frag<F32, D>(Q + orow_n * D, s, h, r < task_n.z);
+      }
+      if (wave_active)
+        attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
+                                [](int, int, int, int) { return true; });
+      __syncthreads();
+      buf ^= 1;
+    }
+    if (valid) {
+      const float l = st[0].l + wave_shfl_xor(st[0].l, 32);
+      const float inv = 1.f / l;
+      // the partial is a convex combination of value rows; half-precision
+      // partials are stored scaled by 2^-e with |o| < 2^e, so every entry keeps
+      // ~2^-12 relative accuracy of max|o| whatever the value range
+      float mx = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < A::MTD; ++mt)
+      for (int mt = 0; mt < A::MTD; ++mt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(st[nt].o[mt][j]));
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * inv;
-    int e = 0;
-    if (!F32 && mx > 0.f) (void)frexpf(mx, &e);
-    const float sc = ldexpf(inv, -e);
-    const int64_t pidx = orow[nt] * k + slot[nt];
-    PartT* dst = o_part + pidx * D + h * (D / 2);
-    store_partial<PartT>(dst, st[nt].o, sc);
-    if (h == 0) lse_part[pidx] = float2{st[nt].m2 + __log2f(l), float(e + ev)};
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(st[0].o[mt][j]));
+      mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * inv;
+      int e = 0;
+      if (!F32 && mx > 0.f) (void)frexpf(mx, &e);
+      const float sc = ldexpf(inv, -e);
+      const int64_t pidx = orow * k + slot;
+      store_partial<PartT>(o_part + pidx * D + h * (D / 2), st[0].o, sc);
+      if (h == 0) lse_part[pidx] = float2{st[0].m2 + __log2f(l), float(e + ev)};
+    }
+    if (!has_next) break;
+    ti = tn;
+    task = task_n;
+    orow = orow_n;
+    slot = slot_n;
+#pragma unroll
+    for (int s = 0; s < A::NS; ++s) bq[0][s] = bqn[s];
   }
 }
 
@@ -609,7 +659,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     float scale2, int64_t n_tiles) {
   using A = AT<F32, D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  int32_t* sidx = reinterpret_cast<int32_t*>(lds + 2 * A::CHUNK);   // [kWinRows][k]
+  int32_t* sidx = reinterpret_cast<int32_t*>(lds + 2 * A::CHUNK);   // [k][kWinRows]
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int64_t bkv = blockIdx.x / n_tiles;
   const int64_t tile = blockIdx.x % n_tiles;
@@ -630,14 +680,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   stage_chunk_dma<F32, D>(lds, src + ch0 * A::CHUNK, tid);
 
   for (int w = tid; w < kWinRows * k; w += kAttnThreads) {
-    const int rr = w / k, i = w % k;
+    const int rr = w / k, i = w % k;   // coalesced idx reads, transposed LDS writes
     const int64_t rh = rho0 + rr;
     int32_t v = -1;
     if (rh < rows_total) {
       const int64_t tt = rh / g, jj = rh % g;
       v = idx[((b * hq + kv * g + jj) * n + tt) * k + i];
     }
-    sidx[w] = v;
+    sidx[i * kWinRows + rr] = v;
   }
   typename A::Frag bq[1][A::NS];
   {
@@ -663,7 +713,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       // keys of a selected block already count in that block's partial
       const int32_t blk = int32_t(key0 / B);
       bool excl = false;
-      for (int i = 0; i < k; ++i) excl |= sidx[r * k + i] == blk;
+      for (int i = 0; i < k; ++i) excl |= sidx[i * kWinRows + r] == blk;
       const int64_t tv = valid ? t : -(int64_t(1) << 40);
       attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
                               [&](int, int mt, int a, int bb) {
@@ -679,14 +729,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const float lw = ws.l + wave_shfl_xor(ws.l, 32);
   float M = lw > 0.f ? ws.m2 + __log2f(lw) : -__builtin_inff();
   for (int i = 0; i < k; ++i)
-    if (sidx[r * k + i] >= 0) M = fmaxf(M, lse_part[orow * k + i].x);
+    if (sidx[i * kWinRows + r] >= 0) M = fmaxf(M, lse_part[orow * k + i].x);
   const float ww = lw > 0.f ? __builtin_amdgcn_exp2f(ws.m2 - M) : 0.f;
   float den = ww * lw;
   const float wws = ldexpf(ww, ev);   // the window's values were scaled by 2^-ev
 #pragma unroll
   for (int mt = 0; mt < A::MTD; ++mt) ws.o[mt] *= wws;
   for (int i = 0; i < k; ++i) {
-    if (sidx[r * k + i] < 0) continue;
+    if (sidx[i * kWinRows + r] < 0) continue;
     const int64_t pidx = orow * k + i;
     const float2 le = lse_part[pidx];
     const float wi = __builtin_amdgcn_exp2f(le.x - M);
@@ -706,6 +756,18 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 }
 
 // ------------------------------------------------------------------ launch --
+
+// Compute units of the current device (queried once; a launch-shape hint only).
+int num_cus() {
+  static const int cus = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      return v;
+    return 256;
+  }();
+  return cus;
+}
 
 struct AttnWs {
   uint32_t* vmax;
@@ -804,7 +866,8 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(bk),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(bshm))) != hipSuccess)
       return e;
-    const int64_t grid = (w.max_tasks + 7) / 8 * 8;
+    // persistent: two workgroups per CU, a multiple of the 8 XCDs
+    const int64_t grid = std::min<int64_t>((w.max_tasks + 7) / 8 * 8, int64_t(num_cus()) * 2 / 8 * 8);
     hipLaunchKernelGGL(bk, dim3(unsigned(grid)), dim3(kAttnThreads), bshm, st, Q, w.img, w.n_chunks,
                        w.tasks,
                        w.task_count, w.entries, w.vmax, static_cast<PartT*>(w.o_part), w.lse_part, s.n,
