@@ -184,6 +184,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 2 GiB device->device (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -192,6 +194,16 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 31
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}), flush=True)
+        return 0
 
     import content_routed_block_stats_amd as ssa
     from synth_inputs import CONFIGS, make_prefill

@@ -1,0 +1,154 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (the same C ABI calls on inputs resident in HBM).
+
+The oracle cannot evaluate millions of rows, so every row is checked for the
+properties a selection has at any size (ascending, distinct, routable,
+exactly min(k, #routable) entries), and a stratified sample of rows -- every
+q-head at uniform positions including the first and last tiles, plus rows
+whose query a planted outlier targets -- is compared one by one with the
+oracle under the rules in parity.py.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import content_routed_block_stats_amd as ssa
+import oracle as O
+from parity import LSE_TOL, O_TOL, STATS_REL, attn_errors, check_idx_properties, idx_ok
+from synth_inputs import CONFIGS, make_decode, make_prefill
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _sample_rows(wl, per_head: int, plants: list[dict], n_plants: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    n = wl.seq_len
+    for h in range(wl.n_q_heads):
+        ts = list(rng.integers(0, n, size=per_head)) + [int(rng.integers(0, 256)), n - 1 - int(rng.integers(0, 256))]
+        for t in ts:
+            rows.add((0, h, int(t)))
+    pick = rng.permutation(len(plants))[:n_plants]
+    for i in pick:
+        p = plants[i]
+        rows.add((p["b"], p["h"], p["t"]))
+    return sorted(rows)
+
+
+def _prefill_fullsize(name: str, per_head: int, n_plants: int, stats_blocks: int):
+    wl = CONFIGS[name]
+    say(f"case {name}: generating on the GPU")
+    data = make_prefill(wl, seed=0, device=DEV)
+    Q, K, V = data["Q"], data["K"], data["V"]
+    say("  block stats / route / attention")
+    mu, sigma = ssa.ssa_block_stats(K, wl.block)
+    idx = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta)
+    Oo, lse = ssa.ssa_sparse_attn_fwd(Q, K, V, idx, block_size=wl.block, window=wl.window,
+                                      scale=wl.scale)
+    torch.cuda.synchronize()
+    say("  selection properties on every row")
+    idx_h = idx.cpu().numpy()
+    check_idx_properties(idx_h[0], wl.seq_len, wl.block, wl.top_k)
+    del idx
+    p = O.Params(wl.block, wl.top_k, wl.window, wl.beta, wl.scale)
+    rows = _sample_rows(wl, per_head, data["plants"], n_plants)
+    say(f"  oracle on {len(rows)} sampled rows")
+    g = wl.group
+    by_kv: dict[int, list] = {}
+    for (b, h, t) in rows:
+        by_kv.setdefault(h // g, []).append((b, h, t))
+    n_exact = n_tie = 0
+    worst_o = worst_l = 0.0
+    bf16_out = Oo.dtype == torch.bfloat16
+    rng = np.random.default_rng(1)
+    for kv, kv_rows in sorted(by_kv.items()):
+        Kh = O.as_f64(K[0, kv])
+        Vh = O.as_f64(V[0, kv])
+        mu_o, sg_o = O.block_stats(Kh, wl.block)
+        # statistics of sampled blocks
+        for c in rng.choice(mu_o.shape[0], size=min(stats_blocks, mu_o.shape[0]), replace=False):
+            scale_s = max(1.0, np.abs(sg_o[c]).max())
+            assert np.abs(mu[0, kv, c].double().cpu().numpy() - mu_o[c]).max() <= STATS_REL * scale_s
+            assert np.abs(sigma[0, kv, c].double().cpu().numpy() - sg_o[c]).max() <= STATS_REL * scale_s
+        for (b, h, t) in kv_rows:
+            q = O.as_f64(Q[0, h, t])
+            row = O.prefill_row(q, Kh, Vh, mu_o, sg_o, p, t)
+            ok, exact = idx_ok(idx_h[0, h, t], row)
+            assert ok, f"selection mismatch at {(h, t)}: {idx_h[0, h, t]} vs {row['idx']}"
+            n_exact += exact
+            n_tie += not exact
+            eo, el = attn_errors(Oo[0, h, t].float().cpu().numpy(), float(lse[0, h, t]), q, Kh, Vh,
+                                 idx_h[0, h, t], t, p, bf16_out=bf16_out)
+            worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+            assert eo <= O_TOL[wl.dtype], f"O error {eo:.3g} at {(h, t)}"
+            assert el <= LSE_TOL, f"LSE error {el:.3g} at {(h, t)}"
+        say(f"  kv head {kv}: {len(kv_rows)} rows ok")
+    say(f"  {name}: exact {n_exact}, near-ties {n_tie}, max|dO| {worst_o:.3g}, "
+        f"max|dLSE| {worst_l:.3g}")
+
+
+@pytest.mark.timeout(600)
+def test_prefill_32k_fullsize():
+    _prefill_fullsize("prefill_32k", per_head=24, n_plants=48, stats_blocks=16)
+
+
+@pytest.mark.timeout(600)
+def test_gqa_prefill_128k_fullsize():
+    _prefill_fullsize("gqa_prefill_128k", per_head=8, n_plants=48, stats_blocks=8)
+
+
+@pytest.mark.timeout(900)
+def test_long_prefill_1m_fullsize():
+    _prefill_fullsize("long_prefill_1m", per_head=4, n_plants=16, stats_blocks=4)
+
+
+@pytest.mark.timeout(900)
+def test_decode_256k_fullsize():
+    wl = CONFIGS["decode_256k"]
+    L = wl.seq_len
+    say("case decode_256k: generating the 32 x 262144-token caches on the GPU")
+    data = make_decode(wl, seed=0, device=DEV, capacity=L + 64)
+    Kc, Vc = data["K_cache"], data["V_cache"]
+    mu, sigma = ssa.ssa_block_stats(Kc, wl.block)
+    cache_len = torch.full((wl.batch,), L, dtype=torch.int32, device=DEV)
+    q, kn, vn = data["q"], data["k_new"], data["v_new"]
+    say("  decode step")
+    o, lse, idx = ssa.ssa_decode_step(q, kn, vn, Kc, Vc, cache_len, mu, sigma, block_size=wl.block,
+                                      top_k=wl.top_k, window=wl.window, beta=wl.beta,
+                                      scale=wl.scale, return_idx=True)
+    torch.cuda.synchronize()
+    assert cache_len.cpu().tolist() == [L + 1] * wl.batch
+    idx_h = idx.cpu().numpy()
+    nbc = (L + 1) // wl.block
+    valid = idx_h >= 0
+    assert np.all(valid.sum(-1) == min(wl.top_k, nbc))
+    assert np.all(np.where(valid, idx_h < nbc, True))
+    assert np.all(np.diff(idx_h, axis=-1) > 0)
+    p = O.Params(wl.block, wl.top_k, wl.window, wl.beta, wl.scale)
+    rng = np.random.default_rng(0)
+    pairs = [(int(b), int(kv)) for b, kv in zip(rng.choice(wl.batch, 4, replace=False),
+                                                rng.integers(0, wl.n_kv_heads, 4))]
+    bf16_out = o.dtype == torch.bfloat16
+    for (b, kv) in pairs:
+        Kh = Kc[b, kv, :L].cpu()
+        Vh = Vc[b, kv, :L].cpu()
+        for h in range(kv * wl.group, (kv + 1) * wl.group):
+            row = O.decode_step(q[b, h], kn[b, kv], vn[b, kv], Kh, Vh, L, p)
+            ok, _ = idx_ok(idx_h[b, h], row)
+            assert ok, f"decode selection mismatch b={b} h={h}"
+            Kfull = np.concatenate([O.as_f64(Kh), O.as_f64(kn[b, kv])[None]])
+            Vfull = np.concatenate([O.as_f64(Vh), O.as_f64(vn[b, kv])[None]])
+            eo, el = attn_errors(o[b, h].float().cpu().numpy(), float(lse[b, h]), O.as_f64(q[b, h]),
+                                 Kfull, Vfull, idx_h[b, h], L, p, bf16_out=bf16_out)
+            assert eo <= O_TOL[wl.dtype] and el <= LSE_TOL, (b, h, eo, el)
+        say(f"  sequence {b} kv head {kv}: {wl.group} rows ok")
