@@ -45,8 +45,8 @@ def gather_bytes(wl) -> float:
 
     Per selected (row, block): the query row (2d bytes, bf16) read by the
     block's task, the fp16 partial written and read back (2 * (2d + 8)), the
-    idx entry read twice by the dispatch (8) and its sorted entry written and
-    read (8).  Per row: the query row for the window pass (2d), the idx row
+    idx entry read twice by the dispatch (8), its sorted entry written and
+    read (8) and the partial's position written and read (8).  Per row: the query row for the window pass (2d), the idx row
     (4k), O written (2d) and LSE (4).  Per (sequence, KV head): K and V read
     once for the blocks and once for the windows (4 * n * d * 2).
     """
@@ -55,7 +55,7 @@ def gather_bytes(wl) -> float:
     sel_per_head = sum(min(k, min(nb, (t + 1) // B)) for t in range(n))
     rows = wl.batch * wl.n_q_heads * n
     sel = wl.batch * wl.n_q_heads * sel_per_head
-    per_sel = 2 * d + 2 * (2 * d + 8) + 8 + 8
+    per_sel = 2 * d + 2 * (2 * d + 8) + 8 + 8 + 8
     per_row = 2 * d + 4 * k + 2 * d + 4
     kv = wl.batch * wl.n_kv_heads * 4 * n * d * 2
     return float(sel * per_sel + rows * per_row + kv)

@@ -9,13 +9,15 @@
 //
 //  1. dispatch  -- a counting sort of (query row, slot) pairs by selected
 //     (sequence, KV head, block): per-workgroup LDS histograms, one exclusive
-//     scan that also cuts every block's row list into tasks of at most
-//     kTaskRows rows, and a scatter into the sorted entry list;
-//  2. block attention -- one workgroup per task stages its block's K and V
-//     once in LDS (64-key chunks, double-buffered), gathers the task's query
-//     rows into MFMA registers, and writes one normalised partial per
-//     (row, slot): o_i = softmax-weighted values over the block and
-//     lse_i (base 2);
+//     scan that cuts every block's row list into tasks of at most kTaskRows
+//     rows, and a scatter into the task-ordered entry list (task j owns
+//     entries [j kTaskRows, (j + 1) kTaskRows)) that also records, per
+//     (row, slot), where its partial will be;
+//  2. block attention -- persistent workgroups keep a block's K and V images
+//     resident in LDS across consecutive tasks of that block, gather each
+//     task's query rows into MFMA registers, and write one normalised
+//     partial per entry (contiguous per task): o_i = softmax-weighted values
+//     over the block and lse_i (base 2);
 //  3. window + merge -- one workgroup per tile of consecutive query rows of a
 //     KV head computes the window part as dense local attention (keys of
 //     selected blocks masked out, so every key of S(t) counts once), then
@@ -35,9 +37,12 @@
 namespace ssa {
 namespace {
 
-constexpr int kAttnThreads = 256;          // 4 waves, 32 query rows each
-constexpr int kTaskTiles = 1;              // 32-row MFMA tiles per wave in a task
-constexpr int kTaskRows = 4 * 32 * kTaskTiles;   // rows per block-attention task
+constexpr int kAttnThreads = 256;          // window pass: 4 waves, 32 query rows each
+constexpr int kBlockThreads = 512;         // block pass: 8 waves, 32 query rows each
+constexpr int kTaskRows = 256;             // rows per block-attention task
+constexpr int kResidentBytes = 128 * 1024; // LDS that keeps a block's K/V images resident
+constexpr int kStageBytes = 4096;          // LDS per wave that lines partials up for storing
+constexpr float kLazyLog2 = 8.f;           // probabilities may reach 2^kLazyLog2 before a rescale
 constexpr int kWinRows = 128;              // rows per window/merge tile
 constexpr int kKeyChunk = 64;              // keys per LDS chunk
 constexpr int kHistTokens = 2048;          // tokens per dispatch workgroup
@@ -63,6 +68,17 @@ struct AT {
 
 // ---------------------------------------------------------------- helpers --
 
+// Copy `bytes` (a multiple of 1 KB) from global memory into LDS with direct
+// global->LDS loads: each wave moves 1 KB per instruction, waves interleave.
+__device__ __forceinline__ void dma_copy(uint8_t* lds, const uint8_t* src, int bytes, int tid,
+                                         int nthreads) {
+  const int wave = tid / 64, lane = tid % 64, waves = nthreads / 64;
+  for (int r = wave; r < bytes / 1024; r += waves)
+    __builtin_amdgcn_global_load_lds(src + r * 1024 + lane * 16,
+                                     (__attribute__((address_space(3))) void*)(lds + r * 1024), 16,
+                                     0, 0);
+}
+
 template <bool F32, int D>
 __device__ __forceinline__ typename AT<F32, D>::Frag load_row_frag(const typename AT<F32, D>::In* row,
                                                                    int s, int h, bool valid) {
@@ -70,8 +86,8 @@ __device__ __forceinline__ typename AT<F32, D>::Frag load_row_frag(const typenam
   if constexpr (F32) {
     floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
     if (valid) {
-      a = *reinterpret_cast<const floatx4*>(row + 16 * s + 4 * h);
-      b = *reinterpret_cast<const floatx4*>(row + 16 * s + 8 + 4 * h);
+      a = *reinterpret_cast<const floatx4*>(row + 16 * s + 8 * h);
+      b = *reinterpret_cast<const floatx4*>(row + 16 * s + 8 * h + 4);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -79,12 +95,8 @@ __device__ __forceinline__ typename AT<F32, D>::Frag load_row_frag(const typenam
       v[e + 4] = b[e];
     }
   } else {
-    u32x2 a = {0u, 0u}, b = a;
-    if (valid) {
-      a = *reinterpret_cast<const u32x2*>(row + 16 * s + 4 * h);
-      b = *reinterpret_cast<const u32x2*>(row + 16 * s + 8 + 4 * h);
-    }
-    u32x4 w = {a[0], a[1], b[0], b[1]};
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (valid) w = *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * h);
     v = __builtin_bit_cast(bf16x8, w);
   }
   return v;
@@ -92,7 +104,7 @@ __device__ __forceinline__ typename AT<F32, D>::Frag load_row_frag(const typenam
 
 // Keys [key0, key0 + 64) of one head (rows >= n_keys read as zero), staged in
 // LDS as MFMA A-operand fragments:
-//   K part: fragment (mt, s), lane (m, h), element e = K[key0 + 32mt + m][frag_k(s,h,e)]
+//   K part: fragment (mt, s), lane (m, h), element e = K[key0 + 32mt + m][16s + 8h + e]
 //   V part: fragment (mt, s), lane (m, h), element e = V[key0 + frag_k(s,h,e)][32mt + m]
 // K moves in 4-element pieces, assigned so that the 64 lanes of one LDS store
 // fill 512 contiguous bytes (no bank conflicts).  V is transposed through
@@ -130,7 +142,7 @@ struct ChunkRegs {
       const int r = 32 * mt + m;
       k[i] = PieceT{};
       if (key0 + r < n_keys)
-        k[i] = *reinterpret_cast<const PieceT*>(Kh + (key0 + r) * D + 16 * s + 8 * sel + 4 * h);
+        k[i] = *reinterpret_cast<const PieceT*>(Kh + (key0 + r) * D + 16 * s + 8 * h + 4 * sel);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -294,10 +306,18 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
           mloc = fmaxf(mloc, v);
         }
     mloc = fmaxf(mloc, wave_shfl_xor(mloc, 32)) * scale2;
-    const float mnew = fmaxf(st[nt].m2, mloc);
-    const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(st[nt].m2 - mref);
-    st[nt].m2 = mnew;
+    // Lazy rescaling: the reference m2 moves (and o, l are rescaled) only
+    // when some row of the wave sees a logit more than kLazyLog2 above it, so
+    // probabilities stay below 2^kLazyLog2 and most chunks skip the rescale.
+    if (__builtin_amdgcn_ballot_w64(mloc > st[nt].m2 + kLazyLog2) != 0) {
+      const float mnew = fmaxf(st[nt].m2, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(st[nt].m2 - (mnew == -__builtin_inff() ? 0.f : mnew));
+      st[nt].m2 = mnew;
+      st[nt].l *= alpha;
+#pragma unroll
+      for (int i = 0; i < A::MTD; ++i) st[nt].o[i] *= alpha;
+    }
+    const float mref = st[nt].m2 == -__builtin_inff() ? 0.f : st[nt].m2;
     float lsum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -307,9 +327,7 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
         sacc[nt][mt][j] = p;
         lsum += p;
       }
-    st[nt].l = st[nt].l * alpha + lsum;
-#pragma unroll
-    for (int i = 0; i < A::MTD; ++i) st[nt].o[i] *= alpha;
+    st[nt].l += lsum;
   }
   // P as the B operand of O^T += V^T P^T: chunk s' covers keys 16s'..16s'+15.
   // The MTD output tiles are independent chains; V fragments are read one
@@ -342,36 +360,69 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
   }
 }
 
-// A lane's half of one partial: the D/2 values of the lane half's columns,
-// in accumulator order, written / read as 16-byte vectors.
-template <typename PartT, int MTD>
-__device__ __forceinline__ void store_partial(PartT* dst, const floatx16 (&o)[MTD], float sc) {
-  if constexpr (sizeof(PartT) == 4) {
+// The partials of a wave's 32 rows (row r: D values, lane half h holds
+// columns h D/2 .. in accumulator order, one row after the other in global
+// memory).  A lane's registers hold one half row, so storing them directly
+// would give each store instruction 64 scattered 16-byte pieces; instead the
+// rows pass through kStageBytes of LDS per wave (rounds of kStageBytes / row
+// bytes rows, 16-byte chunks XOR-swizzled by row against bank conflicts) and
+// leave as fully contiguous 1 KB stores.  Lanes read what other lanes of the
+// wave wrote, so every round is fenced at wavefront scope on both sides: LDS
+// keeps a wave's accesses in order, the fences keep the compiler from reusing
+// earlier loads or moving accesses across them.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename PartT, int D>
+__device__ __forceinline__ void store_partials(uint8_t* stage, PartT* dst, const floatx16 (&o)[D / 32],
+                                               float sc, int ln, int h, int lane) {
+  constexpr int ROWB = D * int(sizeof(PartT));     // bytes per row
+  constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
+  constexpr int HALF = CH / 2;                     // chunks per lane half
+  constexpr int R = kStageBytes / ROWB;            // rows per round
+  auto chunk = [&](int j) {
+    u32x4 w;
+    if constexpr (sizeof(PartT) == 4) {
+      const int mt = j / 4, q = j % 4;
 #pragma unroll
-    for (int mt = 0; mt < MTD; ++mt)
+      for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, o[mt][4 * q + i] * sc);
+    } else {
+      const int mt = j / 2, q = j % 2;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        reinterpret_cast<floatx4*>(dst)[mt * 4 + q] =
-            floatx4{o[mt][4 * q] * sc, o[mt][4 * q + 1] * sc, o[mt][4 * q + 2] * sc,
-                    o[mt][4 * q + 3] * sc};
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MTD; ++mt)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        u32x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = o[mt][8 * q + 2 * i] * sc, b2 = o[mt][8 * q + 2 * i + 1] * sc;
-          w[i] = uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(a))) |
-                 (uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(b2))) << 16);
-        }
-        reinterpret_cast<u32x4*>(dst)[mt * 2 + q] = w;
+      for (int i = 0; i < 4; ++i) {
+        const float a = o[mt][8 * q + 2 * i] * sc, b2 = o[mt][8 * q + 2 * i + 1] * sc;
+        w[i] = uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(a))) |
+               (uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(b2))) << 16);
       }
+    }
+    return w;
+  };
+#pragma unroll
+  for (int rd = 0; rd < 32 / R; ++rd) {
+    wave_lds_sync();
+    if (ln / R == rd) {
+      const int ri = ln % R;
+#pragma unroll
+      for (int j = 0; j < HALF; ++j) {
+        const int c = h * HALF + j;
+        *reinterpret_cast<u32x4*>(stage + ri * ROWB + ((c ^ (ri & (CH - 1))) * 16)) = chunk(j);
+      }
+    }
+    wave_lds_sync();
+    uint8_t* out = reinterpret_cast<uint8_t*>(dst) + rd * kStageBytes;
+#pragma unroll
+    for (int k = 0; k < kStageBytes / 1024; ++k) {
+      const int pc = k * 64 + lane, ri = pc / CH, c = pc % CH;
+      *reinterpret_cast<u32x4*>(out + pc * 16) =
+          *reinterpret_cast<const u32x4*>(stage + ri * ROWB + ((c ^ (ri & (CH - 1))) * 16));
+    }
   }
 }
 
-// o += w * partial (the lane half's values, same order as store_partial).
+// o += w * partial (the lane half's values, in the order store_partials writes).
 template <typename PartT, int MTD>
 __device__ __forceinline__ void accumulate_partial(floatx16 (&o)[MTD], const PartT* src, float w) {
   if constexpr (sizeof(PartT) == 4) {
@@ -430,12 +481,15 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {
 
 // SCATTER = false: add this workgroup's histogram of selected blocks into
 // counts.  SCATTER = true: reserve ranges at cursor and write entries
-// (row id << 5 | slot) into the per-block lists.  A workgroup covers
-// kHistTokens tokens of one (sequence, KV head) and all its group's q-heads.
+// (row id << 5 | slot) into the per-block lists, and the entry position of
+// every selected (row, slot) into pos (same layout as idx).  A workgroup
+// covers kHistTokens tokens of one (sequence, KV head) and all its group's
+// q-heads.
 template <bool SCATTER>
 __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ counts_or_cursor,
-                                                       uint32_t* __restrict__ entries, int64_t n,
+                                                       uint32_t* __restrict__ entries,
+                                                       int32_t* __restrict__ pos, int64_t n,
                                                        int g, int hq, int hkv, int k, int64_t nb) {
   extern __shared__ int32_t hist[];
   const int tid = threadIdx.x;
@@ -464,71 +518,61 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   if (!SCATTER) return;
   __syncthreads();
   for (int j = 0; j < g; ++j) {
-    const int32_t* base = idx + ((b * hq + kv * g + j) * n) * k;
+    const int64_t base = ((b * hq + kv * g + j) * n) * k;
     for (int64_t t = t0 + tid; t < t1; t += 256)
       for (int i = 0; i < k; ++i) {
-        const int32_t c = base[t * k + i];
+        const int32_t c = idx[base + t * k + i];
         if (c >= 0 && c < nb) {
-          const int32_t pos = atomicAdd(&hist[c], 1);
-          entries[pos] = (uint32_t(t * g + j) << 5) | uint32_t(i);
+          const int32_t e = atomicAdd(&hist[c], 1);
+          entries[e] = (uint32_t(t * g + j) << 5) | uint32_t(i);
+          pos[base + t * k + i] = e;
         }
       }
   }
 }
 
-// Exclusive scan of the per-block counts (segment offsets, also copied to the
-// scatter cursor) and of their task counts; emits the task list in block
-// order: task = (segment, first entry, rows).
+// Exclusive scan of the per-block task counts; emits the task list in block
+// order, task j = (segment, first entry j kTaskRows, rows), and points the
+// scatter cursor of every segment at its first task's entries.
 __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
     const int32_t* __restrict__ counts, int32_t* __restrict__ cursor, int4* __restrict__ tasks,
     int32_t* __restrict__ task_count, int64_t nseg) {
   constexpr int ITEMS = 4;
-  __shared__ int32_t sc[kScanThreads], st[kScanThreads];
-  __shared__ int32_t carry_c, carry_t;
+  __shared__ int32_t st[kScanThreads];
+  __shared__ int32_t carry_t;
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    carry_c = 0;
-    carry_t = 0;
-  }
+  if (tid == 0) carry_t = 0;
   __syncthreads();
   for (int64_t base = 0; base < nseg; base += int64_t(kScanThreads) * ITEMS) {
-    int32_t c[ITEMS], tk[ITEMS], sum_c = 0, sum_t = 0;
+    int32_t c[ITEMS], tk[ITEMS], sum_t = 0;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       const int64_t s = base + int64_t(tid) * ITEMS + i;
       c[i] = s < nseg ? counts[s] : 0;
       tk[i] = (c[i] + kTaskRows - 1) / kTaskRows;
-      sum_c += c[i];
       sum_t += tk[i];
     }
-    sc[tid] = sum_c;
     st[tid] = sum_t;
     __syncthreads();
     for (int off = 1; off < kScanThreads; off <<= 1) {
-      const int32_t vc = tid >= off ? sc[tid - off] : 0;
       const int32_t vt = tid >= off ? st[tid - off] : 0;
       __syncthreads();
-      sc[tid] += vc;
       st[tid] += vt;
       __syncthreads();
     }
-    int32_t oc = carry_c + sc[tid] - sum_c, ot = carry_t + st[tid] - sum_t;
+    int32_t ot = carry_t + st[tid] - sum_t;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       const int64_t s = base + int64_t(tid) * ITEMS + i;
       if (s < nseg) {
-        cursor[s] = oc;
+        cursor[s] = ot * kTaskRows;
         for (int q = 0; q < tk[i]; ++q)
-          tasks[ot + q] = int4{int32_t(s), oc + q * kTaskRows, min(kTaskRows, c[i] - q * kTaskRows), 0};
+          tasks[ot + q] = int4{int32_t(s), (ot + q) * kTaskRows, min(kTaskRows, c[i] - q * kTaskRows), 0};
       }
-      oc += c[i];
       ot += tk[i];
     }
     __syncthreads();
-    if (tid == kScanThreads - 1) {
-      carry_c += sc[tid];
-      carry_t += st[tid];
-    }
+    if (tid == kScanThreads - 1) carry_t += st[tid];
     __syncthreads();
   }
   if (tid == 0) task_count[0] = carry_t;
@@ -536,90 +580,105 @@ __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
 
 // ---------------------------------------------------------- block attention --
 
-// Persistent: the tasks of one XCD form a contiguous range (consecutive tasks
-// share a block, so its images stay in that XCD's L2), dealt round-robin to
-// the XCD's workgroups.  While a task runs, the next task's first chunk is
-// staged during the last chunk, its row entries are fetched during chunk 0
-// and its query rows during chunk 1, so a task's start-up latency hides
-// behind the previous task's compute.
+// Persistent, one workgroup per CU.  The tasks of one XCD form a contiguous
+// range (task order is block order) and each workgroup takes a contiguous
+// slice of it, so consecutive tasks of a workgroup mostly share a block.  A
+// block's K/V images (up to kResidentBytes, i.e. 256 keys at d = 128 bf16)
+// stay resident in LDS and are re-staged only when the block (or, for larger
+// blocks, the 256-key segment) changes; within a segment the chunks need no
+// barriers.  The next task's row entries are fetched at the start of a task
+// and its query rows after the first chunk, so they arrive behind compute.
 template <bool F32, int D, typename PartT>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void block_attn_kernel(
+__global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
     int64_t n_chunks, const int4* __restrict__ tasks,
     const int32_t* __restrict__ task_count, const uint32_t* __restrict__ entries,
     const uint32_t* __restrict__ vmax, PartT* __restrict__ o_part, float2* __restrict__ lse_part,
-    int64_t n, int g, int hq, int hkv, int B, int64_t nb, int k, float scale2) {
+    int64_t n, int g, int hq, int hkv, int B, int64_t nb, float scale2) {
   using A = AT<F32, D>;
   using Frag = typename A::Frag;
+  constexpr int SEG_CHUNKS = kResidentBytes / A::CHUNK;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int64_t T = *task_count;
   const int64_t per_xcd = (T + 7) / 8;
-  const int64_t x = blockIdx.x;
+  const int64_t x = blockIdx.x, nw = gridDim.x / 8;
   const int64_t xb = (x % 8) * per_xcd, xe = min(T, xb + per_xcd);
-  const int64_t stride = gridDim.x / 8;
-  int64_t ti = xb + x / 8;
-  if (ti >= xe) return;
+  const int64_t per_wg = (xe - xb + nw - 1) / nw;
+  const int64_t tb = xb + (x / 8) * per_wg, te = min(xe, tb + per_wg);
+  if (tb >= te) return;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int r = 32 * wave + ln;             // this lane's row within a task
-  const int nchunks = B / kKeyChunk;
+  const int block_chunks = B / kKeyChunk;
+  const int seg_chunks = min(block_chunks, SEG_CHUNKS);
+  const int segs = (block_chunks + seg_chunks - 1) / seg_chunks;
 
-  auto image_of = [&](const int4& tk) {
+  auto image_of = [&](const int4& tk, int seg) {
     const int64_t bkv = tk.x / nb, c = tk.x % nb;
-    return img + (bkv * n_chunks + c * (B / kKeyChunk)) * A::CHUNK;
+    return img + (bkv * n_chunks + c * block_chunks + int64_t(seg) * seg_chunks) * A::CHUNK;
   };
-  // the query row of entry code for task tk: global row index and slot
-  auto row_of = [&](const int4& tk, uint32_t code, int64_t& orow, int& slot) {
+  // query row of an entry (row id << 5 | slot) of task tk
+  auto row_of = [&](const int4& tk, uint32_t code) {
     const int64_t bkv = tk.x / nb, b = bkv / hkv, kv = bkv % hkv;
     const int64_t rho = code >> 5;
-    slot = int(code & 31u);
-    orow = (b * hq + kv * g + rho % g) * n + rho / g;
+    return (b * hq + kv * g + rho % g) * n + rho / g;
   };
 
-  int4 task = tasks[ti];
-  uint32_t code = r < task.z ? entries[task.y + r] : 0u;
-  int64_t orow;
-  int slot;
-  row_of(task, code, orow, slot);
+  // Software pipeline over tasks.  At the top of task i the query rows of
+  // task i+1 and the row entries of task i+2 are requested; they arrive
+  // while task i computes and are taken (bq, orow_n) only after task i's
+  // partials are stored.  Entry and partial slots are padded to kTaskRows per
+  // task, so every lane loads and stores unconditionally (lanes past a task's
+  // rows read row 0 and write that task's padding): no branch in the loop
+  // issues vector memory operations, so the waits at the end of a task count
+  // exactly and never wait for the stores just issued (vector loads and
+  // stores share one completion counter).
+  int4 task = tasks[tb];
+  int64_t orow_n;
   Frag bq[1][A::NS];
+  {
+    const uint32_t code = entries[int64_t(tb) * kTaskRows + r];
+    const int64_t orow = row_of(task, r < task.z ? code : 0u);
 #pragma unroll
-  for (int s = 0; s < A::NS; ++s) bq[0][s] = load_row_frag<F32, D>(Q + orow * D, s, h, r < task.z);
-  stage_chunk_dma<F32, D>(lds, image_of(task), tid);
-  int buf = 0;
-  __syncthreads();
+    for (int s = 0; s < A::NS; ++s) bq[0][s] = load_row_frag<F32, D>(Q + orow * D, s, h, true);
+  }
+  int4 task_n = tb + 1 < te ? tasks[tb + 1] : task;
+  {
+    const uint32_t code = entries[min(tb + 1, te - 1) * kTaskRows + r];
+    orow_n = row_of(task_n, tb + 1 < te && r < task_n.z ? code : 0u);
+  }
+  // enter the loop with nothing in flight, as every later iteration does
+  __builtin_amdgcn_s_waitcnt(0);
+  int64_t resident = -1;                    // segment id held in LDS
 
-  while (true) {
-    const int64_t tn = ti + stride;
-    const bool has_next = tn < xe;
-    const int4 task_n = has_next ? tasks[tn] : int4{0, 0, 0, 0};
-    const uint8_t* src = image_of(task);
-    const bool valid = r < task.z, wave_active = 32 * wave < task.z;
-    const int ev = F32 ? 0 : value_exponent(vmax[task.x / nb]);
-    uint32_t code_n = 0;
-    int64_t orow_n = 0;
-    int slot_n = 0;
+  for (int64_t ti = tb; ti < te; ++ti) {
+    // (a) next task's query rows, the entries of the task after it
     Frag bqn[A::NS];
+#pragma unroll
+    for (int s = 0; s < A::NS; ++s) bqn[s] = load_row_frag<F32, D>(Q + orow_n * D, s, h, true);
+    const bool has_nn = ti + 2 < te;
+    const int4 task_nn = has_nn ? tasks[ti + 2] : task;
+    const uint32_t code_nn = entries[min(ti + 2, te - 1) * kTaskRows + r];
+    // (b) this task: every chunk of its block against 8 x 32 query rows
+    const bool wave_active = 32 * wave < task.z;
+    const int ev = F32 ? 0 : value_exponent(vmax[task.x / nb]);
     RowState<D> st[1];
     row_state_init(st[0]);
-    for (int ch = 0; ch < nchunks; ++ch) {
-      uint8_t* nbuf = lds + (buf ^ 1) * A::CHUNK;
-      if (ch + 1 < nchunks)
-        stage_chunk_dma<F32, D>(nbuf, src + (ch + 1) * A::CHUNK, tid);
-      else if (has_next)
-        stage_chunk_dma<F32, D>(nbuf, image_of(task_n), tid);
-      if (ch == 0 && has_next && r < task_n.z) code_n = entries[task_n.y + r];
-      if (ch == (nchunks > 1 ? 1 : 0) && has_next) {
-        row_of(task_n, code_n, orow_n, slot_n);
-#pragma unroll
-        for (int s = 0; s < A::NS; ++s)
-          bqn[s] = load_row_frag<F32, D>(Q + orow_n * D, s, h, r < task_n.z);
+    for (int sg = 0; sg < segs; ++sg) {
+      const int64_t sid = int64_t(task.x) * segs + sg;
+      const int here = min(seg_chunks, block_chunks - sg * seg_chunks);
+      if (sid != resident) {
+        __syncthreads();                    // every wave is done with the old segment
+        dma_copy(lds, image_of(task, sg), here * A::CHUNK, tid, kBlockThreads);
+        __syncthreads();                    // the new segment is in LDS
+        resident = sid;
       }
       if (wave_active)
-        attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
-                                [](int, int, int, int) { return true; });
-      __syncthreads();
-      buf ^= 1;
+        for (int ch = 0; ch < here; ++ch)
+          attend_chunk<F32, D, 1>(lds + ch * A::CHUNK, bq, scale2, lane, st,
+                                  [](int, int, int, int) { return true; });
     }
-    if (valid) {
+    // (c) the normalised partial of every row of the task
+    {
       const float l = st[0].l + wave_shfl_xor(st[0].l, 32);
       const float inv = 1.f / l;
       // the partial is a convex combination of value rows; half-precision
@@ -634,15 +693,15 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       int e = 0;
       if (!F32 && mx > 0.f) (void)frexpf(mx, &e);
       const float sc = ldexpf(inv, -e);
-      const int64_t pidx = orow * k + slot;
-      store_partial<PartT>(o_part + pidx * D + h * (D / 2), st[0].o, sc);
-      if (h == 0) lse_part[pidx] = float2{st[0].m2 + __log2f(l), float(e + ev)};
+      const int64_t pidx = ti * kTaskRows + r;
+      store_partials<PartT, D>(lds + kResidentBytes + wave * kStageBytes,
+                               o_part + (pidx - ln) * D, st[0].o, sc, ln, h, lane);
+      lse_part[pidx] = float2{st[0].m2 + __log2f(l), float(e + ev)};
     }
-    if (!has_next) break;
-    ti = tn;
+    // (d) rotate the pipeline
     task = task_n;
-    orow = orow_n;
-    slot = slot_n;
+    task_n = task_nn;
+    orow_n = row_of(task_nn, has_nn && r < task_nn.z ? code_nn : 0u);
 #pragma unroll
     for (int s = 0; s < A::NS; ++s) bq[0][s] = bqn[s];
   }
@@ -653,13 +712,15 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 template <bool F32, int D, typename PartT, typename OutT>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void window_merge_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
-    int64_t n_chunks, const int32_t* __restrict__ idx, const uint32_t* __restrict__ vmax, const PartT* __restrict__ o_part,
+    int64_t n_chunks, const int32_t* __restrict__ idx, const int32_t* __restrict__ pos,
+    const uint32_t* __restrict__ vmax, const PartT* __restrict__ o_part,
     const float2* __restrict__ lse_part, OutT* __restrict__ O,
     float* __restrict__ lse, int64_t n, int g, int hq, int hkv, int B, int k, int W,
     float scale2, int64_t n_tiles) {
   using A = AT<F32, D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int32_t* sidx = reinterpret_cast<int32_t*>(lds + 2 * A::CHUNK);   // [k][kWinRows]
+  int32_t* spos = sidx + kWinRows * k;                                // [k][kWinRows]
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int64_t bkv = blockIdx.x / n_tiles;
   const int64_t tile = blockIdx.x % n_tiles;
@@ -682,12 +743,15 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   for (int w = tid; w < kWinRows * k; w += kAttnThreads) {
     const int rr = w / k, i = w % k;   // coalesced idx reads, transposed LDS writes
     const int64_t rh = rho0 + rr;
-    int32_t v = -1;
+    int32_t v = -1, e = 0;
     if (rh < rows_total) {
       const int64_t tt = rh / g, jj = rh % g;
-      v = idx[((b * hq + kv * g + jj) * n + tt) * k + i];
+      const int64_t at = ((b * hq + kv * g + jj) * n + tt) * k + i;
+      v = idx[at];
+      if (v >= 0) e = pos[at];
     }
     sidx[i * kWinRows + rr] = v;
+    spos[i * kWinRows + rr] = e;
   }
   typename A::Frag bq[1][A::NS];
   {
@@ -729,7 +793,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const float lw = ws.l + wave_shfl_xor(ws.l, 32);
   float M = lw > 0.f ? ws.m2 + __log2f(lw) : -__builtin_inff();
   for (int i = 0; i < k; ++i)
-    if (sidx[i * kWinRows + r] >= 0) M = fmaxf(M, lse_part[orow * k + i].x);
+    if (sidx[i * kWinRows + r] >= 0) M = fmaxf(M, lse_part[spos[i * kWinRows + r]].x);
   const float ww = lw > 0.f ? __builtin_amdgcn_exp2f(ws.m2 - M) : 0.f;
   float den = ww * lw;
   const float wws = ldexpf(ww, ev);   // the window's values were scaled by 2^-ev
@@ -737,7 +801,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   for (int mt = 0; mt < A::MTD; ++mt) ws.o[mt] *= wws;
   for (int i = 0; i < k; ++i) {
     if (sidx[i * kWinRows + r] < 0) continue;
-    const int64_t pidx = orow * k + i;
+    const int64_t pidx = spos[i * kWinRows + r];
     const float2 le = lse_part[pidx];
     const float wi = __builtin_amdgcn_exp2f(le.x - M);
     den += wi;
@@ -778,6 +842,7 @@ struct AttnWs {
   int32_t* task_count;
   int4* tasks;
   uint32_t* entries;
+  int32_t* pos;
   float2* lse_part;
   void* o_part;
   size_t bytes;
@@ -802,8 +867,10 @@ AttnWs attn_ws_layout(const Shape& s, void* base) {
   const size_t o_img = take(size_t(s.b) * s.hkv * size_t(w.n_chunks) * chunk_bytes);
   const size_t o_counts = take(size_t(nseg) * 4), o_cursor = take(size_t(nseg) * 4);
   const size_t o_tc = take(4), o_tasks = take(size_t(w.max_tasks) * 16);
-  const size_t o_entries = take(size_t(pairs) * 4), o_lse = take(size_t(pairs) * 8);
-  const size_t o_part = take(size_t(pairs) * s.d * es);
+  // entries and partials in task order, kTaskRows slots per task
+  const size_t slots = size_t(w.max_tasks) * kTaskRows;
+  const size_t o_entries = take(slots * 4), o_pos = take(size_t(pairs) * 4);
+  const size_t o_lse = take(slots * 8), o_part = take(slots * s.d * es);
   w.bytes = off;
   if (base != nullptr) {
     uint8_t* p = static_cast<uint8_t*>(base);
@@ -814,6 +881,7 @@ AttnWs attn_ws_layout(const Shape& s, void* base) {
     w.task_count = reinterpret_cast<int32_t*>(p + o_tc);
     w.tasks = reinterpret_cast<int4*>(p + o_tasks);
     w.entries = reinterpret_cast<uint32_t*>(p + o_entries);
+    w.pos = reinterpret_cast<int32_t*>(p + o_pos);
     w.lse_part = reinterpret_cast<float2*>(p + o_lse);
     w.o_part = p + o_part;
   }
@@ -855,34 +923,33 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
           hipSuccess)
         return e;
     hipLaunchKernelGGL(dispatch_kernel<false>, hgrid, dim3(256), hshm, st, idx, w.counts,
-                       (uint32_t*)nullptr, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
+                       (uint32_t*)nullptr, (int32_t*)nullptr, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
     hipLaunchKernelGGL(scan_tasks_kernel, dim3(1), dim3(kScanThreads), 0, st, w.counts, w.cursor,
                        w.tasks, w.task_count, nseg);
     hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(256), hshm, st, idx, w.cursor, w.entries,
-                       s.n, s.g, s.hq, s.hkv, s.k, s.nb);
+                       w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     auto bk = block_attn_kernel<F32, D, PartT>;
-    const size_t bshm = 2 * size_t(A::CHUNK);
+    const size_t bshm = size_t(kResidentBytes) + (kBlockThreads / 64) * size_t(kStageBytes);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(bk),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(bshm))) != hipSuccess)
       return e;
-    // persistent: two workgroups per CU, a multiple of the 8 XCDs
-    const int64_t grid = std::min<int64_t>((w.max_tasks + 7) / 8 * 8, int64_t(num_cus()) * 2 / 8 * 8);
-    hipLaunchKernelGGL(bk, dim3(unsigned(grid)), dim3(kAttnThreads), bshm, st, Q, w.img, w.n_chunks,
-                       w.tasks,
-                       w.task_count, w.entries, w.vmax, static_cast<PartT*>(w.o_part), w.lse_part, s.n,
-                       s.g, s.hq, s.hkv, s.B, s.nb, s.k, scale2);
+    // persistent: one workgroup per CU, a multiple of the 8 XCDs
+    const int64_t grid = std::max<int64_t>(8, int64_t(num_cus()) / 8 * 8);
+    hipLaunchKernelGGL(bk, dim3(unsigned(grid)), dim3(kBlockThreads), bshm, st, Q, w.img, w.n_chunks,
+                       w.tasks, w.task_count, w.entries, w.vmax, static_cast<PartT*>(w.o_part),
+                       w.lse_part, s.n, s.g, s.hq, s.hkv, s.B, s.nb, scale2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto wk = window_merge_kernel<F32, D, PartT, OutT>;
-  const size_t wshm = 2 * size_t(A::CHUNK) + size_t(kWinRows) * std::max(s.k, 1) * 4;
+  const size_t wshm = 2 * size_t(A::CHUNK) + 2 * size_t(kWinRows) * std::max(s.k, 1) * 4;
   if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(wk),
                                hipFuncAttributeMaxDynamicSharedMemorySize, int(wshm))) != hipSuccess)
     return e;
   const int64_t n_tiles = (s.n * s.g + kWinRows - 1) / kWinRows;
   hipLaunchKernelGGL(wk, dim3(unsigned(n_tiles * n_bkv)), dim3(kAttnThreads), wshm, st, Q, w.img,
-                     w.n_chunks, idx, w.vmax, static_cast<const PartT*>(w.o_part), w.lse_part, static_cast<OutT*>(Ov),
-                     lse, s.n, s.g, s.hq, s.hkv, s.B, s.k, s.W, scale2, n_tiles);
+                     w.n_chunks, idx, w.pos, w.vmax, static_cast<const PartT*>(w.o_part), w.lse_part,
+                     static_cast<OutT*>(Ov), lse, s.n, s.g, s.hq, s.hkv, s.B, s.k, s.W, scale2, n_tiles);
   return hipGetLastError();
 }
 
@@ -896,6 +963,10 @@ hipError_t launch_attn_d(const Shape& s, const void* Q, const void* K, const voi
 }  // namespace
 
 size_t attn_workspace_bytes(const Shape& s) { return attn_ws_layout(s, nullptr).bytes; }
+
+int64_t attn_entry_slots(const Shape& s) {
+  return attn_ws_layout(s, nullptr).max_tasks * kTaskRows;
+}
 
 hipError_t launch_sparse_attn(const Shape& s, const void* Q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse, void* ws, hipStream_t st) {

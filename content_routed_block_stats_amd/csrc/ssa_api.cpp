@@ -159,6 +159,8 @@ ssa_status ssa_sparse_attn_fwd(const ssa_params* p, const void* Q, const void* K
     return fail(SSA_ERR_UNSUPPORTED, "more than %lld blocks per sequence", (long long)kMaxBlocksAttn);
   if (int64_t(s.b) * s.hq * s.n * s.k >= (int64_t(1) << 31))
     return fail(SSA_ERR_UNSUPPORTED, "batch * n_q_heads * seq_len * top_k above 2^31");
+  if (s.k > 0 && ssa::attn_entry_slots(s) >= (int64_t(1) << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "routed (row, block) pairs plus per-block task padding above 2^31");
   st = check_ws(ssa::attn_workspace_bytes(s), workspace, workspace_bytes);
   if (st != SSA_OK) return st;
   return from_hip(

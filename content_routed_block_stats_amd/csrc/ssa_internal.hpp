@@ -34,6 +34,9 @@ hipError_t launch_route_topk(const Shape& s, const void* Q, const float* mu, con
 
 // sparse attention (prefill)
 size_t attn_workspace_bytes(const Shape& s);
+// entry / partial slots of the block pass (tasks padded to whole task rows);
+// positions are 32-bit, so this must stay below 2^31
+int64_t attn_entry_slots(const Shape& s);
 hipError_t launch_sparse_attn(const Shape& s, const void* Q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse, void* ws, hipStream_t st);
 

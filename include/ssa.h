@@ -128,6 +128,9 @@ ssa_status ssa_route_topk(const ssa_params* p, const void* Q, const float* mu,
  *        (other contents are undefined behaviour)
  *   O    [b, Hq, n, d] out_dtype, written;  lse [b, Hq, n] float32, written
  *   workspace >= ssa_workspace_size(p, SSA_OP_ATTN) bytes
+ * Limits (SSA_ERR_UNSUPPORTED otherwise): at most 16384 blocks per sequence
+ * when top_k > 0; b * Hq * n * k below 2^31, and so is that count plus 256
+ * slots of padding per (sequence, KV head, block).
  * Arithmetic: MFMA products with float32 accumulation and an online softmax
  * in float32. */
 ssa_status ssa_sparse_attn_fwd(const ssa_params* p, const void* Q, const void* K,
