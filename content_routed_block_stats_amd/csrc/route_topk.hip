@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   using Lay = RouteLayout<D>;
   using QT = typename QFrag<F32>::T;
   constexpr int MT = Lay::MT, NS = Lay::NS, BYTES = Lay::BLOCK_BYTES;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Lay::LDS_BYTES];
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int64_t wid = blockIdx.x;
@@ -192,108 +192,165 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     li[i] = -1;
   }
 
-  // block c's image -> LDS buffer c&1 by direct global->LDS loads (1 KB per
-  // wave instruction); the barrier that ends an iteration waits for them
+  // block c's image -> an LDS buffer by direct global->LDS loads (1 KB per
+  // wave instruction); the barrier that ends a block's iteration waits for them
   const uint8_t* src_base = prep + bkv * nb * int64_t(BYTES);
-  auto stage = [&](int64_t c) {
+  auto stage = [&](int64_t c, uint8_t* dst) {
     const uint8_t* src = src_base + c * BYTES;
-    uint8_t* dst = lds + (c & 1) * Lay::LDS_BYTES;
     for (int r = wave; r < Lay::DMA_ROWS; r += kRouteThreads / 64)
       __builtin_amdgcn_global_load_lds(src + r * 1024 + lane * 16,
                                        (__attribute__((address_space(3))) void*)(dst + r * 1024),
                                        16, 0, 0);
   };
-  if (C_wg > 0) stage(0);
+  if (C_wg > 0) stage(0, lds);
   __syncthreads();
 
-  // Output tiles are contracted one at a time (both row tiles, high then low
-  // part per chunk) and each finished tile is folded into the row-dot (lane
-  // (ln, h) holds P_j + mu_j for j = 32mt + 8a + 4h + b) while the next tile's
-  // MFMAs run.  The last tile's dot and the top-k insert of a block are
-  // deferred to the start of the next block's iteration, where they overlap
-  // that block's first MFMAs; blocks still enter the top-k in order.
-  floatx16 acc[2][MT];
-  float part[2] = {0.f, 0.f}, prev[2] = {0.f, 0.f};
-  auto mfma_tile = [&](const uint8_t* L, int mt) {
-    const floatx16 m = *reinterpret_cast<const floatx16*>(L + Lay::MU_OFF + (h * MT + mt) * 64);
-    acc[0][mt] = m;
-    acc[1][mt] = m;
+  // Hand-scheduled sweep.  Output tiles run from the widest (mt = MT-1, all
+  // 2MT chunks) down to mt = 0, two accumulator sets alternating, and every
+  // MFMA call is followed by a fixed share of vector work that depends only on
+  // earlier tiles: the row-dot of the previous tile (lane (ln, h) holds
+  // P_j + mu_j for j = 32mt + 8a + 4h + b, P's column = this lane's query
+  // row), and, during the widest tile, the finish of the previous block --
+  // the dot of its last tile, the lane-half reduction and the running top-k
+  // insert.  sched_barrier pins that interleave, so the matrix cores stay fed
+  // while the vector units work, whatever the other wave on the SIMD does.
+  // Operand fragments are read from LDS two steps ahead; each tile's first
+  // MFMA takes mu as its accumulator input.
+  constexpr int PARTS = F32 ? 1 : 2;               // bf16: high and low part of T
+  constexpr int NFR = Lay::NF * PARTS;             // fragment reads per block
+  constexpr int NDOT = 32;                         // row-dot FMAs per tile (2 tiles x 16)
+  floatx16 acc[2][2];                              // [set][nt]; tile mt uses set (MT-1-mt)&1
 #pragma unroll
-    for (int s = 0; s <= 2 * mt + 1; ++s) {
-      const uint8_t* F = L + Lay::frag(mt, s) * kFragBytes;
-      if constexpr (F32) {
-        const floatx8 a = *reinterpret_cast<const floatx8*>(F + lane * 32);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma16(a, bq[nt][s], acc[nt][mt]);
-      } else {
-        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(F + lane * 16);
-        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(F + 1024 + lane * 16);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma16(ahi, bq[nt][s], acc[nt][mt]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt][mt] = mma16(alo, bq[nt][s], acc[nt][mt]);
-      }
-    }
-  };
-  auto dot_tile = [&](int mt, float (&pt)[2]) {
+  for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb)
-          pt[nt] = fmaf(acc[nt][mt][4 * a + bb],
-                        QFrag<F32>::elem(bq[nt][2 * mt + (a >> 1)], 4 * (a & 1) + bb), pt[nt]);
+      for (int j = 0; j < 16; ++j) acc[st2][nt][j] = 0.f;
+  float pt[2] = {0.f, 0.f};
+  float sc_ins = -__builtin_inff();
+  int ci_ins = -1;
+
+  // fragment k (= chunk-in-pair * PARTS + part) of chunk pair gp of tile mt
+  auto read_frag = [&](const uint8_t* L, int mt, int gp, int k) {
+    const int sidx = 2 * gp + k / PARTS, part = k % PARTS;
+    const uint8_t* F = L + Lay::frag(mt, sidx) * kFragBytes;
+    if constexpr (F32)
+      return *reinterpret_cast<const QT*>(F + lane * 32);
+    else
+      return *reinterpret_cast<const QT*>(F + part * 1024 + lane * 16);
   };
-  // both lane halves combined, then the running top-k insert of block cb
-  auto insert = [&](float (&pt)[2], int64_t cb) {
+  auto read_mu = [&](const uint8_t* L, int mt) {
+    floatx16 m;
+    const floatx4* p = reinterpret_cast<const floatx4*>(L + Lay::MU_OFF + mt * 64) + h * (MT * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx4 v = p[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[4 * q + e] = v[e];
+    }
+    return m;
+  };
+  auto dot_item = [&](int set, int mt, int i) {
+    const int nt = i / 16, j = i % 16, a = j / 4, bb = j % 4;
+    pt[nt] = fmaf(acc[set][nt][j], QFrag<F32>::elem(bq[nt][2 * mt + (a >> 1)], 4 * (a & 1) + bb),
+                  pt[nt]);
+  };
+  // both lane halves combined: the score of this lane's row for block cb
+  auto reduce = [&](int64_t cb) {
     const float p0 = pt[0] + wave_shfl_xor(pt[0], 32);
     const float p1 = pt[1] + wave_shfl_xor(pt[1], 32);
     pt[0] = pt[1] = 0.f;
-    float sc = h ? p1 : p0;
-    if (cb < my_C && sc > ls[KMAX]) {
-      int ci = int(cb);
-#pragma unroll
-      for (int i = 0; i <= KMAX; ++i) {
-        const bool gt = sc > ls[i];
-        const float ts = ls[i];
-        const int ti = li[i];
-        ls[i] = gt ? sc : ts;
-        li[i] = gt ? ci : ti;
-        sc = gt ? ts : sc;
-        ci = gt ? ti : ci;
-      }
-    }
+    sc_ins = (cb >= 0 && cb < my_C) ? (h ? p1 : p0) : -__builtin_inff();
+    ci_ins = int(cb);
+  };
+  // one step of the running top-(k+1) insertion; strict > keeps the earlier
+  // (lower) block on ties
+  auto insert_step = [&](int i) {
+    const bool gt = sc_ins > ls[i];
+    const float ts = ls[i];
+    const int ti = li[i];
+    ls[i] = gt ? sc_ins : ts;
+    li[i] = gt ? ci_ins : ti;
+    sc_ins = gt ? ts : sc_ins;
+    ci_ins = gt ? ti : ci_ins;
   };
 
-  for (int64_t c = 0; c < C_wg; ++c) {
-    if (c + 1 < C_wg) stage(c + 1);
-    const uint8_t* L = lds + (c & 1) * Lay::LDS_BYTES;
-    mfma_tile(L, 0);
-    if (c > 0) {
-      dot_tile(MT - 1, prev);
-      insert(prev, c - 1);
-    }
+  auto sweep = [&](int64_t c, const uint8_t* L) {
+    // the query fragments are loop-invariant; an empty register constraint
+    // stops the compiler from hoisting their float32 conversions (for the
+    // row-dot) out of the loop, which would need 128 more registers
 #pragma unroll
-    for (int mt = 1; mt < MT; ++mt) {
-      dot_tile(mt - 1, part);
-      mfma_tile(L, mt);
-      // interleave: one MFMA, then three VALU (the previous tile's row-dot)
-      constexpr int kMfmaPerChunk = F32 ? 16 : 4;
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int i = 0; i < (2 * mt + 2) * kMfmaPerChunk; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      for (int s2 = 0; s2 < NS; ++s2) asm volatile("" : "+v"(bq[nt][s2]));
+    // Operands move in chunk pairs (2 PARTS fragments): the reads of pair
+    // p+1 are issued after the first MFMA of pair p, so that MFMA's
+    // wait covers pair p alone (while a direct-to-LDS copy is in flight the
+    // compiler can only wait for all outstanding LDS reads) and pair p+1 has
+    // the rest of pair p to arrive.  Tile mt has mt+1 pairs.
+    constexpr int PK = 2 * PARTS;                  // fragments per pair
+    QT fr[2][PK];
+#pragma unroll
+    for (int k2 = 0; k2 < PK; ++k2) fr[0][k2] = read_frag(L, MT - 1, 0, k2);
+    floatx16 mu_next = read_mu(L, MT - 1);
+    int pslot = 0;                                 // slot of the current pair
+#pragma unroll
+    for (int mt = MT - 1; mt >= 0; --mt) {
+      const int set = (MT - 1 - mt) & 1, pset = set ^ 1;
+      const floatx16 mu_t = mu_next;
+      constexpr int kCallsPerPair = PK * 2;
+      const int calls = (mt + 1) * kCallsPerPair;
+      // vector work of this tile: the previous tile's dot (for the widest
+      // tile: the previous block's last tile), then, for the widest tile,
+      // the reduction and the KMAX+1 insert steps
+      const int nwork = NDOT + (mt == MT - 1 ? 1 + KMAX + 1 : 0);
+#pragma unroll
+      for (int i = 0; i < calls; ++i) {
+        const int gp = i / kCallsPerPair, k2 = (i / 2) % PK, nt = i % 2;
+        const int sidx = 2 * gp + k2 / PARTS;
+        const int slot = (pslot + gp) & 1;
+        const floatx16 cin = (i < 2) ? mu_t : acc[set][nt];
+        acc[set][nt] = mma16(fr[slot][k2], bq[nt][sidx], cin);
+        if (i % kCallsPerPair == 1) {
+          // next pair: later in this tile, else the first of the next tile
+          // (issued in the second call's slot: the scheduler may lift a read
+          // above its own call's MFMA, but not above the previous call's)
+          if (gp < mt) {
+#pragma unroll
+            for (int q2 = 0; q2 < PK; ++q2) fr[slot ^ 1][q2] = read_frag(L, mt, gp + 1, q2);
+          } else if (mt > 0) {
+#pragma unroll
+            for (int q2 = 0; q2 < PK; ++q2) fr[slot ^ 1][q2] = read_frag(L, mt - 1, 0, q2);
+            mu_next = read_mu(L, mt - 1);
+          }
+        }
+#pragma unroll
+        for (int w = i * nwork / calls; w < (i + 1) * nwork / calls; ++w) {
+          if (w < NDOT) {
+            dot_item(pset, mt == MT - 1 ? 0 : mt + 1, w);
+          } else if (w == NDOT) {
+            reduce(c - 1);
+          } else {
+            insert_step(w - NDOT - 1);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      pslot = (pslot + mt + 1) & 1;
     }
-    prev[0] = part[0];
-    prev[1] = part[1];
-    part[0] = part[1] = 0.f;
+  };
+  for (int64_t c = 0; c < C_wg; ++c) {
+    if (c + 1 < C_wg) stage(c + 1, lds + ((c + 1) & 1) * Lay::LDS_BYTES);
+    sweep(c, lds + (c & 1) * Lay::LDS_BYTES);
     __syncthreads();
   }
+  // the last block's final tile, reduction and insert
   if (C_wg > 0) {
-    dot_tile(MT - 1, prev);
-    insert(prev, C_wg - 1);
+#pragma unroll
+    for (int w = 0; w < NDOT; ++w) dot_item((MT - 1) & 1, 0, w);
+    reduce(C_wg - 1);
+#pragma unroll
+    for (int i = 0; i <= KMAX; ++i) insert_step(i);
   }
 
   if (!my_valid) return;
@@ -342,11 +399,8 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
     if (e != hipSuccess) return e;
   }
   const int64_t n_tiles = (s.n * s.g + kRouteRows - 1) / kRouteRows;
-  const size_t shmem = 2 * size_t(Lay::LDS_BYTES);
   auto kern = route_topk_kernel<F32, D, KMAX>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
-  if (e != hipSuccess) return e;
+  constexpr size_t shmem = 0;   // the kernel's LDS buffers are static
   using In = typename QFrag<F32>::In;
   hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles * n_bkv)), dim3(kRouteThreads), shmem, st,
                      static_cast<const In*>(Q), prep, idx, kth, s.n, s.g, s.hq, s.hkv, s.B, s.nb,
