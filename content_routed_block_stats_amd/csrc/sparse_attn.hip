@@ -41,6 +41,7 @@ constexpr int kAttnThreads = 256;          // window pass: 4 waves, 32 query row
 constexpr int kBlockThreads = 512;         // block pass: 8 waves, 32 query rows each
 constexpr int kTaskRows = 256;             // rows per block-attention task
 constexpr int kResidentBytes = 128 * 1024; // LDS that keeps a block's K/V images resident
+constexpr int kRunTasks = 8;               // consecutive tasks a workgroup takes at a time
 constexpr int kStageBytes = 4096;          // LDS per wave that lines partials up for storing
 constexpr float kLazyLog2 = 8.f;           // probabilities may reach 2^kLazyLog2 before a rescale
 constexpr int kWinRows = 128;              // rows per window/merge tile
@@ -473,6 +474,12 @@ __global__ __launch_bounds__(256) void value_max_kernel(const bf16_t* __restrict
 
 // ---------------------------------------------------------------- dispatch --
 
+template <typename PartT, int D>
+__global__ void null_partial_kernel(PartT* o_part, float2* lse_part, int64_t slot) {
+  for (int i = threadIdx.x; i < D; i += blockDim.x) o_part[slot * D + i] = PartT{};
+  if (threadIdx.x == 0) lse_part[slot] = float2{-__builtin_inff(), 0.f};
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count;
        i += int64_t(gridDim.x) * blockDim.x)
@@ -600,12 +607,15 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
   constexpr int SEG_CHUNKS = kResidentBytes / A::CHUNK;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int64_t T = *task_count;
-  const int64_t per_xcd = (T + 7) / 8;
-  const int64_t x = blockIdx.x, nw = gridDim.x / 8;
-  const int64_t xb = (x % 8) * per_xcd, xe = min(T, xb + per_xcd);
-  const int64_t per_wg = (xe - xb + nw - 1) / nw;
-  const int64_t tb = xb + (x / 8) * per_wg, te = min(xe, tb + per_wg);
-  if (tb >= te) return;
+  // this workgroup's p-th task: runs of kRunTasks consecutive tasks, runs
+  // dealt round-robin over the workgroups, so that at any moment the whole
+  // chip works on a narrow stretch of the task list (one KV head, a few
+  // blocks): that head's query rows then stay in the memory-side cache
+  // across the k times each of them is gathered
+  const int64_t G = gridDim.x;
+  auto seq = [&](int64_t p) { return (blockIdx.x + (p / kRunTasks) * G) * kRunTasks + p % kRunTasks; };
+  const int64_t tb = seq(0);
+  if (tb >= T) return;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int r = 32 * wave + ln;             // this lane's row within a task
   const int block_chunks = B / kKeyChunk;
@@ -641,23 +651,25 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
 #pragma unroll
     for (int s = 0; s < A::NS; ++s) bq[0][s] = load_row_frag<F32, D>(Q + orow * D, s, h, true);
   }
-  int4 task_n = tb + 1 < te ? tasks[tb + 1] : task;
+  const bool has_1 = seq(1) < T;
+  int4 task_n = has_1 ? tasks[seq(1)] : task;
   {
-    const uint32_t code = entries[min(tb + 1, te - 1) * kTaskRows + r];
-    orow_n = row_of(task_n, tb + 1 < te && r < task_n.z ? code : 0u);
+    const uint32_t code = entries[(has_1 ? seq(1) : tb) * kTaskRows + r];
+    orow_n = row_of(task_n, has_1 && r < task_n.z ? code : 0u);
   }
   // enter the loop with nothing in flight, as every later iteration does
   __builtin_amdgcn_s_waitcnt(0);
   int64_t resident = -1;                    // segment id held in LDS
 
-  for (int64_t ti = tb; ti < te; ++ti) {
+  for (int64_t p = 0, ti = tb; ti < T; ti = seq(++p)) {
     // (a) next task's query rows, the entries of the task after it
     Frag bqn[A::NS];
 #pragma unroll
     for (int s = 0; s < A::NS; ++s) bqn[s] = load_row_frag<F32, D>(Q + orow_n * D, s, h, true);
-    const bool has_nn = ti + 2 < te;
-    const int4 task_nn = has_nn ? tasks[ti + 2] : task;
-    const uint32_t code_nn = entries[min(ti + 2, te - 1) * kTaskRows + r];
+    const int64_t t2 = seq(p + 2);
+    const bool has_nn = t2 < T;
+    const int4 task_nn = has_nn ? tasks[t2] : task;
+    const uint32_t code_nn = entries[(has_nn ? t2 : ti) * kTaskRows + r];
     // (b) this task: every chunk of its block against 8 x 32 query rows
     const bool wave_active = 32 * wave < task.z;
     const int ev = F32 ? 0 : value_exponent(vmax[task.x / nb]);
@@ -714,16 +726,24 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
     int64_t n_chunks, const int32_t* __restrict__ idx, const int32_t* __restrict__ pos,
     const uint32_t* __restrict__ vmax, const PartT* __restrict__ o_part,
-    const float2* __restrict__ lse_part, OutT* __restrict__ O,
+    const float2* __restrict__ lse_part, int64_t null_slot, OutT* __restrict__ O,
     float* __restrict__ lse, int64_t n, int g, int hq, int hkv, int B, int k, int W,
-    float scale2, int64_t n_tiles) {
+    float scale2, int64_t n_tiles, int64_t n_work) {
   using A = AT<F32, D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int32_t* sidx = reinterpret_cast<int32_t*>(lds + 2 * A::CHUNK);   // [k][kWinRows]
   int32_t* spos = sidx + kWinRows * k;                                // [k][kWinRows]
+  float2* wml = reinterpret_cast<float2*>(spos + kWinRows * k);       // window (m2, l) per row
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
-  const int64_t bkv = blockIdx.x / n_tiles;
-  const int64_t tile = blockIdx.x % n_tiles;
+  // workgroups are dealt round-robin over the 8 XCDs; give each XCD a
+  // contiguous run of tiles so that neighbouring tiles, whose windows share
+  // key chunks, meet in the same L2
+  // (the grid is n_work rounded up to a multiple of 8; the extra ones exit)
+  const int64_t per_xcd = int64_t(gridDim.x) / 8;
+  const int64_t lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (lin >= n_work) return;
+  const int64_t bkv = lin / n_tiles;
+  const int64_t tile = lin % n_tiles;
   const int64_t b = bkv / hkv, kv = bkv % hkv;
   const int64_t rho0 = tile * kWinRows, rows_total = n * g;
 
@@ -787,36 +807,111 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     }
     __syncthreads();
   }
-  if (!valid) return;
-  // merge: window part (m2, l, o unnormalised) with the routed partials
-  RowState<D>& ws = st[0];
-  const float lw = ws.l + wave_shfl_xor(ws.l, 32);
-  float M = lw > 0.f ? ws.m2 + __log2f(lw) : -__builtin_inff();
-  for (int i = 0; i < k; ++i)
-    if (sidx[i * kWinRows + r] >= 0) M = fmaxf(M, lse_part[spos[i * kWinRows + r]].x);
-  const float ww = lw > 0.f ? __builtin_amdgcn_exp2f(ws.m2 - M) : 0.f;
-  float den = ww * lw;
-  const float wws = ldexpf(ww, ev);   // the window's values were scaled by 2^-ev
+  // ---- hand the window part over to the merge layout (LDS, reusing the
+  // chunk buffers; the loop above ended on a barrier).  Element e of a row is
+  // column pi(e) = 32mt + 8a + 4h + b for e = h D/2 + 16mt + 4a + b -- the
+  // order partials are stored in -- so a lane half's 64 values are one
+  // contiguous run; 16-byte units are XOR-swizzled by row.
+  {
+    constexpr int U = D / 4;                        // 16-byte units per float32 row
+    float* wo = reinterpret_cast<float*>(lds);
+    const RowState<D>& ws = st[0];
 #pragma unroll
-  for (int mt = 0; mt < A::MTD; ++mt) ws.o[mt] *= wws;
-  for (int i = 0; i < k; ++i) {
-    if (sidx[i * kWinRows + r] < 0) continue;
-    const int64_t pidx = spos[i * kWinRows + r];
-    const float2 le = lse_part[pidx];
-    const float wi = __builtin_amdgcn_exp2f(le.x - M);
-    den += wi;
-    accumulate_partial<PartT>(ws.o, o_part + pidx * D + h * (D / 2), ldexpf(wi, int(le.y)));
+    for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = (h * (D / 2) + 16 * mt + 4 * q) / 4;
+        *reinterpret_cast<floatx4*>(wo + r * D + 4 * (u ^ (r % U))) =
+            floatx4{ws.o[mt][4 * q], ws.o[mt][4 * q + 1], ws.o[mt][4 * q + 2], ws.o[mt][4 * q + 3]};
+      }
+    const float lw = ws.l + wave_shfl_xor(ws.l, 32);
+    if (h == 0) wml[r] = float2{ws.m2, lw};
   }
-  const float inv = 1.f / den;
-  OutT* out = O + orow * D;
+  wave_lds_sync();
+
+  // ---- merge, in the partials' own layout: CH lanes per row, each owning
+  // one 16-byte unit of every partial (coalesced reads), RPR rows per pass.
+  constexpr int CH = D * int(sizeof(PartT)) / 16;   // 16-byte units per partial row
+  constexpr int EPU = 16 / int(sizeof(PartT));      // elements per unit
+  constexpr int RPR = 64 / CH;
+  constexpr int GRP = 16;                           // partials requested at once
+  const float* wo = reinterpret_cast<const float*>(lds);
+  constexpr int U = D / 4;
+  for (int rd = 0; rd < 32 / RPR; ++rd) {
+    const int rr = 32 * wave + rd * RPR + lane / CH, sub = lane % CH;
+    const int64_t rh = rho0 + rr;
+    if (rh >= rows_total) continue;
+    const int64_t row = (b * hq + kv * g + rh % g) * n + rh / g;
+    const float2 wl = wml[rr];
+    // running (max, sum, weighted values) over the window part and then the
+    // partials in groups of GRP; every load is unconditional -- absent slots
+    // read the null partial (zeros, lse = -inf) -- so a group's loads all
+    // go out before any of them is waited for
+    float M = wl.y > 0.f ? wl.x + __log2f(wl.y) : -__builtin_inff();
+    float den = wl.y > 0.f ? wl.y * __builtin_amdgcn_exp2f(wl.x - M) : 0.f;   // = 1 or 0
+    float acc[EPU];
+    {
+      const float wws = wl.y > 0.f ? ldexpf(__builtin_amdgcn_exp2f(wl.x - M), ev) : 0.f;
 #pragma unroll
-  for (int mt = 0; mt < A::MTD; ++mt)
+      for (int e = 0; e < EPU; ++e) {
+        const int el = sub * EPU + e, u = el / 4;
+        acc[e] = wo[rr * D + 4 * (u ^ (rr % U)) + el % 4] * wws;
+      }
+    }
+    for (int i0 = 0; i0 < k; i0 += GRP) {
+      int64_t pidx[GRP];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int j = 0; j < GRP; ++j) {
+        const int i = min(i0 + j, k - 1);
+        const int32_t sel = sidx[i * kWinRows + rr], at = spos[i * kWinRows + rr];
+        pidx[j] = (i0 + j < k && sel >= 0) ? int64_t(at) : null_slot;
+      }
+      u32x4 pv[GRP];
+      float2 le[GRP];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-        store_from_f32(out, 32 * mt + 8 * a + 4 * h + bb, ws.o[mt][4 * a + bb] * inv);
-  if (h == 0) lse[orow] = (M + __log2f(den)) * kLn2;
+      for (int j = 0; j < GRP; ++j) {
+        le[j] = lse_part[pidx[j]];
+        pv[j] = reinterpret_cast<const u32x4*>(o_part + pidx[j] * D)[sub];
+      }
+      float Mg = M;
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) Mg = fmaxf(Mg, le[j].x);
+      const float resc = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
+      M = Mg;
+      den *= resc;
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) acc[e] *= resc;
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const float wi = le[j].x == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(le[j].x - M);
+        den += wi;
+        const float ws2 = ldexpf(wi, int(le[j].y));
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) {
+          float v;
+          if constexpr (sizeof(PartT) == 4) {
+            // (copy the element out first: bit-casting a vector element
+            // lvalue directly reads element 0 with this compiler)
+            const uint32_t bits = pv[j][e];
+            v = __builtin_bit_cast(float, bits);
+          } else {
+            const uint32_t w2 = pv[j][e / 2];
+            v = static_cast<float>(__builtin_bit_cast(_Float16, u16((e & 1) ? (w2 >> 16) : (w2 & 0xFFFFu))));
+          }
+          acc[e] = fmaf(ws2, v, acc[e]);
+        }
+      }
+    }
+    const float inv = 1.f / den;
+    OutT* out = O + row * D;
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) {
+      const int el = sub * EPU + e;                 // element -> column
+      const int hh = el / (D / 2), rem = el % (D / 2), mt = rem / 16, j = rem % 16;
+      store_from_f32(out, 32 * mt + 8 * (j / 4) + 4 * hh + (j % 4), acc[e] * inv);
+    }
+    if (sub == 0) lse[row] = (M + __log2f(den)) * kLn2;
+  }
 }
 
 // ------------------------------------------------------------------ launch --
@@ -847,6 +942,7 @@ struct AttnWs {
   void* o_part;
   size_t bytes;
   int64_t max_tasks;
+  int64_t null_slot;
 };
 
 AttnWs attn_ws_layout(const Shape& s, void* base) {
@@ -868,9 +964,12 @@ AttnWs attn_ws_layout(const Shape& s, void* base) {
   const size_t o_counts = take(size_t(nseg) * 4), o_cursor = take(size_t(nseg) * 4);
   const size_t o_tc = take(4), o_tasks = take(size_t(w.max_tasks) * 16);
   // entries and partials in task order, kTaskRows slots per task
+  // one more partial slot past the tasks': the null partial (zeros, lse -inf)
+  // that the merge reads for absent selections
   const size_t slots = size_t(w.max_tasks) * kTaskRows;
+  w.null_slot = int64_t(slots);
   const size_t o_entries = take(slots * 4), o_pos = take(size_t(pairs) * 4);
-  const size_t o_lse = take(slots * 8), o_part = take(slots * s.d * es);
+  const size_t o_lse = take((slots + 1) * 8), o_part = take((slots + 1) * s.d * es);
   w.bytes = off;
   if (base != nullptr) {
     uint8_t* p = static_cast<uint8_t*>(base);
@@ -912,6 +1011,9 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
   }
   hipLaunchKernelGGL((kv_image_kernel<F32, D>), dim3(unsigned(w.n_chunks), unsigned(n_bkv)),
                      dim3(kAttnThreads), 0, st, K, V, w.vmax, w.img, s.n, w.n_chunks);
+  if (s.k > 0)
+    hipLaunchKernelGGL((null_partial_kernel<PartT, D>), dim3(1), dim3(64), 0, st,
+                       static_cast<PartT*>(w.o_part), w.lse_part, w.null_slot);
   if (s.k > 0 && nseg > 0) {
     hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((nseg + 255) / 256, 4096))),
                        dim3(256), 0, st, w.counts, nseg, 0);
@@ -942,14 +1044,17 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto wk = window_merge_kernel<F32, D, PartT, OutT>;
-  const size_t wshm = 2 * size_t(A::CHUNK) + 2 * size_t(kWinRows) * std::max(s.k, 1) * 4;
+  const size_t wshm =
+      2 * size_t(A::CHUNK) + 2 * size_t(kWinRows) * std::max(s.k, 1) * 4 + size_t(kWinRows) * 8;
   if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(wk),
                                hipFuncAttributeMaxDynamicSharedMemorySize, int(wshm))) != hipSuccess)
     return e;
   const int64_t n_tiles = (s.n * s.g + kWinRows - 1) / kWinRows;
-  hipLaunchKernelGGL(wk, dim3(unsigned(n_tiles * n_bkv)), dim3(kAttnThreads), wshm, st, Q, w.img,
+  // a multiple of 8 workgroups, so that the XCD remapping is a bijection
+  hipLaunchKernelGGL(wk, dim3(unsigned((n_tiles * n_bkv + 7) / 8 * 8)), dim3(kAttnThreads), wshm, st, Q, w.img,
                      w.n_chunks, idx, w.pos, w.vmax, static_cast<const PartT*>(w.o_part), w.lse_part,
-                     static_cast<OutT*>(Ov), lse, s.n, s.g, s.hq, s.hkv, s.B, s.k, s.W, scale2, n_tiles);
+                     w.null_slot, static_cast<OutT*>(Ov), lse, s.n, s.g, s.hq, s.hkv, s.B, s.k, s.W, scale2, n_tiles,
+                     n_tiles * n_bkv);
   return hipGetLastError();
 }
 
