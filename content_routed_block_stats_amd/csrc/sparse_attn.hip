@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) void value_max_kernel(const bf16_t* __restrict
 template <typename PartT, int D>
 __global__ void null_partial_kernel(PartT* o_part, float2* lse_part, int64_t slot) {
   for (int i = threadIdx.x; i < D; i += blockDim.x) o_part[slot * D + i] = PartT{};
-  if (threadIdx.x == 0) lse_part[slot] = float2{-__builtin_inff(), 0.f};
+  if (threadIdx.x == 0) lse_part[slot] = float2{-__builtin_inff(), -__builtin_inff()};
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {
@@ -505,12 +505,17 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   const int64_t t1 = min(n, t0 + kHistTokens);
   for (int64_t i = tid; i < nb; i += 256) hist[i] = 0;
   __syncthreads();
+  constexpr int KG = 8;   // a row's selections in groups: loads, then LDS counts
   for (int j = 0; j < g; ++j) {
     const int32_t* base = idx + ((b * hq + kv * g + j) * n) * k;
     for (int64_t t = t0 + tid; t < t1; t += 256)
-      for (int i = 0; i < k; ++i) {
-        const int32_t c = base[t * k + i];
-        if (c >= 0 && c < nb) atomicAdd(&hist[c], 1);
+      for (int i0 = 0; i0 < k; i0 += KG) {
+        int32_t c[KG];
+#pragma unroll
+        for (int q = 0; q < KG; ++q) c[q] = i0 + q < k ? base[t * k + i0 + q] : -1;
+#pragma unroll
+        for (int q = 0; q < KG; ++q)
+          if (c[q] >= 0 && c[q] < nb) atomicAdd(&hist[c[q]], 1);
       }
   }
   __syncthreads();
@@ -524,16 +529,24 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   }
   if (!SCATTER) return;
   __syncthreads();
+  // the LDS reservations of a group are independent and go out together
+  // instead of one round trip each
   for (int j = 0; j < g; ++j) {
     const int64_t base = ((b * hq + kv * g + j) * n) * k;
     for (int64_t t = t0 + tid; t < t1; t += 256)
-      for (int i = 0; i < k; ++i) {
-        const int32_t c = idx[base + t * k + i];
-        if (c >= 0 && c < nb) {
-          const int32_t e = atomicAdd(&hist[c], 1);
-          entries[e] = (uint32_t(t * g + j) << 5) | uint32_t(i);
-          pos[base + t * k + i] = e;
-        }
+      for (int i0 = 0; i0 < k; i0 += KG) {
+        int32_t c[KG], e[KG];
+#pragma unroll
+        for (int q = 0; q < KG; ++q) c[q] = i0 + q < k ? idx[base + t * k + i0 + q] : -1;
+#pragma unroll
+        for (int q = 0; q < KG; ++q)
+          e[q] = (c[q] >= 0 && c[q] < nb) ? atomicAdd(&hist[c[q]], 1) : -1;
+#pragma unroll
+        for (int q = 0; q < KG; ++q)
+          if (e[q] >= 0) {
+            entries[e[q]] = (uint32_t(t * g + j) << 5) | uint32_t(i0 + q);
+            pos[base + t * k + i0 + q] = e[q];
+          }
       }
   }
 }
@@ -689,26 +702,21 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
           attend_chunk<F32, D, 1>(lds + ch * A::CHUNK, bq, scale2, lane, st,
                                   [](int, int, int, int) { return true; });
     }
-    // (c) the normalised partial of every row of the task
+    // (c) the partial of every row of the task: the unnormalised sums
+    // o = sum_j p_j v_j (values pre-scaled by 2^-ev) times 2^-e, where
+    // l = f 2^e with f in [1/2, 1), so |o 2^-e| <= max|v| 2^-ev < 2^15 fits
+    // half precision without a per-row maximum; with it go
+    // x = m2 + log2 l (the block's log2-sum-exp) and y = m2 + e + ev, and the
+    // merge weighs the partial by 2^(x - M) in the denominator and by
+    // 2^(y - M) in the numerator
     {
       const float l = st[0].l + wave_shfl_xor(st[0].l, 32);
-      const float inv = 1.f / l;
-      // the partial is a convex combination of value rows; half-precision
-      // partials are stored scaled by 2^-e with |o| < 2^e, so every entry keeps
-      // ~2^-12 relative accuracy of max|o| whatever the value range
-      float mx = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < A::MTD; ++mt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(st[0].o[mt][j]));
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * inv;
       int e = 0;
-      if (!F32 && mx > 0.f) (void)frexpf(mx, &e);
-      const float sc = ldexpf(inv, -e);
+      (void)frexpf(l, &e);
       const int64_t pidx = ti * kTaskRows + r;
       store_partials<PartT, D>(lds + kResidentBytes + wave * kStageBytes,
-                               o_part + (pidx - ln) * D, st[0].o, sc, ln, h, lane);
-      lse_part[pidx] = float2{st[0].m2 + __log2f(l), float(e + ev)};
+                               o_part + (pidx - ln) * D, st[0].o, ldexpf(1.f, -e), ln, h, lane);
+      lse_part[pidx] = float2{st[0].m2 + __log2f(l), st[0].m2 + float(e + ev)};
     }
     // (d) rotate the pipeline
     task = task_n;
@@ -885,7 +893,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       for (int j = 0; j < GRP; ++j) {
         const float wi = le[j].x == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(le[j].x - M);
         den += wi;
-        const float ws2 = ldexpf(wi, int(le[j].y));
+        const float ws2 = le[j].y == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(le[j].y - M);
 #pragma unroll
         for (int e = 0; e < EPU; ++e) {
           float v;
