@@ -110,6 +110,19 @@ SMALL = {
                                                           top_k=0, window=200, plants=4),
     "bf16_wide_window": CONFIGS["prefill_32k"].replace(n_q_heads=1, n_kv_heads=1, seq_len=1111,
                                                        block=64, top_k=4, window=300, plants=4),
+    # blocks that the block pass walks in more than one LDS-resident segment,
+    # with a ragged last segment (d=128 bf16: 256 keys per segment)
+    "bf16_block320_two_segments": CONFIGS["gqa_prefill_128k"].replace(
+        n_q_heads=4, n_kv_heads=2, seq_len=320 * 12 + 50, block=320, top_k=4, window=100, plants=4),
+    "bf16_block1024_four_segments": CONFIGS["gqa_prefill_128k"].replace(
+        n_q_heads=2, n_kv_heads=1, seq_len=1024 * 5 + 5, block=1024, top_k=2, window=1024, plants=2),
+    # d=64 bf16: 512 keys per segment
+    "bf16_d64_block576": CONFIGS["prefill_32k"].replace(
+        n_q_heads=2, n_kv_heads=2, head_dim=64, seq_len=576 * 6 + 11, block=576, top_k=3, window=64,
+        plants=4),
+    # block smaller than a segment and not a power of two
+    "f32_block192": CONFIGS["tiny_prefill_4k"].replace(seq_len=2000, block=192, top_k=4, window=80,
+                                                       plants=4),
 }
 
 
