@@ -125,6 +125,41 @@ def route_scores_from_logits(q: np.ndarray, K: np.ndarray, B: int, C: int,
     return out
 
 
+# -- tempered routing family (exact block score) ------------------------------
+
+def tempered_scores(q: np.ndarray, K: np.ndarray, B: int, C: int, beta: float) -> np.ndarray:
+    """T_c(q) = (1/beta) log( (1/B) sum_{j in block c} exp(beta q.k_j) ) for blocks c < C.
+
+    The temperature family of the write-up's module list (centroid <->
+    cumulant <-> exact max), read as the exact log-mean-exp of the block's raw
+    logits: its second-order expansion in beta is r_c(q) = <q, mu_c> +
+    (beta/2) q^T Sigma_c q; beta -> 0 gives the block mean of the logits (the
+    centroid score), beta -> infinity the block maximum.  beta > 0.  Evaluated
+    with the maximum factored out: with u_j = beta q.k_j and m = max_j u_j,
+    T_c = (m + log sum_j exp(u_j - m) - log B) / beta.
+    """
+    if not beta > 0:
+        raise ValueError("the tempered score needs beta > 0")
+    q = as_f64(q)
+    K = as_f64(K)
+    out = np.zeros(C)
+    for c in range(C):
+        u = beta * (K[c * B:(c + 1) * B] @ q)
+        m = u.max()
+        out[c] = (m + math.log(np.exp(u - m).sum()) - math.log(B)) / beta
+    return out
+
+
+def tempered_row(q: np.ndarray, K: np.ndarray, B: int, k: int, beta: float, t: int) -> dict:
+    """Routing of one query row by the tempered score: the complete causal
+    blocks' scores, then the same top-k rule as the cumulant router."""
+    nb = as_f64(K).shape[0] // B
+    C = routable_blocks(t, B, nb)
+    r = tempered_scores(q, K, B, C, beta)
+    idx, r_k, r_k1 = select_topk(r, k)
+    return dict(idx=idx, scores=r, r_k=r_k, r_k1=r_k1)
+
+
 # -- step 3: top-k selection ---------------------------------------------------
 
 def select_topk(r: np.ndarray, k: int) -> tuple[np.ndarray, float, float]:
@@ -272,8 +307,11 @@ def recovery_weight(beta: float, delta: float, mu: float) -> float:
 
 # -- study without a pin ----------------------------------------------------------
 
-def planted_recall(oracle: PrefillOracle, plants: list[dict], beta: float | None = None) -> float:
-    """Fraction of planted outliers whose block the target row selects.
+def planted_recall(oracle: PrefillOracle, plants: list[dict], beta: float | None = None,
+                   score: str = "cumulant") -> float:
+    """Fraction of planted outliers whose block the target row selects, routing
+    by the second-cumulant score (score="cumulant") or by the exact tempered
+    score (score="tempered", beta > 0).
 
     PARITY UNPINNED: the write-up states only the qualitative result
     (second-cumulant routing recovers targets that centroid routing misses).
@@ -288,7 +326,11 @@ def planted_recall(oracle: PrefillOracle, plants: list[dict], beta: float | None
         Kh, Vh, mu, sigma = oracle.head(pl["b"], kv)
         t = pl["t"]
         C = routable_blocks(t, p.block, mu.shape[0])
-        r = route_scores(as_f64(oracle.Q[pl["b"], pl["h"], t]), mu[:C], sigma[:C], p.beta)
+        q = as_f64(oracle.Q[pl["b"], pl["h"], t])
+        if score == "tempered":
+            r = tempered_scores(q, Kh, p.block, C, p.beta)
+        else:
+            r = route_scores(q, mu[:C], sigma[:C], p.beta)
         idx, _, _ = select_topk(r, p.top_k)
         hits += int(pl["block"] in idx.tolist())
     return hits / len(plants)

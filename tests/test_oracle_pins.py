@@ -27,7 +27,8 @@ def _impl(**overrides):
         block_stats=OR.block_stats, route_scores=OR.route_scores,
         route_scores_from_logits=OR.route_scores_from_logits, select_topk=OR.select_topk,
         routable_blocks=OR.routable_blocks, key_set=OR.key_set, attend=OR.attend,
-        dropped_mass=OR.dropped_mass, recovery_weight=OR.recovery_weight)
+        dropped_mass=OR.dropped_mass, recovery_weight=OR.recovery_weight,
+        tempered_scores=OR.tempered_scores)
     for k, v in overrides.items():
         setattr(ns, k, v)
 
@@ -341,10 +342,58 @@ def check_invariances(ns, seed=9):
     assert abs((l2 - l1) - cshift) < 1e-12
 
 
+def check_tempered_closed_form(ns):
+    """Tempered score on hand-worked blocks (golden): two keys whose scaled
+    logits 0 and ln 3 average to exp-mean 2 give ln(2)/beta; equal logits give
+    the logit for every beta."""
+    ts = _golden()["tempered_score"]
+    q = np.zeros(4)
+    q[0] = 1.0
+    for case in ts["cases"]:
+        K = np.zeros((2, 4))
+        K[1, 0] = case["a"]
+        T = ns.tempered_scores(q, K, 2, 1, case["beta"])
+        assert abs(T[0] - case["T"]) < 1e-12, (case, T)
+    cl = ts["constant_logits"]
+    K = np.zeros((8, 4))
+    K[:, 0] = cl["s"]
+    for beta in cl["betas"]:
+        T = ns.tempered_scores(q, K, 4, 2, beta)
+        np.testing.assert_allclose(T, [cl["s"], cl["s"]], rtol=0, atol=1e-12)
+
+
+def check_tempered_limits(ns, seed=7):
+    """Tempered score against the logit moments (NumPy mean/var/max): beta -> 0
+    gives the block mean, the O(beta^2) remainder of mean + (beta/2) var, the
+    bound max - ln(B)/beta <= T <= max, and monotonicity in beta."""
+    rng = np.random.default_rng(seed)
+    B, d, C = 16, 8, 3
+    K = rng.normal(size=(C * B, d))
+    q = rng.normal(size=d)
+    logits = [K[c * B:(c + 1) * B] @ q for c in range(C)]
+    mean = np.array([np.mean(s) for s in logits])
+    var = np.array([np.var(s) for s in logits])
+    mx = np.array([np.max(s) for s in logits])
+    np.testing.assert_allclose(ns.tempered_scores(q, K, B, C, 1e-9), mean, rtol=0, atol=1e-6)
+    e2 = np.abs(ns.tempered_scores(q, K, B, C, 1e-2) - (mean + 0.5e-2 * var))
+    e3 = np.abs(ns.tempered_scores(q, K, B, C, 1e-3) - (mean + 0.5e-3 * var))
+    assert np.all(e2 < 1e-2) and np.all(e3 <= e2 / 30 + 1e-12), (e2, e3)
+    for beta in (50.0, 1e3):
+        T = ns.tempered_scores(q, K, B, C, beta)
+        assert np.all(T <= mx + 1e-12) and np.all(T >= mx - math.log(B) / beta - 1e-12)
+    prev = None
+    for beta in (0.1, 0.5, 1.0, 2.0, 4.0, 8.0):
+        T = ns.tempered_scores(q, K, B, C, beta)
+        if prev is not None:
+            assert np.all(T >= prev - 1e-12)
+        prev = T
+
+
 CHECKS = [check_golden, check_stats_vs_library, check_scores_two_ways, check_centroid_limit,
           check_topk_brute, check_dense_reduction, check_window_only, check_gather_equals_mask,
           check_recovery_law, check_recovery_law_pipeline, check_dropped_mass,
-          check_decode_equals_prefill, check_invariances]
+          check_decode_equals_prefill, check_invariances, check_tempered_closed_form,
+          check_tempered_limits]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda f: f.__name__)
@@ -433,6 +482,23 @@ def _mut_dropped_swapped(q, K, S, t, scale):
     return 1 - a, b
 
 
+def _mut_tempered_log_sum(q, K, B, C, beta):
+    return OR.tempered_scores(q, K, B, C, beta) + math.log(B) / beta
+
+
+def _mut_tempered_undivided(q, K, B, C, beta):
+    return OR.tempered_scores(q, K, B, C, beta) * beta
+
+
+def _mut_tempered_max(q, K, B, C, beta):
+    K = np.asarray(K, float)
+    return np.array([np.max(K[c * B:(c + 1) * B] @ q) for c in range(C)])
+
+
+def _mut_tempered_neg_beta(q, K, B, C, beta):
+    return -OR.tempered_scores(-np.asarray(q, float), K, B, C, beta)
+
+
 MUTANTS = {
     "sample_covariance": dict(block_stats=_mut_sample_cov),
     "beta_not_halved": dict(route_scores=_mut_full_beta),
@@ -447,6 +513,10 @@ MUTANTS = {
     "covariance_asymmetric": dict(block_stats=_mut_stats_transposed),
     "recovery_sign": dict(recovery_weight=_mut_recovery_sign),
     "dropped_mass_complement": dict(dropped_mass=_mut_dropped_swapped),
+    "tempered_log_sum_not_mean": dict(tempered_scores=_mut_tempered_log_sum),
+    "tempered_not_divided_by_beta": dict(tempered_scores=_mut_tempered_undivided),
+    "tempered_block_max": dict(tempered_scores=_mut_tempered_max),
+    "tempered_beta_sign": dict(tempered_scores=_mut_tempered_neg_beta),
 }
 
 
