@@ -31,13 +31,13 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "kv_chunks.hpp"
 #include "ssa_common.hpp"
 #include "ssa_internal.hpp"
 
 namespace ssa {
 namespace {
 
-constexpr int kAttnThreads = 256;          // window pass: 4 waves, 32 query rows each
 constexpr int kBlockThreads = 512;         // block pass: 8 waves, 32 query rows each
 constexpr int kTaskRows = 256;             // rows per block-attention task
 constexpr int kResidentBytes = 128 * 1024; // LDS that keeps a block's K/V images resident
@@ -45,193 +45,8 @@ constexpr int kRunTasks = 8;               // consecutive tasks a workgroup take
 constexpr int kStageBytes = 4096;          // LDS per wave that lines partials up for storing
 constexpr float kLazyLog2 = 8.f;           // probabilities may reach 2^kLazyLog2 before a rescale
 constexpr int kWinRows = 128;              // rows per window/merge tile
-constexpr int kKeyChunk = 64;              // keys per LDS chunk
 constexpr int kHistTokens = 2048;          // tokens per dispatch workgroup
 constexpr int kScanThreads = 1024;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-template <bool F32, int D>
-struct AT {
-  using In = typename std::conditional<F32, float, bf16_t>::type;
-  using Frag = typename std::conditional<F32, floatx8, bf16x8>::type;    // Q, K operands
-  using VFrag = typename std::conditional<F32, floatx8, f16x8>::type;    // P, V operands
-  static constexpr int ES = F32 ? 4 : 2;          // element bytes
-  static constexpr int LOG_NS = D == 128 ? 3 : 2;
-  static constexpr int FRAG = 64 * 8 * ES;         // one operand fragment
-  static constexpr int NS = D / 16;                // 16-wide chunks of d
-  static constexpr int MTD = D / 32;               // 32-wide tiles of d
-  static constexpr int KBYTES = 2 * NS * FRAG;     // 64 keys of K
-  static constexpr int VBYTES = MTD * 4 * FRAG;    // 64 keys of V
-  static constexpr int CHUNK = KBYTES + VBYTES;
-  static constexpr int PIECE = 4 * ES;             // 4 elements
-};
-
-// ---------------------------------------------------------------- helpers --
-
-// Copy `bytes` (a multiple of 1 KB) from global memory into LDS with direct
-// global->LDS loads: each wave moves 1 KB per instruction, waves interleave.
-__device__ __forceinline__ void dma_copy(uint8_t* lds, const uint8_t* src, int bytes, int tid,
-                                         int nthreads) {
-  const int wave = tid / 64, lane = tid % 64, waves = nthreads / 64;
-  for (int r = wave; r < bytes / 1024; r += waves)
-    __builtin_amdgcn_global_load_lds(src + r * 1024 + lane * 16,
-                                     (__attribute__((address_space(3))) void*)(lds + r * 1024), 16,
-                                     0, 0);
-}
-
-template <bool F32, int D>
-__device__ __forceinline__ typename AT<F32, D>::Frag load_row_frag(const typename AT<F32, D>::In* row,
-                                                                   int s, int h, bool valid) {
-  typename AT<F32, D>::Frag v;
-  if constexpr (F32) {
-    floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
-    if (valid) {
-      a = *reinterpret_cast<const floatx4*>(row + 16 * s + 8 * h);
-      b = *reinterpret_cast<const floatx4*>(row + 16 * s + 8 * h + 4);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = a[e];
-      v[e + 4] = b[e];
-    }
-  } else {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (valid) w = *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * h);
-    v = __builtin_bit_cast(bf16x8, w);
-  }
-  return v;
-}
-
-// Keys [key0, key0 + 64) of one head (rows >= n_keys read as zero), staged in
-// LDS as MFMA A-operand fragments:
-//   K part: fragment (mt, s), lane (m, h), element e = K[key0 + 32mt + m][16s + 8h + e]
-//   V part: fragment (mt, s), lane (m, h), element e = V[key0 + frag_k(s,h,e)][32mt + m]
-// K moves in 4-element pieces, assigned so that the 64 lanes of one LDS store
-// fill 512 contiguous bytes (no bank conflicts).  V is transposed through
-// registers in 4-key x 4-column tiles and, for bfloat16 inputs, converted to
-// float16 after scaling by an exact power of two (vscale) that keeps every
-// value of the head inside the float16 range: bf16 values then convert
-// exactly, so P V runs as one float16 MFMA with P carrying 11 fraction bits.
-// load() issues the global reads into registers and store() writes them to
-// LDS, so a chunk's reads are in flight while the previous chunk is computed.
-template <bool F32, int D>
-struct ChunkRegs {
-  using A = AT<F32, D>;
-  using In = typename A::In;
-  using PieceT = typename std::conditional<F32, floatx4, u32x2>::type;
-  static constexpr int KPT = kKeyChunk * (D / 4) / kAttnThreads;         // K pieces per thread
-  static constexpr int VPT = (kKeyChunk / 4) * (D / 4) / kAttnThreads;   // V tiles per thread
-  PieceT k[KPT];
-  PieceT v[VPT][4];
-
-  // piece w of the K chunk: lanes vary (m, sel) fastest, then h, s, mt
-  __device__ static __forceinline__ void kpiece(int w, int& mt, int& m, int& s, int& h, int& sel) {
-    m = w & 31;
-    sel = (w >> 5) & 1;
-    h = (w >> 6) & 1;
-    s = (w >> 7) & (A::NS - 1);
-    mt = w >> (7 + A::LOG_NS);
-  }
-
-  __device__ __forceinline__ void load(const In* Kh, const In* Vh, int64_t key0, int64_t n_keys,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      int mt, m, s, h, sel;
-      kpiece(tid + i * kAttnThreads, mt, m, s, h, sel);
-      const int r = 32 * mt + m;
-      k[i] = PieceT{};
-      if (key0 + r < n_keys)
-        k[i] = *reinterpret_cast<const PieceT*>(Kh + (key0 + r) * D + 16 * s + 8 * h + 4 * sel);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int w = tid + i * kAttnThreads, kq = w / (D / 4), dq = w % (D / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[i][r] = PieceT{};
-        if (key0 + 4 * kq + r < n_keys)
-          v[i][r] = *reinterpret_cast<const PieceT*>(Vh + (key0 + 4 * kq + r) * D + 4 * dq);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* lds, int tid, float vscale) const {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      int mt, m, s, h, sel;
-      kpiece(tid + i * kAttnThreads, mt, m, s, h, sel);
-      *reinterpret_cast<PieceT*>(lds + (mt * A::NS + s) * A::FRAG + (h * 32 + m) * 8 * A::ES +
-                                 sel * A::PIECE) = k[i];
-    }
-    uint8_t* vl = lds + A::KBYTES;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int w = tid + i * kAttnThreads, kq = w / (D / 4), dq = w % (D / 4);
-      const int s = kq / 4, kg = kq % 4, sel = kg >> 1, h = kg & 1;
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        const int d = 4 * dq + dd, mt = d / 32, m = d % 32;
-        PieceT col;
-        if constexpr (F32) {
-          col = floatx4{v[i][0][dd], v[i][1][dd], v[i][2][dd], v[i][3][dd]};
-        } else {
-          const int word = dd >> 1, shift = (dd & 1) * 16;
-          uint32_t e[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float x = bf16_bits_to_f32((v[i][r][word] >> shift) & 0xFFFFu) * vscale;
-            e[r] = __builtin_bit_cast(u16, static_cast<_Float16>(x));
-          }
-          col = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-        }
-        *reinterpret_cast<PieceT*>(vl + (mt * 4 + s) * A::FRAG + (h * 32 + m) * 8 * A::ES +
-                                   sel * A::PIECE) = col;
-      }
-    }
-  }
-};
-
-// Power-of-two scale for the float16 value operand of one head: vexp_bits is
-// the largest |v| of the head as bfloat16 bits; returns e >= 0 with
-// max|v| * 2^-e < 2^15.
-__device__ __forceinline__ int value_exponent(uint32_t vmax_bits) {
-  const float vmax = bf16_bits_to_f32(vmax_bits & 0x7FFFu);
-  int E = 0;
-  if (vmax > 0.f) (void)frexpf(vmax, &E);   // vmax < 2^E
-  return E > 15 ? E - 15 : 0;
-}
-
-// Chunk images: every 64-key chunk of every head, already in the LDS layout
-// above (K fragments, then V transposed and, for bfloat16 inputs, converted to
-// float16).  Written once per call; the attention kernels then stage a chunk
-// with straight 16-byte global->LDS DMA loads, no registers and no transposes.
-template <bool F32, int D>
-__global__ __launch_bounds__(kAttnThreads) void kv_image_kernel(
-    const typename AT<F32, D>::In* __restrict__ K, const typename AT<F32, D>::In* __restrict__ V,
-    const uint32_t* __restrict__ vmax, uint8_t* __restrict__ img, int64_t n, int64_t n_chunks) {
-  using A = AT<F32, D>;
-  const int64_t ci = blockIdx.x, bkv = blockIdx.y;
-  const float vscale = F32 ? 1.f : ldexpf(1.f, -value_exponent(vmax[bkv]));
-  ChunkRegs<F32, D> cr;
-  cr.load(K + bkv * n * D, V + bkv * n * D, ci * kKeyChunk, n, threadIdx.x);
-  cr.store(img + (bkv * n_chunks + ci) * A::CHUNK, threadIdx.x, vscale);
-}
-
-// Copy one chunk image (A::CHUNK bytes) into LDS: each wave moves a quarter,
-// 1 KB per instruction, global -> LDS directly.
-template <bool F32, int D>
-__device__ __forceinline__ void stage_chunk_dma(uint8_t* lds, const uint8_t* src, int tid) {
-  constexpr int PER_WAVE = AT<F32, D>::CHUNK / (kAttnThreads / 64);
-  const int wave = tid / 64, lane = tid % 64;
-#pragma unroll
-  for (int i = 0; i < PER_WAVE / 1024; ++i) {
-    const int off = wave * PER_WAVE + i * 1024;
-    __builtin_amdgcn_global_load_lds(src + off + lane * 16,
-                                     (__attribute__((address_space(3))) void*)(lds + off), 16, 0, 0);
-  }
-}
 
 // Running softmax state of one query row, split over the two lane halves.
 template <int D>
@@ -452,38 +267,12 @@ __device__ __forceinline__ void accumulate_partial(floatx16 (&o)[MTD], const Par
   }
 }
 
-// Largest |v| of every (sequence, KV head), as bfloat16 bits (order-preserving
-// for non-negative values), for the float16 value scale.
-__global__ __launch_bounds__(256) void value_max_kernel(const bf16_t* __restrict__ V,
-                                                        uint32_t* __restrict__ vmax,
-                                                        int64_t per_head) {
-  const int64_t bkv = blockIdx.y;
-  const u32x4* src = reinterpret_cast<const u32x4*>(V + bkv * per_head);
-  const int64_t n16 = per_head / 8;
-  uint32_t m = 0;
-  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n16;
-       i += int64_t(gridDim.x) * blockDim.x) {
-    const u32x4 w = src[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = max(m, uint32_t(__shfl_xor(int(m), o, 64)));
-  if ((threadIdx.x & 63) == 0) atomicMax(&vmax[bkv], m);
-}
-
 // ---------------------------------------------------------------- dispatch --
 
 template <typename PartT, int D>
 __global__ void null_partial_kernel(PartT* o_part, float2* lse_part, int64_t slot) {
   for (int i = threadIdx.x; i < D; i += blockDim.x) o_part[slot * D + i] = PartT{};
   if (threadIdx.x == 0) lse_part[slot] = float2{-__builtin_inff(), -__builtin_inff()};
-}
-
-__global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {
-  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count;
-       i += int64_t(gridDim.x) * blockDim.x)
-    p[i] = v;
 }
 
 // SCATTER = false: add this workgroup's histogram of selected blocks into
