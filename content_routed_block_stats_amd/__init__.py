@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     make_params,
     ssa_block_stats,
     ssa_decode_step,
+    ssa_route_tempered,
     ssa_route_topk,
     ssa_sparse_attn_fwd,
     ssa_workspace_size,

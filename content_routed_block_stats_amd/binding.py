@@ -66,11 +66,12 @@ def lib() -> ctypes.CDLL:
     L.ssa_block_stats.argtypes = [P, _vp, _vp, _vp, _vp]
     L.ssa_workspace_size.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     L.ssa_route_topk.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.ssa_route_tempered.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
     L.ssa_sparse_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_decode_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
-    for name in ("ssa_block_stats", "ssa_workspace_size", "ssa_route_topk", "ssa_sparse_attn_fwd",
-                 "ssa_decode_step"):
+    for name in ("ssa_block_stats", "ssa_workspace_size", "ssa_route_topk", "ssa_route_tempered",
+                 "ssa_sparse_attn_fwd", "ssa_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
@@ -176,6 +177,25 @@ def ssa_route_topk(Q: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, *, bl
     ws = _workspace(p, SSA_OP_ROUTE, Q.device, workspace)
     _check(lib().ssa_route_topk(ctypes.byref(p), _ptr(Q), _ptr(mu), _ptr(sigma), _ptr(idx),
                                 _ptr(kth), _ptr(ws), ws.numel(), _stream()))
+    return (idx, kth) if want_kth else idx
+
+
+def ssa_route_tempered(Q: torch.Tensor, K: torch.Tensor, *, block_size: int, top_k: int,
+                       beta: float, want_kth: bool = False, idx: torch.Tensor | None = None):
+    """Exact tempered routing: Q [b, Hq, n, d], K [b, Hkv, n, d] -> idx [b, Hq, n, k] int32
+    (, kth [.., 2]): top-k of (1/beta) ln mean_j exp(beta q.k_j) over routable blocks."""
+    _dev_check(Q, K)
+    b, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    if K.shape != (b, hkv, n, d) or K.dtype != Q.dtype:
+        raise ValueError("K does not match Q")
+    p = make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=n,
+                    block_size=block_size, top_k=top_k, beta=beta, in_dtype=Q.dtype)
+    if idx is None:
+        idx = torch.empty((b, hq, n, top_k), dtype=torch.int32, device=Q.device)
+    kth = torch.empty((b, hq, n, 2), dtype=torch.float32, device=Q.device) if want_kth else None
+    _check(lib().ssa_route_tempered(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(idx), _ptr(kth),
+                                    _stream()))
     return (idx, kth) if want_kth else idx
 
 

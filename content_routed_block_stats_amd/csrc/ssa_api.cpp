@@ -110,6 +110,22 @@ ssa_status ssa_block_stats(const ssa_params* p, const void* K, float* mu, float*
                   "ssa_block_stats");
 }
 
+ssa_status ssa_route_tempered(const ssa_params* p, const void* Q, const void* K, int32_t* idx,
+                              float* kth, void* stream) {
+  ssa::Shape s;
+  ssa_status st = check_params(p, &s);
+  if (st != SSA_OK) return st;
+  if (!(p->beta > 0.f)) return fail(SSA_ERR_INVALID_ARGUMENT, "the tempered score needs beta > 0");
+  SSA_NONNULL(Q);
+  SSA_NONNULL(K);
+  if (s.k > 0) SSA_NONNULL(idx);
+  if (ssa::tempered_route_tiles(s) >= (int64_t(1) << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "too many query rows for one launch");
+  if (s.k == 0 && kth == nullptr) return ok();
+  return from_hip(ssa::launch_route_tempered(s, Q, K, idx, kth, (hipStream_t)stream),
+                  "ssa_route_tempered");
+}
+
 ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes) {
   ssa::Shape s;
   ssa_status st = check_params(p, &s);

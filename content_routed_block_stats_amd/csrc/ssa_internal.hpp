@@ -32,6 +32,12 @@ size_t route_workspace_bytes(const Shape& s);
 hipError_t launch_route_topk(const Shape& s, const void* Q, const float* mu, const float* sigma,
                              int32_t* idx, float* kth, void* ws, hipStream_t st);
 
+// exact tempered block score + top-k (prefill); no workspace.  Grid size in
+// workgroups (must stay below 2^31).
+int64_t tempered_route_tiles(const Shape& s);
+hipError_t launch_route_tempered(const Shape& s, const void* Q, const void* K, int32_t* idx,
+                                 float* kth, hipStream_t st);
+
 // sparse attention (prefill)
 size_t attn_workspace_bytes(const Shape& s);
 // entry / partial slots of the block pass (tasks padded to whole task rows);

@@ -116,6 +116,29 @@ ssa_status ssa_route_topk(const ssa_params* p, const void* Q, const float* mu,
                           const float* sigma, int32_t* idx, float* kth, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Exact tempered routing and top-k (write-up, "The idea in one screen": the
+ * temperature family that links the centroid score, the second-cumulant
+ * score and the exact block maximum).  For every query row (b, h, t) and every
+ * routable block c ((c+1)B-1 <= t):
+ *   T_c = (1/beta) ln( (1/B) sum_{j in block c} exp(beta q.k_j) )   (raw q)
+ * whose expansion to second order in beta is the ssa_route_topk score; then
+ * the same top-k rule (min(k, #routable) highest, ties to the lower c).
+ *   Q    [b, Hq, n, d]   in_dtype
+ *   K    [b, Hkv, n, d]  in_dtype (the keys themselves: every key of every
+ *                        routable block is read, so the cost is that of
+ *                        dense causal Q K^T)
+ *   idx  [b, Hq, n, k]   int32, written as by ssa_route_topk
+ *   kth  [b, Hq, n, 2]   float32, written if not NULL: k-th and (k+1)-th
+ *                        largest T (-inf where absent)
+ * beta must be > 0 (SSA_ERR_INVALID_ARGUMENT otherwise).  No workspace.
+ * Limits (SSA_ERR_UNSUPPORTED otherwise): b * Hkv * ceil(n Hq/Hkv / 256)
+ * below 2^31.
+ * Arithmetic: q.k_j on MFMA (bf16 products exact, float32 accumulation;
+ * float32 MFMA for float32 inputs), the log-sum-exp in float32 in base 2 with
+ * the block's maximum factored out. */
+ssa_status ssa_route_tempered(const ssa_params* p, const void* Q, const void* K, int32_t* idx,
+                              float* kth, void* stream);
+
 /* Sparse attention forward (write-up, introduction steps ii-iii).  For every
  * query row (b, h, t):
  *   S(t) = union of the keys of the blocks in idx(b,h,t) (entries < 0 are

@@ -99,3 +99,25 @@ def test_workspace_sizes_scale_with_problem():
 def test_status_strings():
     for code in range(5):
         assert B.status_string(code).startswith("SSA_")
+
+
+@pytest.mark.parametrize("beta", [0.0, -1.0, float("inf")])
+def test_tempered_route_rejects_non_positive_beta(beta):
+    p = _p(beta=beta)
+    got = ssa.lib().ssa_route_tempered(ctypes.byref(p), 256, 256, 256, None, None)
+    assert got == B.SSA_ERR_INVALID_ARGUMENT, B.status_string(got)
+    assert "beta" in ssa.lib().ssa_last_error().decode()
+
+
+def test_tempered_route_checks_pointers_on_host():
+    p = _p(beta=2.0)
+    L = ssa.lib()
+    assert L.ssa_route_tempered(ctypes.byref(p), None, 256, 256, None, None) == \
+        B.SSA_ERR_INVALID_ARGUMENT                    # Q NULL
+    assert L.ssa_route_tempered(ctypes.byref(p), 256, None, 256, None, None) == \
+        B.SSA_ERR_INVALID_ARGUMENT                    # K NULL
+    assert L.ssa_route_tempered(ctypes.byref(p), 256, 256, None, None, None) == \
+        B.SSA_ERR_INVALID_ARGUMENT                    # idx NULL with top_k > 0
+    # nothing requested (k = 0, no kth): returns before any launch
+    p0 = _p(beta=2.0, top_k=0)
+    assert L.ssa_route_tempered(ctypes.byref(p0), 256, 256, None, None, None) == B.SSA_OK
