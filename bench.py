@@ -2,6 +2,7 @@
 """Throughput of the SSA hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --recall-sweep [--workload NAME]
 
 A step is one pass of the prefill hot path over one batch of seeded synthetic
 input already resident in HBM: ssa_block_stats -> ssa_route_topk ->
@@ -9,8 +10,11 @@ ssa_sparse_attn_fwd.  The default workload is the n = 131072 GQA prefill
 (32 q-heads / 8 KV heads, d = 128, bf16, B = 256, k = 16, W = 256, beta = 2).
 Prints ONE JSON line: query-tokens/s, per-stage times from HIP events on the
 launch stream, the routing kernel against the bf16 MFMA roofline, the gather
-against the HBM roofline, a decode step on the 32 x 256K-token cache, and the
-CPU oracle timed on a bounded sample of the same workload.
+against the HBM roofline, the exact tempered router (ssa_route_tempered, same
+workload and beta, outside the step) against the MFMA roofline, a decode step
+on the 32 x 256K-token cache, and the CPU oracle timed on a bounded sample of
+the same workload.  --recall-sweep instead prints the planted-target recall of
+the centroid, second-cumulant and tempered scores across beta.
 """
 from __future__ import annotations
 
@@ -174,6 +178,62 @@ def bench_decode(steps: int, warmup: int) -> dict:
             "steps": steps}
 
 
+def tempered_flops(wl) -> float:
+    """Algorithmic flops of the exact tempered score: 2d per (query row, key of a routable block)."""
+    n, B, d = wl.seq_len, wl.block, wl.head_dim
+    nb = n // B
+    pairs_per_head = B * nb * (nb - 1) // 2 + (n - nb * B + 1) * nb
+    return float(wl.batch * wl.n_q_heads * pairs_per_head) * B * 2 * d
+
+
+def recall_sweep(wl, seed: int, betas: list[float]) -> dict:
+    """Planted-target recall of the centroid / second-cumulant / exact tempered
+    scores across beta, and how often the cumulant selection agrees with the
+    tempered one, on the seeded planted generator (every plant's target row
+    asks whether its planted block is selected)."""
+    import torch
+
+    import content_routed_block_stats_amd as ssa
+    from synth_inputs import make_prefill
+
+    data = make_prefill(wl, seed=seed, device="cuda")
+    Q, K = data["Q"], data["K"]
+    mu, sigma = ssa.ssa_block_stats(K, wl.block)
+    plants = data["plants"]
+    pb = torch.tensor([p["b"] for p in plants], device="cuda")
+    ph = torch.tensor([p["h"] for p in plants], device="cuda")
+    pt = torch.tensor([p["t"] for p in plants], device="cuda")
+    pc = torch.tensor([p["block"] for p in plants], device="cuda", dtype=torch.int32)
+    # agreement sample: rows with more routable blocks than k
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    t_lo = (wl.top_k + 1) * wl.block - 1
+    m = 16384
+    sb = torch.randint(wl.batch, (m,), generator=gen).cuda()
+    sh = torch.randint(wl.n_q_heads, (m,), generator=gen).cuda()
+    st = torch.randint(t_lo, wl.seq_len, (m,), generator=gen).cuda()
+
+    def recall(idx):
+        return float((idx[pb, ph, pt] == pc[:, None]).any(-1).float().mean())
+
+    rows = []
+    for beta in betas:
+        idx_c = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=beta)
+        rec = {"beta": beta, "recall_cumulant": round(recall(idx_c), 4)}
+        if beta > 0:
+            idx_t = ssa.ssa_route_tempered(Q, K, block_size=wl.block, top_k=wl.top_k, beta=beta)
+            a, b_ = idx_c[sb, sh, st], idx_t[sb, sh, st]
+            agree = (a[:, :, None] == b_[:, None, :]).any(-1).float().mean()
+            rec.update(recall_tempered=round(recall(idx_t), 4),
+                       cumulant_vs_tempered_overlap=round(float(agree), 4))
+            del idx_t
+        del idx_c
+        rows.append(rec)
+    torch.cuda.synchronize()
+    return {"study": "planted recall vs beta", "workload": wl.name, "seed": seed,
+            "plants": len(plants), "agreement_rows": m, "centroid_is_beta_0": True,
+            "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +244,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--recall-sweep", action="store_true",
+                    help="only print the planted-recall-vs-beta study for --workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 2 GiB device->device (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -212,6 +274,10 @@ def main() -> int:
     if wl.decode:
         print("choose a prefill workload", file=sys.stderr)
         return 2
+    if args.recall_sweep:
+        betas = [0.0, 0.25, 0.5, 1.0, 2.0, 4.0, 8.0, 16.0, 32.0]
+        print(json.dumps(recall_sweep(wl, args.seed, betas)), flush=True)
+        return 0
     dev = "cuda"
     print(f"[bench] generating {wl.name} on {torch.cuda.get_device_name(0)}", file=sys.stderr,
           flush=True)
@@ -267,7 +333,7 @@ def main() -> int:
     gb = gather_bytes(wl)
     gbs = gb / (t_attn * 1e-3) / 1e9
     route_digest = kernel_source_digest("route_topk.hip", "ssa_common.hpp")
-    attn_digest = kernel_source_digest("sparse_attn.hip", "ssa_common.hpp")
+    attn_digest = kernel_source_digest("sparse_attn.hip", "kv_chunks.hpp", "ssa_common.hpp")
     tokens = b * n
     res = {
         "metric": "SSA prefill query-tokens/s at n=128K + % of MFMA/HBM roofline",
@@ -298,6 +364,21 @@ def main() -> int:
                             "traffic": counted_traffic("sparse_attn_fwd", attn_digest),
                             "algorithmic_bytes_per_launch": gb},
     }
+    # the exact tempered score (same workload and beta), outside the step
+    ssa.ssa_route_tempered(Q, K, block_size=wl.block, top_k=wl.top_k, beta=wl.beta, idx=idx)
+    te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    te0.record()
+    for _ in range(reps):
+        ssa.ssa_route_tempered(Q, K, block_size=wl.block, top_k=wl.top_k, beta=wl.beta, idx=idx)
+    te1.record()
+    torch.cuda.synchronize()
+    t_temp = te0.elapsed_time(te1) / reps
+    tf = tempered_flops(wl) / (t_temp * 1e-3) / 1e12
+    res["tempered_route"] = {"kernel": "tempered_route", "ms": round(t_temp, 3), "bound": "mfma",
+                             "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "algorithmic_flops_per_launch": tempered_flops(wl), "reps": reps}
     del O, lse, ws_a, ws_r
     if not args.no_decode:
         print("[bench] decode step", file=sys.stderr, flush=True)
