@@ -38,8 +38,8 @@
 namespace ssa {
 namespace {
 
-constexpr int kTempThreads = 256;   // 4 waves: one per SIMD, two workgroups per CU
-constexpr int kTempRows = 256;      // 64 query rows per wave
+constexpr int kTempThreads = 512;   // 8 waves, two per SIMD in two groups
+constexpr int kTempRows = 512;      // 64 query rows per wave
 constexpr float kTempLazy = 8.f;    // largest term of a running sum, log2
 
 // Keys [key0, key0 + 64) of one head -> LDS, K fragment (mt, s) at
@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kTempThreads) void tempered_route_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * A::KBYTES];
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int grp = wave / (kTempThreads / 128);      // waves w and w + 4 share a SIMD
   const int64_t wid = blockIdx.x;
   const int64_t bkv = wid % n_bkv;
   const int64_t tile = n_tiles - 1 - wid / n_bkv;   // longest rows first
@@ -117,30 +118,22 @@ __global__ __launch_bounds__(kTempThreads) void tempered_route_kernel(
     li[i] = -1;
   }
 
-  if (n_chunks > 0) stage_keys<F32, D>(lds, Kh, 0, wave, lane);
-  __syncthreads();
-
-  float m2[2] = {0.f, 0.f}, l[2] = {0.f, 0.f};
-  for (int64_t ch = 0; ch < n_chunks; ++ch) {
-    if (ch + 1 < n_chunks)
-      stage_keys<F32, D>(lds + ((ch + 1) & 1) * A::KBYTES, Kh, (ch + 1) * kKeyChunk, wave, lane);
-    const uint8_t* L = lds + (ch & 1) * A::KBYTES;
+  floatx16 sacc[2][2];
+  // S^T = K Q^T for the chunk in LDS buffer L.  K fragments move in pairs of
+  // 16-wide chunks (4 fragments); the next pair's LDS reads are issued after
+  // the second MFMA of the current pair, so the wait before a pair covers
+  // that pair alone (while a direct-to-LDS copy is in flight only a full wait
+  // on LDS reads is possible).
+  auto scores = [&](const uint8_t* L) {
     auto kfrag = [&](int mt, int s) {
       return *reinterpret_cast<const Frag*>(L + (mt * NS + s) * A::FRAG + lane * 8 * A::ES);
     };
-
-    floatx16 sacc[2][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[nt][mt][j] = 0.f;
-    // S^T = K Q^T.  K fragments move in pairs of 16-wide chunks (4
-    // fragments); the next pair's LDS reads are issued after the second MFMA
-    // of the current pair, so the wait before a pair covers that pair alone
-    // (while a direct-to-LDS copy is in flight only a full wait on LDS reads
-    // is possible).
     Frag ka[2][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) ka[0][q] = kfrag(q % 2, q / 2);
@@ -158,10 +151,15 @@ __global__ __launch_bounds__(kTempThreads) void tempered_route_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
 
-    // running base-2 log-sum-exp per row; lane (ln, h) holds keys
-    // 32mt + 8a + 4h + b of the chunk for rows 32nt + ln
-    const bool first = ch % cpb == 0;
+  // Running base-2 log-sum-exp per row over the chunk's logits (lane (ln, h)
+  // holds keys 32mt + 8a + 4h + b of the chunk for rows 32nt + ln); at a
+  // block's last chunk, its score enters the running top-(k+1).
+  float m2[2] = {0.f, 0.f}, l[2] = {0.f, 0.f};
+  int jb = 0;          // chunk within the current block
+  int64_t cb = 0;      // current block
+  auto accumulate = [&]() {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float mx = -__builtin_inff();
@@ -170,7 +168,7 @@ __global__ __launch_bounds__(kTempThreads) void tempered_route_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[nt][mt][j]);
       mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * c2;
-      if (first) {
+      if (jb == 0) {
         m2[nt] = mx;
         l[nt] = 0.f;
       } else if (__builtin_amdgcn_ballot_w64(mx > m2[nt] + kTempLazy) != 0) {
@@ -186,17 +184,15 @@ __global__ __launch_bounds__(kTempThreads) void tempered_route_kernel(
           ps[j % 4] += __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][j], c2, -m2[nt]));
       l[nt] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     }
-
-    if (ch % cpb == cpb - 1) {
-      const int64_t c = ch / cpb;
+    if (jb == cpb - 1) {
       float T[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const float lt = l[nt] + wave_shfl_xor(l[nt], 32);
         T[nt] = ((m2[nt] + __builtin_amdgcn_logf(lt)) * kLn2 - log_b) * inv_beta;
       }
-      float sc = (c < my_C) ? (h ? T[1] : T[0]) : -__builtin_inff();
-      int ci = int(c);
+      float sc = (cb < my_C) ? (h ? T[1] : T[0]) : -__builtin_inff();
+      int ci = int(cb);
       // one pass of the running top-(k+1); strict > keeps the lower block on ties
 #pragma unroll
       for (int i = 0; i <= KMAX; ++i) {
@@ -208,6 +204,31 @@ __global__ __launch_bounds__(kTempThreads) void tempered_route_kernel(
         sc = gt ? ts : sc;
         ci = gt ? ti : ci;
       }
+      jb = 0;
+      ++cb;
+    } else {
+      ++jb;
+    }
+  };
+
+  // Half-step schedule.  Every wave alternates scores(c) and accumulate(c);
+  // the second group of waves runs half a step behind the first, so on each
+  // SIMD one wave issues MFMAs while the other runs the exponentials.  Chunk
+  // c + 1 is staged during half-step 2c + 1 into the buffer that chunk c - 1
+  // used (read by both groups before half-step 2c); the barrier that ends a
+  // half-step also waits for the copies issued in it.
+  if (n_chunks > 0) stage_keys<F32, D>(lds, Kh, 0, wave, lane);
+  __syncthreads();
+  for (int64_t hs = 0; hs <= 2 * n_chunks; ++hs) {
+    const int64_t c = hs >> 1;
+    if ((hs & 1) && c + 1 < n_chunks)
+      stage_keys<F32, D>(lds + ((c + 1) & 1) * A::KBYTES, Kh, (c + 1) * kKeyChunk, wave, lane);
+    const int64_t j = hs - grp;
+    if (j >= 0 && j < 2 * n_chunks) {
+      if ((j & 1) == 0)
+        scores(lds + ((j >> 1) & 1) * A::KBYTES);
+      else
+        accumulate();
     }
     __syncthreads();
   }
