@@ -160,6 +160,49 @@ def tempered_row(q: np.ndarray, K: np.ndarray, B: int, k: int, beta: float, t: i
     return dict(idx=idx, scores=r, r_k=r_k, r_k1=r_k1)
 
 
+# -- query-tile-shared routing (block-level selection) ------------------------
+#
+# The write-up's fast kernel routes per query block: its cost notes name an
+# (n/b)^2 block-score GEMM and an argsort BlockMask build.  Reading: query
+# tile j holds positions [jB, (j+1)B) of one (sequence, q-head); the tile
+# selects one set of blocks for all its queries, the top k of the tile's
+# summed routing score R_c = sum_{t in tile} r_c(q_t) over the blocks complete
+# before the tile starts (c < j); each row then attends exactly over the
+# tile's blocks plus its own window.
+
+def tile_routable_blocks(j: int, nb: int) -> int:
+    """Blocks routable for query tile j: those complete before the tile's first
+    query, c < j (c + 1 <= j, so (c+1)B - 1 <= jB - 1 < jB)."""
+    return max(0, min(nb, j))
+
+
+def tile_scores(Qt: np.ndarray, mu: np.ndarray, sigma: np.ndarray, beta: float) -> np.ndarray:
+    """R_c = sum over the tile's query rows of r_c(q_t), for every block given."""
+    Qt = as_f64(Qt)
+    R = np.zeros(np.asarray(mu).shape[0])
+    for q in Qt:
+        R += route_scores(q, mu, sigma, beta)
+    return R
+
+
+def tile_select(Qh: np.ndarray, mu: np.ndarray, sigma: np.ndarray, p: Params, j: int) -> dict:
+    """Selection of query tile j of one (sequence, q-head): Qh [n, d] are the
+    head's queries, mu/sigma its KV head's block statistics."""
+    Qh = as_f64(Qh)
+    n = Qh.shape[0]
+    C = tile_routable_blocks(j, mu.shape[0])
+    R = tile_scores(Qh[j * p.block:min(n, (j + 1) * p.block)], mu[:C], sigma[:C], p.beta)
+    idx, r_k, r_k1 = select_topk(R, p.top_k)
+    return dict(idx=idx, scores=R, r_k=r_k, r_k1=r_k1)
+
+
+def tile_prefill_row(q, K, V, tile_idx: np.ndarray, p: Params, t: int) -> dict:
+    """Exact attention of row t over its tile's selected blocks and its window."""
+    S = key_set(t, tile_idx, p.block, p.window)
+    O, lse = attend(q, K, V, S, p.scale)
+    return dict(S=S, O=O, lse=lse)
+
+
 # -- step 3: top-k selection ---------------------------------------------------
 
 def select_topk(r: np.ndarray, k: int) -> tuple[np.ndarray, float, float]:

@@ -28,9 +28,24 @@ def _impl(**overrides):
         route_scores_from_logits=OR.route_scores_from_logits, select_topk=OR.select_topk,
         routable_blocks=OR.routable_blocks, key_set=OR.key_set, attend=OR.attend,
         dropped_mass=OR.dropped_mass, recovery_weight=OR.recovery_weight,
-        tempered_scores=OR.tempered_scores)
+        tempered_scores=OR.tempered_scores, tile_routable_blocks=OR.tile_routable_blocks,
+        tile_scores=OR.tile_scores)
     for k, v in overrides.items():
         setattr(ns, k, v)
+
+    def tile_select(Qh, mu, sigma, p, j):
+        n = Qh.shape[0]
+        C = ns.tile_routable_blocks(j, mu.shape[0])
+        R = ns.tile_scores(Qh[j * p.block:min(n, (j + 1) * p.block)], mu[:C], sigma[:C], p.beta)
+        idx, r_k, r_k1 = ns.select_topk(R, p.top_k)
+        return dict(idx=idx, scores=R, r_k=r_k, r_k1=r_k1)
+
+    def tile_prefill_row(q, K, V, tile_idx, p, t):
+        S = ns.key_set(t, tile_idx, p.block, p.window)
+        Oo, lse = ns.attend(q, K, V, S, p.scale)
+        return dict(S=S, O=Oo, lse=lse)
+    ns.tile_select = tile_select
+    ns.tile_prefill_row = tile_prefill_row
 
     def prefill_row(q, K, V, mu, sigma, p, t, with_dense=False):
         C = ns.routable_blocks(t, p.block, mu.shape[0])
@@ -389,11 +404,98 @@ def check_tempered_limits(ns, seed=7):
         prev = T
 
 
+def check_tile_scores_moments(ns, seed=11):
+    """Tile score two ways: the sum over the tile's rows of the logit moments
+    (NumPy mean and population variance of q_t.k_j over each block, no block
+    statistics) and the closed form s.mu_c + (beta/2) <Sigma_c, M> with
+    s = sum_t q_t and M = sum_t q_t q_t^T."""
+    rng = np.random.default_rng(seed)
+    for (T, d, B, C, beta) in ((5, 6, 8, 4, 2.0), (1, 3, 4, 3, 0.7), (9, 4, 16, 2, 5.0)):
+        Qt = rng.normal(size=(T, d))
+        K = rng.normal(size=(C * B, d)) + rng.normal(size=(C, 1, d)).repeat(B, 1).reshape(C * B, d)
+        mu, sigma = ns.block_stats(K, B)
+        R = ns.tile_scores(Qt, mu, sigma, beta)
+        want = np.zeros(C)
+        for c in range(C):
+            L = Qt @ K[c * B:(c + 1) * B].T          # [T, B] logits
+            want[c] = np.sum(np.mean(L, axis=1) + 0.5 * beta * np.var(L, axis=1))
+        np.testing.assert_allclose(R, want, rtol=1e-12, atol=1e-11)
+        s_, M = Qt.sum(0), Qt.T @ Qt
+        closed = np.array([s_ @ mu[c] + 0.5 * beta * np.sum(sigma[c] * M) for c in range(C)])
+        np.testing.assert_allclose(R, closed, rtol=1e-12, atol=1e-11)
+
+
+def check_tile_select_brute(ns, seed=12):
+    """The tile's selection is the k-subset of routable blocks with the largest
+    total routing score over the tile's rows (brute force over subsets, scores
+    from the raw logits), and no block at or after the tile is routable."""
+    import itertools
+    rng = np.random.default_rng(seed)
+    n, d, B = 70, 4, 8
+    Q, K, _ = _rand_head(rng, n, d, B)
+    mu, sigma = ns.block_stats(K, B)
+    nb = n // B
+    for k in (1, 2, 3):
+        p = O.Params(B, k, B, 2.0, 0.5)
+        for j in range(0, (n + B - 1) // B):
+            sel = ns.tile_select(Q, mu, sigma, p, j)
+            rows = Q[j * B:min(n, (j + 1) * B)]
+            C = min(j, nb)
+            total = np.zeros(C)
+            for c in range(C):
+                L = rows @ K[c * B:(c + 1) * B].T
+                total[c] = np.sum(np.mean(L, 1) + np.var(L, 1))   # beta / 2 = 1
+            got = [c for c in sel["idx"].tolist() if c >= 0]
+            assert all(c < j for c in got), (j, got)
+            assert len(got) == min(k, C)
+            if C:
+                best = max(itertools.combinations(range(C), min(k, C)),
+                           key=lambda S: sum(total[c] for c in S))
+                assert sorted(best) == got, (j, k, got, best)
+
+
+def check_tile_single_row(ns, seed=13):
+    """A tile holding one query (position jB) selects what that row selects by
+    itself: the tile's routable blocks are exactly the row's."""
+    rng = np.random.default_rng(seed)
+    d, B = 5, 8
+    for j in (0, 1, 3, 6):
+        n = j * B + 1
+        Q, K, V = _rand_head(rng, n, d, B)
+        mu, sigma = ns.block_stats(K, B)
+        p = O.Params(B, 2, 4, 2.0, 0.4)
+        tile = ns.tile_select(Q, mu, sigma, p, j)
+        row = ns.prefill_row(Q[j * B], K, V, mu, sigma, p, j * B)
+        assert tile["idx"].tolist() == row["idx"].tolist(), (j, tile["idx"], row["idx"])
+        np.testing.assert_allclose(tile["scores"], row["scores"], rtol=1e-12, atol=1e-12)
+
+
+def check_tile_dense_reduction(ns, seed=14):
+    """k >= nb and W >= B: every row of every tile attends to all keys <= t,
+    i.e. dense causal attention (torch SDPA, CPU float64)."""
+    rng = np.random.default_rng(seed)
+    for (n, d, B, W) in ((67, 8, 8, 8), (50, 6, 5, 9)):
+        Q, K, V = _rand_head(rng, n, d, B)
+        mu, sigma = ns.block_stats(K, B)
+        scale = 1 / math.sqrt(d)
+        p = O.Params(B, n // B + 2, W, 2.0, scale)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(Q)[None, None], torch.tensor(K)[None, None], torch.tensor(V)[None, None],
+            is_causal=True, scale=scale)[0, 0].numpy()
+        for j in range((n + B - 1) // B):
+            sel = ns.tile_select(Q, mu, sigma, p, j)
+            for t in range(j * B, min(n, (j + 1) * B)):
+                row = ns.tile_prefill_row(Q[t], K, V, sel["idx"], p, t)
+                assert row["S"].tolist() == list(range(t + 1)), (t, row["S"])
+                np.testing.assert_allclose(row["O"], ref[t], rtol=1e-12, atol=1e-12)
+
+
 CHECKS = [check_golden, check_stats_vs_library, check_scores_two_ways, check_centroid_limit,
           check_topk_brute, check_dense_reduction, check_window_only, check_gather_equals_mask,
           check_recovery_law, check_recovery_law_pipeline, check_dropped_mass,
           check_decode_equals_prefill, check_invariances, check_tempered_closed_form,
-          check_tempered_limits]
+          check_tempered_limits, check_tile_scores_moments, check_tile_select_brute,
+          check_tile_single_row, check_tile_dense_reduction]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda f: f.__name__)
@@ -499,6 +601,22 @@ def _mut_tempered_neg_beta(q, K, B, C, beta):
     return -OR.tempered_scores(-np.asarray(q, float), K, B, C, beta)
 
 
+def _mut_tile_own_block(j, nb):
+    return max(0, min(nb, j + 1))
+
+
+def _mut_tile_first_row(Qt, mu, sigma, beta):
+    return OR.tile_scores(np.asarray(Qt)[:1], mu, sigma, beta)
+
+
+def _mut_tile_max_row(Qt, mu, sigma, beta):
+    return np.max([OR.route_scores(q, mu, sigma, beta) for q in OR.as_f64(Qt)], axis=0)
+
+
+def _mut_tile_no_variance(Qt, mu, sigma, beta):
+    return OR.tile_scores(Qt, mu, sigma, 0.0)
+
+
 MUTANTS = {
     "sample_covariance": dict(block_stats=_mut_sample_cov),
     "beta_not_halved": dict(route_scores=_mut_full_beta),
@@ -517,6 +635,10 @@ MUTANTS = {
     "tempered_not_divided_by_beta": dict(tempered_scores=_mut_tempered_undivided),
     "tempered_block_max": dict(tempered_scores=_mut_tempered_max),
     "tempered_beta_sign": dict(tempered_scores=_mut_tempered_neg_beta),
+    "tile_routes_own_block": dict(tile_routable_blocks=_mut_tile_own_block),
+    "tile_first_row_only": dict(tile_scores=_mut_tile_first_row),
+    "tile_max_over_rows": dict(tile_scores=_mut_tile_max_row),
+    "tile_variance_dropped": dict(tile_scores=_mut_tile_no_variance),
 }
 
 
@@ -545,3 +667,28 @@ def test_planted_recall_report():
     r0 = O.planted_recall(orc, data["plants"], beta=0.0)
     print(f"planted recall beta=2: {r2:.3f}  beta=0: {r0:.3f}")
     assert r2 >= r0
+
+
+def test_oracle_compositions_match_pinned_copies():
+    """The oracle's own row and tile compositions are the step sequences the
+    pins exercise (same functions, same order), on random inputs."""
+    rng = np.random.default_rng(21)
+    n, d, B = 75, 6, 8
+    Q, K, V = _rand_head(rng, n, d, B)
+    mu, sigma = OR.block_stats(K, B)
+    p = O.Params(B, 3, 5, 2.0, 0.45)
+    ns = _impl()
+    for t in (0, 7, 8, 40, 74):
+        a = OR.prefill_row(Q[t], K, V, mu, sigma, p, t)
+        b = ns.prefill_row(Q[t], K, V, mu, sigma, p, t)
+        assert a["idx"].tolist() == b["idx"].tolist() and a["S"].tolist() == b["S"].tolist()
+        assert np.array_equal(a["O"], b["O"]) and a["lse"] == b["lse"]
+    for j in range((n + B - 1) // B):
+        a = OR.tile_select(Q, mu, sigma, p, j)
+        b = ns.tile_select(Q, mu, sigma, p, j)
+        assert a["idx"].tolist() == b["idx"].tolist()
+        assert np.array_equal(a["scores"], b["scores"])
+        for t in range(j * B, min(n, (j + 1) * B), 3):
+            ra = OR.tile_prefill_row(Q[t], K, V, a["idx"], p, t)
+            rb = ns.tile_prefill_row(Q[t], K, V, b["idx"], p, t)
+            assert ra["S"].tolist() == rb["S"].tolist() and np.array_equal(ra["O"], rb["O"])
