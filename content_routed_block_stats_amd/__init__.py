@@ -12,8 +12,10 @@ from .binding import (  # noqa: F401
     ssa_block_stats,
     ssa_decode_step,
     ssa_route_tempered,
+    ssa_route_tiles,
     ssa_route_topk,
     ssa_sparse_attn_fwd,
+    ssa_tile_attn_fwd,
     ssa_workspace_size,
     status_string,
 )

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("SSA_MI355X_LIB", os.path.join(HERE, "libssa_mi355x.so
 
 SSA_OK, SSA_ERR_INVALID_ARGUMENT, SSA_ERR_UNSUPPORTED, SSA_ERR_WORKSPACE_TOO_SMALL, SSA_ERR_HIP = range(5)
 SSA_F32, SSA_BF16 = 0, 1
-SSA_OP_ROUTE, SSA_OP_ATTN, SSA_OP_DECODE = 1, 2, 3
+SSA_OP_ROUTE, SSA_OP_ATTN, SSA_OP_DECODE, SSA_OP_ROUTE_TILES, SSA_OP_TILE_ATTN = 1, 2, 3, 4, 5
 
 _vp = ctypes.c_void_p
 
@@ -67,11 +67,13 @@ def lib() -> ctypes.CDLL:
     L.ssa_workspace_size.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     L.ssa_route_topk.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_route_tempered.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
+    L.ssa_route_tiles.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.ssa_tile_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_sparse_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_decode_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
     for name in ("ssa_block_stats", "ssa_workspace_size", "ssa_route_topk", "ssa_route_tempered",
-                 "ssa_sparse_attn_fwd", "ssa_decode_step"):
+                 "ssa_route_tiles", "ssa_tile_attn_fwd", "ssa_sparse_attn_fwd", "ssa_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
@@ -197,6 +199,58 @@ def ssa_route_tempered(Q: torch.Tensor, K: torch.Tensor, *, block_size: int, top
     _check(lib().ssa_route_tempered(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(idx), _ptr(kth),
                                     _stream()))
     return (idx, kth) if want_kth else idx
+
+
+def ssa_route_tiles(Q: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, *, block_size: int,
+                    top_k: int, beta: float = 2.0, want_kth: bool = False,
+                    idx: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Query-tile-shared routing: Q [b, Hq, n, d], block statistics -> idx
+    [b, Hq, ceil(n/B), k] int32 (, kth [.., 2]), one selection per tile of B positions."""
+    _dev_check(Q, mu, sigma)
+    b, hq, n, d = Q.shape
+    hkv = mu.shape[1]
+    if mu.shape[:2] != (b, hkv) or mu.shape[2] != n // block_size or mu.shape[3] != d:
+        raise ValueError("mu does not match Q and block_size")
+    if sigma.shape != (*mu.shape, d):
+        raise ValueError("sigma does not match mu")
+    p = make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=n,
+                    block_size=block_size, top_k=top_k, beta=beta, in_dtype=Q.dtype)
+    tiles = (n + block_size - 1) // block_size
+    if idx is None:
+        idx = torch.empty((b, hq, tiles, top_k), dtype=torch.int32, device=Q.device)
+    kth = torch.empty((b, hq, tiles, 2), dtype=torch.float32, device=Q.device) if want_kth else None
+    ws = _workspace(p, SSA_OP_ROUTE_TILES, Q.device, workspace)
+    _check(lib().ssa_route_tiles(ctypes.byref(p), _ptr(Q), _ptr(mu), _ptr(sigma), _ptr(idx),
+                                 _ptr(kth), _ptr(ws), ws.numel(), _stream()))
+    return (idx, kth) if want_kth else idx
+
+
+def ssa_tile_attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, *,
+                      block_size: int, window: int, scale: float | None = None,
+                      out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Exact softmax over each tile's selected blocks + the row's window -> (O, lse)."""
+    _dev_check(Q, K, V, idx)
+    b, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    if K.shape != (b, hkv, n, d) or V.shape != K.shape:
+        raise ValueError("K/V do not match Q")
+    tiles = (n + block_size - 1) // block_size
+    if idx.dtype != torch.int32 or idx.shape[:3] != (b, hq, tiles):
+        raise ValueError("idx must be int32 [b, Hq, ceil(n/B), k]")
+    top_k = idx.shape[3]
+    out_dtype = out_dtype or Q.dtype
+    p = make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=n,
+                    block_size=block_size, top_k=top_k, window=window, scale=scale,
+                    in_dtype=Q.dtype, out_dtype=out_dtype)
+    if out is None:
+        out = torch.empty((b, hq, n, d), dtype=out_dtype, device=Q.device)
+    if lse is None:
+        lse = torch.empty((b, hq, n), dtype=torch.float32, device=Q.device)
+    ws = _workspace(p, SSA_OP_TILE_ATTN, Q.device, workspace)
+    _check(lib().ssa_tile_attn_fwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx),
+                                   _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return out, lse
 
 
 def ssa_sparse_attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, *,

@@ -1,7 +1,9 @@
-// K/V chunk images shared by the attention and the exact-score routing
-// kernels: every 64-key chunk of a head laid out as MFMA operand fragments
-// (K as the A operand of S^T = K Q^T; V transposed, as the A operand of
-// O^T = V^T P^T), staged into LDS with direct global->LDS loads.
+// K/V chunk images shared by the attention kernels (per-query block
+// attention, tile attention) and the exact-score router: every 64-key chunk
+// of a head laid out as MFMA operand fragments (K as the A operand of
+// S^T = K Q^T; V transposed, as the A operand of O^T = V^T P^T), staged into
+// LDS with direct global->LDS loads; and the online-softmax step over one
+// staged chunk that all attention kernels share.
 //
 // K part: fragment (mt, s), lane (m, h), element e = K[key0 + 32mt + m][16s + 8h + e];
 // a query row's B-operand fragment s (load_row_frag) holds q[16s + 8h + e]
@@ -226,6 +228,138 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count;
        i += int64_t(gridDim.x) * blockDim.x)
     p[i] = v;
+}
+
+// ------------------------------------------------ attention over a chunk --
+
+constexpr float kLazyLog2 = 8.f;   // probabilities may reach 2^kLazyLog2 before a rescale
+
+// Running softmax state of one query row, split over the two lane halves.
+template <int D>
+struct RowState {
+  floatx16 o[D / 32];    // unnormalised output, lane half's columns
+  float m2;              // running max of scaled logits (base 2), full row
+  float l;               // this lane half's share of the running sum
+};
+
+template <int D>
+__device__ __forceinline__ void row_state_init(RowState<D>& st) {
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st.o[i][j] = 0.f;
+  st.m2 = -__builtin_inff();
+  st.l = 0.f;
+}
+
+// One 64-key chunk for the NT 32-row tiles of this wave; every fragment read
+// from LDS feeds NT MFMAs.  mask(nt, mt, a, b) says whether key
+// 32mt + 8a + 4h + b of the chunk counts for this lane's row of tile nt.
+// Probabilities are exp2(s * scale2 - m) with the running row max m in the
+// same base-2 units; for bfloat16 inputs they enter P V as float16.
+template <bool F32, int D, int NT, typename Mask>
+__device__ __forceinline__ void attend_chunk(const uint8_t* lds,
+                                             const typename AT<F32, D>::Frag (&bq)[NT][D / 16],
+                                             float scale2, int lane, RowState<D> (&st)[NT],
+                                             Mask mask) {
+  using A = AT<F32, D>;
+  using Frag = typename A::Frag;
+  using VFrag = typename A::VFrag;
+  floatx16 sacc[NT][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[nt][mt][j] = 0.f;
+  // S^T = K Q^T: the two 32-key tiles are independent accumulator chains,
+  // interleaved; K fragments are read from LDS two steps ahead of use.
+  auto kfrag = [&](int mt, int s) {
+    return *reinterpret_cast<const Frag*>(lds + (mt * A::NS + s) * A::FRAG + lane * 8 * A::ES);
+  };
+  Frag ka[3][2];
+  ka[0][0] = kfrag(0, 0);
+  ka[0][1] = kfrag(1, 0);
+  ka[1][0] = kfrag(0, 1);
+  ka[1][1] = kfrag(1, 1);
+#pragma unroll
+  for (int s = 0; s < A::NS; ++s) {
+    if (s + 2 < A::NS) {
+      ka[(s + 2) % 3][0] = kfrag(0, s + 2);
+      ka[(s + 2) % 3][1] = kfrag(1, s + 2);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[nt][mt] = mma16(ka[s % 3][mt], bq[nt][s], sacc[nt][mt]);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float v = sacc[nt][mt][4 * a + b];
+          if (!mask(nt, mt, a, b)) v = -__builtin_inff();
+          sacc[nt][mt][4 * a + b] = v;
+          mloc = fmaxf(mloc, v);
+        }
+    mloc = fmaxf(mloc, wave_shfl_xor(mloc, 32)) * scale2;
+    // Lazy rescaling: the reference m2 moves (and o, l are rescaled) only
+    // when some row of the wave sees a logit more than kLazyLog2 above it, so
+    // probabilities stay below 2^kLazyLog2 and most chunks skip the rescale.
+    if (__builtin_amdgcn_ballot_w64(mloc > st[nt].m2 + kLazyLog2) != 0) {
+      const float mnew = fmaxf(st[nt].m2, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(st[nt].m2 - (mnew == -__builtin_inff() ? 0.f : mnew));
+      st[nt].m2 = mnew;
+      st[nt].l *= alpha;
+#pragma unroll
+      for (int i = 0; i < A::MTD; ++i) st[nt].o[i] *= alpha;
+    }
+    const float mref = st[nt].m2 == -__builtin_inff() ? 0.f : st[nt].m2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[nt][mt][j], scale2, -mref));
+        sacc[nt][mt][j] = p;
+        lsum += p;
+      }
+    st[nt].l += lsum;
+  }
+  // P as the B operand of O^T += V^T P^T: chunk s' covers keys 16s'..16s'+15.
+  // The MTD output tiles are independent chains; V fragments are read one
+  // step ahead of use.
+  const uint8_t* vl = lds + A::KBYTES;
+  auto vfrag = [&](int mt, int sp) {
+    return *reinterpret_cast<const VFrag*>(vl + (mt * 4 + sp) * A::FRAG + lane * 8 * A::ES);
+  };
+  VFrag va[2][A::MTD];
+#pragma unroll
+  for (int mt = 0; mt < A::MTD; ++mt) va[0][mt] = vfrag(mt, 0);
+#pragma unroll
+  for (int sp = 0; sp < 4; ++sp) {
+    if (sp + 1 < 4) {
+#pragma unroll
+      for (int mt = 0; mt < A::MTD; ++mt) va[(sp + 1) & 1][mt] = vfrag(mt, sp + 1);
+    }
+    VFrag pf[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = sacc[nt][sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)];
+        if constexpr (F32) pf[nt][e] = pv; else pf[nt][e] = static_cast<_Float16>(pv);
+      }
+#pragma unroll
+    for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) st[nt].o[mt] = mma16(va[sp & 1][mt], pf[nt], st[nt].o[mt]);
+  }
 }
 
 

@@ -126,6 +126,54 @@ ssa_status ssa_route_tempered(const ssa_params* p, const void* Q, const void* K,
                   "ssa_route_tempered");
 }
 
+ssa_status ssa_route_tiles(const ssa_params* p, const void* Q, const float* mu, const float* sigma,
+                           int32_t* idx, float* kth, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  ssa::Shape s;
+  ssa_status st = check_params(p, &s);
+  if (st != SSA_OK) return st;
+  SSA_NONNULL(Q);
+  if (s.nb > 0) {
+    SSA_NONNULL(mu);
+    SSA_NONNULL(sigma);
+  }
+  if (s.k > 0) SSA_NONNULL(idx);
+  const int64_t tiles = ssa::tile_count(s);
+  if (int64_t(s.b) * s.hq > 65535 || int64_t(s.b) * s.hkv > 65535 ||
+      int64_t(s.b) * s.hq * tiles >= (int64_t(1) << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "too many (sequence, head) pairs or tiles for one launch");
+  st = check_ws(ssa::route_tiles_workspace_bytes(s), workspace, workspace_bytes);
+  if (st != SSA_OK) return st;
+  if (s.k == 0 && kth == nullptr) return ok();
+  return from_hip(ssa::launch_route_tiles(s, Q, mu, sigma, idx, kth, workspace, (hipStream_t)stream),
+                  "ssa_route_tiles");
+}
+
+ssa_status ssa_tile_attn_fwd(const ssa_params* p, const void* Q, const void* K, const void* V,
+                             const int32_t* idx, void* O, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  ssa::Shape s;
+  ssa_status st = check_params(p, &s);
+  if (st != SSA_OK) return st;
+  SSA_NONNULL(Q);
+  SSA_NONNULL(K);
+  SSA_NONNULL(V);
+  SSA_NONNULL(O);
+  SSA_NONNULL(lse);
+  if (s.k > 0) SSA_NONNULL(idx);
+  const int64_t list = int64_t(s.k) * (s.B / 64) + (int64_t(s.W) + 254) / 64 + 2;
+  if (list > ssa::tile_attn_max_list())
+    return fail(SSA_ERR_UNSUPPORTED, "top_k * block_size / 64 + (window + 254) / 64 + 2 = %lld "
+                "chunks exceeds %d", (long long)list, ssa::tile_attn_max_list());
+  const int64_t subs = (s.B + 255) / 256;
+  if (int64_t(s.b) * s.hq * ssa::tile_count(s) * subs >= (int64_t(1) << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "too many tiles for one launch");
+  st = check_ws(ssa::tile_attn_workspace_bytes(s), workspace, workspace_bytes);
+  if (st != SSA_OK) return st;
+  return from_hip(ssa::launch_tile_attn(s, Q, K, V, idx, O, lse, workspace, (hipStream_t)stream),
+                  "ssa_tile_attn_fwd");
+}
+
 ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes) {
   ssa::Shape s;
   ssa_status st = check_params(p, &s);
@@ -135,6 +183,8 @@ ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes) {
     case SSA_OP_ROUTE: *bytes = ssa::route_workspace_bytes(s); break;
     case SSA_OP_ATTN: *bytes = ssa::attn_workspace_bytes(s); break;
     case SSA_OP_DECODE: *bytes = ssa::decode_workspace_bytes(s); break;
+    case SSA_OP_ROUTE_TILES: *bytes = ssa::route_tiles_workspace_bytes(s); break;
+    case SSA_OP_TILE_ATTN: *bytes = ssa::tile_attn_workspace_bytes(s); break;
     default: return fail(SSA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
   return ok();

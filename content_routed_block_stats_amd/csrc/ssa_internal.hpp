@@ -38,6 +38,20 @@ int64_t tempered_route_tiles(const Shape& s);
 hipError_t launch_route_tempered(const Shape& s, const void* Q, const void* K, int32_t* idx,
                                  float* kth, hipStream_t st);
 
+// query-tile-shared routing (prefill): tiles of B positions per (sequence,
+// q-head); idx [b, hq, tile_count, k]
+int64_t tile_count(const Shape& s);
+size_t route_tiles_workspace_bytes(const Shape& s);
+hipError_t launch_route_tiles(const Shape& s, const void* Q, const float* mu, const float* sigma,
+                              int32_t* idx, float* kth, void* ws, hipStream_t st);
+
+// attention over tile selections (prefill); the chunk list of one workgroup
+// (k B/64 selected chunks + the window's) must fit tile_attn_max_list()
+size_t tile_attn_workspace_bytes(const Shape& s);
+int tile_attn_max_list();
+hipError_t launch_tile_attn(const Shape& s, const void* Q, const void* K, const void* V,
+                            const int32_t* tidx, void* O, float* lse, void* ws, hipStream_t st);
+
 // sparse attention (prefill)
 size_t attn_workspace_bytes(const Shape& s);
 // entry / partial slots of the block pass (tasks padded to whole task rows);

@@ -52,7 +52,9 @@ typedef enum ssa_dtype { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
 typedef enum ssa_op {
   SSA_OP_ROUTE = 1,   /* workspace of ssa_route_topk */
   SSA_OP_ATTN = 2,    /* workspace of ssa_sparse_attn_fwd */
-  SSA_OP_DECODE = 3   /* workspace of ssa_decode_step */
+  SSA_OP_DECODE = 3,  /* workspace of ssa_decode_step */
+  SSA_OP_ROUTE_TILES = 4,  /* workspace of ssa_route_tiles */
+  SSA_OP_TILE_ATTN = 5     /* workspace of ssa_tile_attn_fwd */
 } ssa_op;
 
 /* Shapes and method parameters.  Limits checked by every call:
@@ -138,6 +140,47 @@ ssa_status ssa_route_topk(const ssa_params* p, const void* Q, const float* mu,
  * the block's maximum factored out. */
 ssa_status ssa_route_tempered(const ssa_params* p, const void* Q, const void* K, int32_t* idx,
                               float* kth, void* stream);
+
+/* Query-tile-shared routing (write-up: the fused kernel routes per query
+ * block -- its compute-floor notes name an (n/b)^2 block-score GEMM and an
+ * argsort block-mask build).  Tile j of each (sequence, q-head) holds the
+ * positions [jB, (j+1)B) (the last tile may be partial: ceil(n/B) tiles).
+ * It selects, for all its queries, the min(k, #routable) blocks among those
+ * complete before it (c < j) with the highest summed routing score
+ *   R_c = sum_{t in tile} r_c(q_t) = s.mu_c + (beta/2) <Sigma_c, M>,
+ *   s = sum_t q_t,  M = sum_t q_t q_t^T         (raw q, KV head of the head),
+ * ties to the lower c.
+ *   Q          [b, Hq, n, d]                in_dtype
+ *   mu, sigma  as written by ssa_block_stats
+ *   idx        [b, Hq, ceil(n/B), k]       int32, written: ascending, -1 padded
+ *   kth        [b, Hq, ceil(n/B), 2]       float32, written if not NULL: the
+ *                                          k-th and (k+1)-th largest R (-inf
+ *                                          where absent)
+ *   workspace  >= ssa_workspace_size(p, SSA_OP_ROUTE_TILES) bytes
+ * Arithmetic: M and s on MFMA (bf16 products exact, float32 accumulation),
+ * R on float32 MFMA.  Limits (SSA_ERR_UNSUPPORTED otherwise): b * Hq and
+ * b * Hkv at most 65535, b * Hq * ceil(n/B) below 2^31. */
+ssa_status ssa_route_tiles(const ssa_params* p, const void* Q, const float* mu, const float* sigma,
+                           int32_t* idx, float* kth, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Attention over tile selections (write-up, introduction steps ii-iii, with
+ * the selection of ssa_route_tiles).  For every query row (b, h, t) of tile
+ * j = t / B:
+ *   S(t) = union of the keys of the blocks in idx(b, h, j) (entries < 0 are
+ *          ignored) and the window [max(0, t-W+1), t], each key once;
+ *   O = sum_j softmax(scale * q.k_j) v_j over S(t), LSE = ln sum exp(...).
+ *   Q, K, V, O, lse  as for ssa_sparse_attn_fwd
+ *   idx        [b, Hq, ceil(n/B), k] int32 as written by ssa_route_tiles:
+ *              every entry -1 or a block < j, distinct (other contents are
+ *              undefined behaviour)
+ *   workspace  >= ssa_workspace_size(p, SSA_OP_TILE_ATTN) bytes
+ * Limits (SSA_ERR_UNSUPPORTED otherwise): k * B/64 + (W + 254)/64 + 2 at most
+ * 1024 chunks per workgroup; b * Hq * ceil(n/B) * ceil(B/256) below 2^31.
+ * Arithmetic: as ssa_sparse_attn_fwd. */
+ssa_status ssa_tile_attn_fwd(const ssa_params* p, const void* Q, const void* K, const void* V,
+                             const int32_t* idx, void* O, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Sparse attention forward (write-up, introduction steps ii-iii).  For every
  * query row (b, h, t):
