@@ -10,8 +10,11 @@ ssa_sparse_attn_fwd.  The default workload is the n = 131072 GQA prefill
 (32 q-heads / 8 KV heads, d = 128, bf16, B = 256, k = 16, W = 256, beta = 2).
 Prints ONE JSON line: query-tokens/s, per-stage times from HIP events on the
 launch stream, the routing kernel against the bf16 MFMA roofline, the gather
-against the HBM roofline, the exact tempered router (ssa_route_tempered, same
-workload and beta, outside the step) against the MFMA roofline, a decode step
+against the HBM roofline, the query-tile-shared variant (ssa_route_tiles +
+ssa_tile_attn_fwd on the same workload: its step time, planted recall and the
+tile attention against the MFMA roofline), the exact tempered router
+(ssa_route_tempered, same workload and beta, outside the step) against the
+MFMA roofline, a decode step
 on the 32 x 256K-token cache, and the CPU oracle timed on a bounded sample of
 the same workload.  --recall-sweep instead prints the planted-target recall of
 the centroid, second-cumulant and tempered scores across beta.
@@ -184,6 +187,30 @@ def tempered_flops(wl) -> float:
     nb = n // B
     pairs_per_head = B * nb * (nb - 1) // 2 + (n - nb * B + 1) * nb
     return float(wl.batch * wl.n_q_heads * pairs_per_head) * B * 2 * d
+
+
+def tile_attn_flops(wl, idx_t) -> float:
+    """Algorithmic flops of ssa_tile_attn_fwd on its actual selections: 4d per
+    (row, key of S(t)), S(t) = the tile's selected blocks + the row's window,
+    each key once (window keys inside a selected block counted once)."""
+    import torch
+
+    n, B, W, d = wl.seq_len, wl.block, wl.window, wl.head_dim
+    dev = idx_t.device
+    t = torch.arange(n, device=dev)
+    win = torch.clamp(t + 1, max=W).to(torch.float64)            # window keys per row
+    total = 0.0
+    for b in range(idx_t.shape[0]):
+        for h in range(idx_t.shape[1]):
+            sel = idx_t[b, h].to(torch.int64)                      # [tiles, k]
+            rows_sel = sel[t // B]                                 # [n, k]
+            valid = rows_sel >= 0
+            lo = torch.maximum(rows_sel * B, (t - W + 1)[:, None])
+            hi = torch.minimum(rows_sel * B + B - 1, t[:, None])
+            overlap = torch.clamp(hi - lo + 1, min=0) * valid
+            keys = valid.sum(-1) * B + win - overlap.sum(-1)
+            total += float(keys.sum())
+    return 4.0 * d * total
 
 
 def recall_sweep(wl, seed: int, betas: list[float]) -> dict:
@@ -364,6 +391,59 @@ def main() -> int:
                             "traffic": counted_traffic("sparse_attn_fwd", attn_digest),
                             "algorithmic_bytes_per_launch": gb},
     }
+    # the query-tile-shared variant: one selection per tile of B positions
+    tiles = (n + wl.block - 1) // wl.block
+    idx_t = torch.empty((b, hq, tiles, wl.top_k), dtype=torch.int32, device=dev)
+    ws_rt = torch.empty(ssa.ssa_workspace_size(p, 4), dtype=torch.uint8, device=dev)
+    ws_ta = torch.empty(ssa.ssa_workspace_size(p, 5), dtype=torch.uint8, device=dev)
+
+    def tile_step(ev=None):
+        if ev:
+            ev[0].record()
+        ssa.ssa_block_stats(K, wl.block, mu=mu, sigma=sigma)
+        if ev:
+            ev[1].record()
+        ssa.ssa_route_tiles(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta,
+                            idx=idx_t, workspace=ws_rt)
+        if ev:
+            ev[2].record()
+        ssa.ssa_tile_attn_fwd(Q, K, V, idx_t, block_size=wl.block, window=wl.window,
+                              scale=wl.scale, out=O, lse=lse, workspace=ws_ta)
+        if ev:
+            ev[3].record()
+
+    tile_step()
+    torch.cuda.synchronize()
+    treps = max(3, args.steps // 2)
+    tevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(treps)]
+    for i in range(treps):
+        tile_step(tevs[i])
+    torch.cuda.synchronize()
+    tst = [sum(e[j].elapsed_time(e[j + 1]) for e in tevs) / treps for j in range(3)]
+    t_tile = sum(tst)
+    ta_fl = tile_attn_flops(wl, idx_t)
+    ta_tf = ta_fl / (tst[2] * 1e-3) / 1e12
+    plants = data["plants"]
+    pb = torch.tensor([q["b"] for q in plants], device=dev)
+    ph = torch.tensor([q["h"] for q in plants], device=dev)
+    pt = torch.tensor([q["t"] for q in plants], device=dev)
+    pc = torch.tensor([q["block"] for q in plants], device=dev, dtype=torch.int32)
+    rec_tile = float((idx_t[pb, ph, pt // wl.block] == pc[:, None]).any(-1).float().mean())
+    rec_row = float((idx[pb, ph, pt] == pc[:, None]).any(-1).float().mean())
+    res["tile_routed"] = {
+        "what": "one selection per query tile of B positions (summed routing score), same workload",
+        "ms_per_step": round(t_tile, 4), "value": round(tokens / (t_tile * 1e-3), 1),
+        "unit": "query-tokens/s", "speedup_vs_per_query": round(ms / t_tile, 3),
+        "stages_ms": {"block_stats": round(tst[0], 4), "route_tiles": round(tst[1], 4),
+                      "tile_attn_fwd": round(tst[2], 4)},
+        "planted_recall": round(rec_tile, 4), "planted_recall_per_query": round(rec_row, 4),
+        "roofline": {"kernel": "tile_attn", "bound": "mfma", "achieved": round(ta_tf, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ta_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops_per_launch": ta_fl},
+        "steps": treps}
+    del ws_rt, ws_ta, idx_t
+
     # the exact tempered score (same workload and beta), outside the step
     ssa.ssa_route_tempered(Q, K, block_size=wl.block, top_k=wl.top_k, beta=wl.beta, idx=idx)
     te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

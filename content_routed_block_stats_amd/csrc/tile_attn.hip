@@ -30,17 +30,24 @@ __global__ __launch_bounds__(kTileThreads) void tile_attn_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
     const uint32_t* __restrict__ vmax, const int32_t* __restrict__ tidx, OutT* __restrict__ O,
     float* __restrict__ lse, int64_t n, int g, int hq, int hkv, int B, int k, int W, float scale2,
-    int64_t n_tiles, int subs, int64_t n_chunks) {
+    int64_t n_tiles, int subs, int64_t n_chunks, int64_t n_work) {
   using A = AT<F32, D>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * A::CHUNK];
   __shared__ int32_t list[kMaxList];
   __shared__ int32_t nlist[2];   // selected-chunk count, total count
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
-  const int64_t wg = blockIdx.x;
-  const int sub = int(wg % subs);
-  const int64_t j = (wg / subs) % n_tiles, bh = wg / (int64_t(subs) * n_tiles);
-  const int64_t b = bh / hq, hh = bh % hq, kv = hh / g, bkv = b * hkv + kv;
+  // Work items run sub-tile fastest, then the group's q-heads, then tiles,
+  // then (sequence, KV head); consecutive items go to one XCD (workgroup i
+  // runs on XCD i % 8), so the heads of a tile share their window chunks and
+  // neighbouring tiles their blocks in that XCD's L2.
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t wi = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (wi >= n_work) return;
+  const int sub = int(wi % subs);
+  const int64_t jg = (wi / subs) % g, j = (wi / (int64_t(subs) * g)) % n_tiles;
+  const int64_t bkv = wi / (int64_t(subs) * g * n_tiles), b = bkv / hkv, kv = bkv % hkv;
+  const int64_t bh = b * hq + kv * g + jg;
   const int64_t r0 = j * B + int64_t(sub) * kTileRows;
   const int64_t r_end = min(min(n, (j + 1) * B), r0 + kTileRows) - 1;   // last row (inclusive)
   if (r0 > r_end) return;
@@ -174,11 +181,12 @@ hipError_t launch_tile_attn_t(const Shape& s, const void* Qv, const void* Kv, co
                      static_cast<const In*>(Vv), w.vmax, w.img, s.n, w.n_chunks);
   const int64_t n_tiles = tile_count(s);
   const int subs = (s.B + kTileRows - 1) / kTileRows;
-  const int64_t grid = int64_t(s.b) * s.hq * n_tiles * subs;
+  const int64_t n_work = int64_t(s.b) * s.hq * n_tiles * subs;
+  const int64_t grid = (n_work + 7) / 8 * 8;   // a multiple of the 8 XCDs
   hipLaunchKernelGGL((tile_attn_kernel<F32, D, OutT>), dim3(unsigned(grid)), dim3(kTileThreads), 0,
                      st, static_cast<const In*>(Qv), w.img, w.vmax, tidx, static_cast<OutT*>(Ov),
                      lse, s.n, s.g, s.hq, s.hkv, s.B, s.k, s.W, s.scale * kLog2e, n_tiles, subs,
-                     w.n_chunks);
+                     w.n_chunks, n_work);
   return hipGetLastError();
 }
 

@@ -38,14 +38,19 @@ constexpr int kScoreRows = 128;      // GEMM rows (tile, q-head pairs) per workg
 constexpr int kScoreCols = 64;       // GEMM columns (blocks) per workgroup
 constexpr int kScoreStages = 4;      // register stages of the GEMM's operand prefetch
 
-// Packed moment layout for head dimension D: the NUP upper 32x32 tiles of the
-// d x d matrix in (mt, nt >= mt) order, 1024 floats each (row-major inside the
-// tile), then D floats of the first moment.
+// Packed moment coordinates for head dimension D: the NUP upper 32x32 tiles
+// of the d x d matrix in (mt, nt >= mt) order, 1024 coordinates each
+// (row-major inside the tile), then the D coordinates of the first moment --
+// P in all, contracted 16 at a time (STEPS steps).  Stored step-major per KV
+// head, [step][row][16] with row = j g + jg, so that the GEMM's operand loads
+// for 32 consecutive rows are one contiguous 2 KB run.
 template <int D>
 struct Moments {
   static constexpr int MT = D / 32;
   static constexpr int NUP = MT * (MT + 1) / 2;
   static constexpr int P = NUP * 1024 + D;      // floats per tile
+  static constexpr int SIG_STEPS = NUP * 64;    // 16-coordinate steps of the M part
+  static constexpr int STEPS = P / 16;          // ... and of M then s
 };
 
 __host__ __device__ constexpr void up_tile(int u, int mt_count, int& mt, int& nt) {
@@ -85,7 +90,10 @@ __global__ __launch_bounds__(256) void tile_moments_kernel(const typename AT<F32
   const int64_t b = bh / hq, hh = bh % hq, kv = hh / g, jg = hh % g;
   const int64_t t0 = j * B, t1 = min(n, t0 + B);
   const In* Qh = Q + bh * n * D;
-  float* out = Am + (((b * hkv + kv) * n_tiles + j) * g + jg) * int64_t(Mo::P);
+  const int64_t rows_total = n_tiles * g;
+  // coordinate p of this tile's row -> [step p / 16][row][p % 16]
+  float* out = Am + ((b * hkv + kv) * Mo::STEPS * rows_total + j * g + jg) * 16;
+  auto put = [&](int p, float v) { out[(int64_t(p / 16) * rows_total) * 16 + p % 16] = v; };
 
   // byte offset of (dimension c, row r) in the transposed chunk
   auto qt_off = [](int c, int r) { return (c * kMomRows + 8 * ((r / 8) ^ (c % 8)) + r % 8) * ES; };
@@ -160,12 +168,12 @@ __global__ __launch_bounds__(256) void tile_moments_kernel(const typename AT<F32
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 8 * (i / 4) + 4 * h + i % 4;
-        out[job * 1024 + row * 32 + ln] = w * acc[q][i];
+        put(job * 1024 + row * 32 + ln, w * acc[q][i]);
       }
     } else if (ln == 0) {
       const int x = job - Mo::NUP;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) out[Mo::NUP * 1024 + 32 * x + 8 * (i / 4) + 4 * h + i % 4] = acc[q][i];
+      for (int i = 0; i < 16; ++i) put(Mo::NUP * 1024 + 32 * x + 8 * (i / 4) + 4 * h + i % 4, acc[q][i]);
     }
   }
 }
@@ -185,40 +193,46 @@ __global__ __launch_bounds__(256) void tile_score_kernel(const float* __restrict
                                                          const float* __restrict__ mu,
                                                          float* __restrict__ R, int g, int hq,
                                                          int hkv, int64_t nb, int64_t n_tiles,
-                                                         float half_beta) {
+                                                         float half_beta, int64_t n_ct,
+                                                         int64_t n_rt, int64_t n_work) {
   using Mo = Moments<D>;
-  constexpr int P = Mo::P;
-  constexpr int SIG_STEPS = Mo::NUP * 64;        // 32 rows x 2 halves per packed tile
+  constexpr int SIG_STEPS = Mo::SIG_STEPS;
   constexpr int MU_STEPS = D / 16;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int wr = wave / 2, wc = wave % 2;
-  const int64_t bkv = blockIdx.z, b = bkv / hkv, kv = bkv % hkv;
+  // Work items run column tile fastest, then row tile, then KV head, and
+  // consecutive items go to one XCD (workgroup i runs on XCD i % 8): the
+  // column tiles of a row tile read the same moment rows at about the same
+  // time, from that XCD's L2.
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t wi = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (wi >= n_work) return;
+  const int64_t ct = wi % n_ct, rt = (wi / n_ct) % n_rt, bkv = wi / (n_ct * n_rt);
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
   const int64_t rows_total = n_tiles * g;
-  const int64_t rt0 = int64_t(blockIdx.y) * kScoreRows, c0 = int64_t(blockIdx.x) * kScoreCols;
+  const int64_t rt0 = rt * kScoreRows, c0 = ct * kScoreCols;
   const int64_t j_hi = min(n_tiles - 1, (rt0 + kScoreRows - 1) / g);
   if (c0 >= min(nb, j_hi)) return;               // no block before any tile of this row tile
 
   const int64_t r_base = rt0 + 64 * wr;
   const int64_t c = c0 + 32 * wc + ln;
   const bool c_ok = c < nb;
+  // operand rows past the end read row 0 / block 0 (their results are never
+  // stored), so every load is unconditional and stays in flight
   const float* arow[2];
-  bool r_ok[2];
 #pragma unroll
   for (int rs = 0; rs < 2; ++rs) {
     const int64_t r = r_base + 32 * rs + ln;
-    r_ok[rs] = r < rows_total;
-    arow[rs] = Am + (bkv * rows_total + (r_ok[rs] ? r : 0)) * int64_t(P);
+    arow[rs] = Am + (bkv * Mo::STEPS * rows_total + (r < rows_total ? r : 0)) * 16 + 8 * h;
   }
-  const float* sig_c = sigma + (bkv * nb + (c_ok ? c : 0)) * int64_t(D) * D;
-  const float* mu_c = mu + (bkv * nb + (c_ok ? c : 0)) * int64_t(D);
+  const int64_t step_stride = rows_total * 16;
+  const float* sig_c = sigma + (bkv * nb + (c_ok ? c : 0)) * int64_t(D) * D + 8 * h;
+  const float* mu_c = mu + (bkv * nb + (c_ok ? c : 0)) * int64_t(D) + 8 * h;
 
-  auto ld8 = [](const float* p, bool ok) {
+  auto ld8 = [](const float* p) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(p);
+    const floatx4 b2 = *reinterpret_cast<const floatx4*>(p + 4);
     floatx8 v;
-    floatx4 a = {0.f, 0.f, 0.f, 0.f}, b2 = a;
-    if (ok) {
-      a = *reinterpret_cast<const floatx4*>(p);
-      b2 = *reinterpret_cast<const floatx4*>(p + 4);
-    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[e] = a[e];
@@ -226,13 +240,18 @@ __global__ __launch_bounds__(256) void tile_score_kernel(const float* __restrict
     }
     return v;
   };
-  // contraction step st of the Sigma part: packed tile u, row i, half j0
-  auto sig_coord = [&](int st, int& a_off, int& s_off) {
-    const int u = st / 64, i = (st / 2) % 32, j0 = 16 * (st % 2);
-    int mt, nt;
-    up_tile(u, Mo::MT, mt, nt);
-    a_off = u * 1024 + i * 32 + j0 + 8 * h;
-    s_off = (32 * mt + i) * D + 32 * nt + j0 + 8 * h;
+  // Contraction step st of the Sigma part covers packed tile u = st / 64,
+  // its row i = (st / 2) % 32 and half j0 = 16 (st % 2): 16 st + 8h on the
+  // packed-moment side; on the Sigma side row 32 mt + i, columns 32 nt + j0
+  // + 8h, with (mt, nt) the u-th upper tile (scalar arithmetic: u >= T_m,
+  // T_m = m MT - m (m - 1) / 2, for each m counts one more mt).
+  auto sig_off = [](int st) {
+    const int u = st >> 6, i = (st >> 1) & 31, j0 = (st & 1) << 4;
+    int mt = 0;
+#pragma unroll
+    for (int m = 1; m < Mo::MT; ++m) mt += u >= m * Mo::MT - m * (m - 1) / 2 ? 1 : 0;
+    const int nt = u - (mt * Mo::MT - mt * (mt - 1) / 2) + mt;
+    return (32 * mt + i) * D + 32 * nt + j0;
   };
 
   floatx16 acc[2];
@@ -243,11 +262,9 @@ __global__ __launch_bounds__(256) void tile_score_kernel(const float* __restrict
 
   floatx8 fa[kScoreStages][2], fb[kScoreStages];
   auto load_step = [&](int st, int slot) {
-    int ao, so;
-    sig_coord(st, ao, so);
 #pragma unroll
-    for (int rs = 0; rs < 2; ++rs) fa[slot][rs] = ld8(arow[rs] + ao, r_ok[rs]);
-    fb[slot] = ld8(sig_c + so, c_ok);
+    for (int rs = 0; rs < 2; ++rs) fa[slot][rs] = ld8(arow[rs] + st * step_stride);
+    fb[slot] = ld8(sig_c + sig_off(st));
   };
 #pragma unroll
   for (int q = 0; q < kScoreStages; ++q) load_step(q, q);
@@ -256,7 +273,9 @@ __global__ __launch_bounds__(256) void tile_score_kernel(const float* __restrict
     for (int q = 0; q < kScoreStages; ++q) {
 #pragma unroll
       for (int rs = 0; rs < 2; ++rs) acc[rs] = mma16(fa[q][rs], fb[q], acc[rs]);
-      if (st0 + q + kScoreStages < SIG_STEPS) load_step(st0 + q + kScoreStages, q);
+      // the last stages re-read step 0 instead of running past the end
+      const int nx = st0 + q + kScoreStages;
+      load_step(nx < SIG_STEPS ? nx : 0, q);
     }
   }
   // (beta/2) <Sigma_c, M_j>, then + s_j . mu_c
@@ -264,18 +283,12 @@ __global__ __launch_bounds__(256) void tile_score_kernel(const float* __restrict
   for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[rs][i] *= half_beta;
-  {
-    floatx8 ma[MU_STEPS][2], mb[MU_STEPS];
 #pragma unroll
-    for (int s = 0; s < MU_STEPS; ++s) {
+  for (int s2 = 0; s2 < MU_STEPS; ++s2) {
+    const floatx8 mb = ld8(mu_c + 16 * s2);
 #pragma unroll
-      for (int rs = 0; rs < 2; ++rs) ma[s][rs] = ld8(arow[rs] + Mo::NUP * 1024 + 16 * s + 8 * h, r_ok[rs]);
-      mb[s] = ld8(mu_c + 16 * s + 8 * h, c_ok);
-    }
-#pragma unroll
-    for (int s = 0; s < MU_STEPS; ++s)
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs) acc[rs] = mma16(ma[s][rs], mb[s], acc[rs]);
+    for (int rs = 0; rs < 2; ++rs)
+      acc[rs] = mma16(ld8(arow[rs] + (SIG_STEPS + s2) * step_stride), mb, acc[rs]);
   }
 
   // acc lane (ln, h): rows 8a + 4h + b of the 32-row group, block c
@@ -423,15 +436,17 @@ hipError_t launch_route_tiles(const Shape& s, const void* Q, const float* mu, co
                   : (s.d == 64 ? launch_moments<true, 64>(s, Q, Am, n_tiles, st)
                                : launch_moments<true, 128>(s, Q, Am, n_tiles, st));
     if (e != hipSuccess) return e;
-    const dim3 grid(unsigned((s.nb + kScoreCols - 1) / kScoreCols),
-                    unsigned((n_tiles * s.g + kScoreRows - 1) / kScoreRows), unsigned(s.b * s.hkv));
+    const int64_t n_ct = (s.nb + kScoreCols - 1) / kScoreCols;
+    const int64_t n_rt = (n_tiles * s.g + kScoreRows - 1) / kScoreRows;
+    const int64_t n_work = n_ct * n_rt * s.b * s.hkv;
+    const dim3 grid(unsigned((n_work + 7) / 8 * 8));   // a multiple of the 8 XCDs
     const float hb = 0.5f * s.beta;
     if (s.d == 64)
       hipLaunchKernelGGL((tile_score_kernel<64>), grid, dim3(256), 0, st, Am, sigma, mu, R, s.g,
-                         s.hq, s.hkv, s.nb, n_tiles, hb);
+                         s.hq, s.hkv, s.nb, n_tiles, hb, n_ct, n_rt, n_work);
     else
       hipLaunchKernelGGL((tile_score_kernel<128>), grid, dim3(256), 0, st, Am, sigma, mu, R, s.g,
-                         s.hq, s.hkv, s.nb, n_tiles, hb);
+                         s.hq, s.hkv, s.nb, n_tiles, hb, n_ct, n_rt, n_work);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
