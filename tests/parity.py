@@ -85,3 +85,17 @@ def check_idx_properties(idx: np.ndarray, n: int, B: int, k: int) -> None:
     assert np.all(np.diff(big, axis=-1)[..., :] >= 0) and np.all(
         (np.diff(big, axis=-1) > 0) | ~valid[..., 1:]), "not ascending / not distinct"
     assert np.all(np.where(valid, idx < routable[None, :, None], True)), "non-routable block selected"
+
+
+def check_tile_properties(idx: np.ndarray, n: int, B: int, k: int) -> None:
+    """Every tile: ascending distinct blocks before the tile, min(k, min(j, nb))
+    of them, -1 padding at the end.  idx: [rows, tiles, k]."""
+    nb = n // B
+    tiles = idx.shape[-2]
+    want = np.minimum(k, np.minimum(np.arange(tiles), nb))
+    valid = idx >= 0
+    assert np.array_equal(valid.sum(-1), np.broadcast_to(want, valid.shape[:-1]))
+    assert np.all(valid == (np.arange(k) < want[:, None]))
+    big = np.where(valid, idx, np.iinfo(np.int32).max)
+    assert np.all((np.diff(big, axis=-1) > 0) | ~valid[..., 1:])
+    assert np.all(np.where(valid, idx < np.arange(tiles)[:, None], True))

@@ -18,7 +18,8 @@ import torch
 
 import content_routed_block_stats_amd as ssa
 import oracle as O
-from parity import LSE_TOL, O_TOL, STATS_REL, attn_errors, check_idx_properties, idx_ok
+from parity import (LSE_TOL, O_TOL, STATS_REL, attn_errors, check_idx_properties,
+                    check_tile_properties, idx_ok)
 from synth_inputs import CONFIGS, make_decode, make_prefill
 
 pytestmark = pytest.mark.gpu
@@ -152,3 +153,44 @@ def test_decode_256k_fullsize():
                                  Kfull, Vfull, idx_h[b, h], L, p, bf16_out=bf16_out)
             assert eo <= O_TOL[wl.dtype] and el <= LSE_TOL, (b, h, eo, el)
         say(f"  sequence {b} kv head {kv}: {wl.group} rows ok")
+
+
+@pytest.mark.timeout(600)
+def test_gqa_prefill_128k_tiles_fullsize():
+    """Query-tile-shared routing and tile attention at the 128K GQA workload:
+    properties of every tile's selection, and sampled tiles (their selection
+    and sampled rows' O and LSE) against the oracle."""
+    wl = CONFIGS["gqa_prefill_128k"]
+    say("case gqa_prefill_128k tiles: generating on the GPU")
+    data = make_prefill(wl, seed=0, device=DEV)
+    Q, K, V = data["Q"], data["K"], data["V"]
+    mu, sigma = ssa.ssa_block_stats(K, wl.block)
+    idx = ssa.ssa_route_tiles(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta)
+    Oo, lse = ssa.ssa_tile_attn_fwd(Q, K, V, idx, block_size=wl.block, window=wl.window,
+                                    scale=wl.scale)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    say("  selection properties on every tile")
+    check_tile_properties(idx_h[0], wl.seq_len, wl.block, wl.top_k)
+    p = O.Params(wl.block, wl.top_k, wl.window, wl.beta, wl.scale)
+    rng = np.random.default_rng(3)
+    tiles = idx_h.shape[2]
+    picks = [(0, 0), (5, 1), (31, 17), (6, 130), (22, tiles - 1), (13, int(rng.integers(200, tiles)))]
+    bf16_out = Oo.dtype == torch.bfloat16
+    for (h, j) in picks:
+        kv = h // wl.group
+        Kh = O.as_f64(K[0, kv])
+        Vh = O.as_f64(V[0, kv])
+        C = min(j, wl.seq_len // wl.block)          # the tile's routable blocks
+        mu_o, sg_o = O.block_stats(Kh[:C * wl.block], wl.block)
+        orc = O.tile_select(O.as_f64(Q[0, h, :(j + 1) * wl.block]), mu_o, sg_o, p, j)
+        ok, _ = idx_ok(idx_h[0, h, j], orc)
+        assert ok, f"tile selection mismatch at head {h}, tile {j}: {idx_h[0, h, j]} vs {orc['idx']}"
+        for t in sorted(set([j * wl.block, j * wl.block + wl.block - 1] +
+                            list(rng.integers(j * wl.block, (j + 1) * wl.block, size=6)))):
+            eo, el = attn_errors(Oo[0, h, t].float().cpu().numpy(), float(lse[0, h, t]),
+                                 O.as_f64(Q[0, h, t]), Kh, Vh, idx_h[0, h, j], t, p,
+                                 bf16_out=bf16_out)
+            assert eo <= O_TOL[wl.dtype] and el <= LSE_TOL, (h, j, t, eo, el)
+        say(f"  head {h} tile {j}: selection ok, rows ok")
+

@@ -19,7 +19,7 @@ import torch
 
 import content_routed_block_stats_amd as ssa
 import oracle as O
-from parity import LSE_TOL, O_TOL, attn_errors, idx_ok
+from parity import LSE_TOL, O_TOL, attn_errors, check_tile_properties, idx_ok
 from synth_inputs import CONFIGS, make_prefill
 
 pytestmark = pytest.mark.gpu
@@ -68,20 +68,6 @@ def run_tiles(data, wl, out_dtype=None):
                                     scale=wl.scale, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return dict(idx=idx, kth=kth, O=Oo, lse=lse)
-
-
-def check_tile_properties(idx: np.ndarray, n: int, B: int, k: int) -> None:
-    """Every tile: ascending distinct blocks before the tile, min(k, min(j, nb))
-    of them, -1 padding at the end.  idx: [rows, tiles, k]."""
-    nb = n // B
-    tiles = idx.shape[-2]
-    want = np.minimum(k, np.minimum(np.arange(tiles), nb))
-    valid = idx >= 0
-    assert np.array_equal(valid.sum(-1), np.broadcast_to(want, valid.shape[:-1]))
-    assert np.all(valid == (np.arange(k) < want[:, None]))
-    big = np.where(valid, idx, np.iinfo(np.int32).max)
-    assert np.all((np.diff(big, axis=-1) > 0) | ~valid[..., 1:])
-    assert np.all(np.where(valid, idx < np.arange(tiles)[:, None], True))
 
 
 def compare(data, res, wl, row_limit=600, seed=0):
