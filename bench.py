@@ -440,6 +440,8 @@ def main() -> int:
         "roofline": {"kernel": "tile_attn", "bound": "mfma", "achieved": round(ta_tf, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ta_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": counted_traffic("tile_attn", kernel_source_digest(
+                         "tile_attn.hip", "kv_chunks.hpp", "ssa_common.hpp")),
                      "algorithmic_flops_per_launch": ta_fl},
         "steps": treps}
     del ws_rt, ws_ta, idx_t
@@ -458,6 +460,8 @@ def main() -> int:
     res["tempered_route"] = {"kernel": "tempered_route", "ms": round(t_temp, 3), "bound": "mfma",
                              "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": counted_traffic("tempered_route", kernel_source_digest(
+                                 "tempered_route.hip", "kv_chunks.hpp", "ssa_common.hpp")),
                              "algorithmic_flops_per_launch": tempered_flops(wl), "reps": reps}
     del O, lse, ws_a, ws_r
     if not args.no_decode:
