@@ -252,6 +252,60 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndarray,
     return O, float(m + math.log(l))
 
 
+# -- backward: gradients through the exact attention over S(t) -----------------
+#
+# Training through the layer (the write-up's module list trains small SSA
+# models and its "Selected results" adapt a dense model swapped to SSA): the
+# selection is a discrete choice, so gradients flow through the softmax
+# attention over the chosen keys, with S(t) held fixed.  For a loss L with
+# upstream gradient dO_t = dL/dO_t:
+#   p_j = softmax_j(scale q.k_j) over j in S(t),  O = sum_j p_j v_j,
+#   dP_j = dO . v_j,   D = sum_j p_j dP_j  (= dO . O),
+#   dS_j = p_j (dP_j - D)                 (softmax Jacobian),
+#   dq   = scale sum_j dS_j k_j,   dk_j += scale dS_j q,   dv_j += p_j dO.
+
+def attend_backward(q: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndarray, scale: float,
+                    dO: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(dq [d], dK_S [|S|, d], dV_S [|S|, d]) of one row's attention over keys S."""
+    q = as_f64(q)
+    Ks = as_f64(K)[S]
+    Vs = as_f64(V)[S]
+    dO = as_f64(dO)
+    s = scale * (Ks @ q)
+    p = np.exp(s - s.max())
+    p = p / p.sum()
+    dP = Vs @ dO
+    D = float(p @ dP)
+    dS = p * (dP - D)
+    dq = scale * (dS @ Ks)
+    dK = scale * np.outer(dS, q)
+    dV = np.outer(p, dO)
+    return dq, dK, dV
+
+
+def head_backward(Qh, K, V, idx_h, p: Params, dOh, rows=None):
+    """Gradients for the q-heads of one KV head with fixed selections.
+
+    Qh, dOh: [g, n, d] (the group's q-heads); K, V: [n, d]; idx_h: [g, n, k]
+    per-query selections (as the forward used).  Returns (dQ [g, n, d],
+    dK [n, d], dV [n, d]); dK/dV sum over every row of the group.  rows, if
+    given, restricts the sum to those (j, t) rows (the other dQ rows stay 0).
+    """
+    Qh, dOh = as_f64(Qh), as_f64(dOh)
+    g, n, d = Qh.shape
+    dQ = np.zeros((g, n, d))
+    dK = np.zeros((n, d))
+    dV = np.zeros((n, d))
+    it = rows if rows is not None else [(j, t) for j in range(g) for t in range(n)]
+    for (j, t) in it:
+        S = key_set(t, np.asarray(idx_h)[j, t], p.block, p.window)
+        dq, dk, dv = attend_backward(Qh[j, t], K, V, S, p.scale, dOh[j, t])
+        dQ[j, t] = dq
+        dK[S] += dk
+        dV[S] += dv
+    return dQ, dK, dV
+
+
 # -- step 6: dropped mass ------------------------------------------------------
 
 def dropped_mass(q: np.ndarray, K: np.ndarray, S: np.ndarray, t: int,

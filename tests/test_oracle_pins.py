@@ -29,7 +29,7 @@ def _impl(**overrides):
         routable_blocks=OR.routable_blocks, key_set=OR.key_set, attend=OR.attend,
         dropped_mass=OR.dropped_mass, recovery_weight=OR.recovery_weight,
         tempered_scores=OR.tempered_scores, tile_routable_blocks=OR.tile_routable_blocks,
-        tile_scores=OR.tile_scores)
+        tile_scores=OR.tile_scores, attend_backward=OR.attend_backward)
     for k, v in overrides.items():
         setattr(ns, k, v)
 
@@ -46,6 +46,19 @@ def _impl(**overrides):
         return dict(S=S, O=Oo, lse=lse)
     ns.tile_select = tile_select
     ns.tile_prefill_row = tile_prefill_row
+
+    def head_backward(Qh, K, V, idx_h, p, dOh):
+        g, n, d = Qh.shape
+        dQ, dK, dV = np.zeros((g, n, d)), np.zeros((n, d)), np.zeros((n, d))
+        for j in range(g):
+            for t in range(n):
+                S = ns.key_set(t, idx_h[j, t], p.block, p.window)
+                dq, dk, dv = ns.attend_backward(Qh[j, t], K, V, S, p.scale, dOh[j, t])
+                dQ[j, t] = dq
+                dK[S] += dk
+                dV[S] += dv
+        return dQ, dK, dV
+    ns.head_backward = head_backward
 
     def prefill_row(q, K, V, mu, sigma, p, t, with_dense=False):
         C = ns.routable_blocks(t, p.block, mu.shape[0])
@@ -490,12 +503,106 @@ def check_tile_dense_reduction(ns, seed=14):
                 np.testing.assert_allclose(row["O"], ref[t], rtol=1e-12, atol=1e-12)
 
 
+def _bwd_case(rng, g=2, n=40, d=4, B=8, k=2, W=5):
+    Q = rng.normal(size=(g, n, d))
+    K = rng.normal(size=(n, d)) + np.repeat(rng.normal(size=(n // B + 1, d)), B, 0)[:n]
+    V = rng.normal(size=(n, d))
+    dO = rng.normal(size=(g, n, d))
+    mu, sigma = OR.block_stats(K, B)
+    p = O.Params(B, k, W, 2.0, 0.6)
+    idx = np.stack([np.stack([OR.prefill_row(Q[j, t], K, V, mu, sigma, p, t)["idx"]
+                              for t in range(n)]) for j in range(g)])
+    return Q, K, V, dO, idx, p
+
+
+def _forward_loss(Q, K, V, dO, idx, p):
+    """L = sum_t dO_t . O_t with the selections fixed (forward by the textbook
+    masked-dense softmax, independent of the oracle's attend)."""
+    g, n, _ = Q.shape
+    L = 0.0
+    for j in range(g):
+        for t in range(n):
+            S = set(OR.key_set(t, idx[j, t], p.block, p.window).tolist())
+            mask = np.array([jj in S for jj in range(n)])
+            o, _ = _textbook(Q[j, t], K, V, mask, p.scale)
+            L += float(dO[j, t] @ o)
+    return L
+
+
+def check_backward_finite_differences(ns, seed=15):
+    """Central differences of L = sum dO.O against the gradients, in every
+    coordinate of a few q, k and v entries (selections held fixed)."""
+    rng = np.random.default_rng(seed)
+    Q, K, V, dO, idx, p = _bwd_case(rng)
+    dQ, dK, dV = ns.head_backward(Q, K, V, idx, p, dO)
+    h = 1e-6
+    for (name, X, G) in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV)):
+        flat = X.reshape(-1)
+        gflat = G.reshape(-1)
+        for i in rng.choice(flat.size, size=12, replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp = _forward_loss(Q, K, V, dO, idx, p)
+            flat[i] = old - h
+            lm = _forward_loss(Q, K, V, dO, idx, p)
+            flat[i] = old
+            num = (lp - lm) / (2 * h)
+            assert abs(num - gflat[i]) <= 1e-6 * max(1.0, abs(num)), (name, int(i), num, gflat[i])
+
+
+def check_backward_autograd(ns, seed=16):
+    """Gradients against torch autograd (CPU, float64) of the masked-dense
+    formulation with the mask M[t, j] = [j in S(t)], GQA heads sharing K, V."""
+    rng = np.random.default_rng(seed)
+    Q, K, V, dO, idx, p = _bwd_case(rng, g=3, n=33, d=5, B=4, k=3, W=3)
+    g, n, d = Q.shape
+    M = np.zeros((g, n, n), dtype=bool)
+    for j in range(g):
+        for t in range(n):
+            M[j, t, OR.key_set(t, idx[j, t], p.block, p.window)] = True
+    Qt = torch.tensor(Q, requires_grad=True)
+    Kt = torch.tensor(K, requires_grad=True)
+    Vt = torch.tensor(V, requires_grad=True)
+    sc = (Qt @ Kt.T) * p.scale
+    sc = sc.masked_fill(~torch.tensor(M), float("-inf"))
+    Ot = torch.softmax(sc, -1) @ Vt
+    (Ot * torch.tensor(dO)).sum().backward()
+    dQ, dK, dV = ns.head_backward(Q, K, V, idx, p, dO)
+    np.testing.assert_allclose(dQ, Qt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dK, Kt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dV, Vt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def check_backward_dense(ns, seed=17):
+    """k >= nb and W >= B: the gradients are dense causal attention's (torch
+    SDPA backward, CPU float64)."""
+    rng = np.random.default_rng(seed)
+    n, d, B = 30, 4, 6
+    Q = rng.normal(size=(1, n, d))
+    K = rng.normal(size=(n, d))
+    V = rng.normal(size=(n, d))
+    dO = rng.normal(size=(1, n, d))
+    p = O.Params(B, n // B + 1, B, 2.0, 0.5)
+    idx = np.array([[sorted(list(range(min(n // B, (t + 1) // B)))) +
+                     [-1] * (p.top_k - min(n // B, (t + 1) // B)) for t in range(n)]])
+    Qt = torch.tensor(Q[None], requires_grad=True)
+    Kt = torch.tensor(K[None, None], requires_grad=True)
+    Vt = torch.tensor(V[None, None], requires_grad=True)
+    Ot = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, is_causal=True, scale=0.5)
+    (Ot * torch.tensor(dO[None])).sum().backward()
+    dQ, dK, dV = ns.head_backward(Q, K, V, idx, p, dO)
+    np.testing.assert_allclose(dQ, Qt.grad[0].numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dK, Kt.grad[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dV, Vt.grad[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
 CHECKS = [check_golden, check_stats_vs_library, check_scores_two_ways, check_centroid_limit,
           check_topk_brute, check_dense_reduction, check_window_only, check_gather_equals_mask,
           check_recovery_law, check_recovery_law_pipeline, check_dropped_mass,
           check_decode_equals_prefill, check_invariances, check_tempered_closed_form,
           check_tempered_limits, check_tile_scores_moments, check_tile_select_brute,
-          check_tile_single_row, check_tile_dense_reduction]
+          check_tile_single_row, check_tile_dense_reduction, check_backward_finite_differences,
+          check_backward_autograd, check_backward_dense]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda f: f.__name__)
@@ -617,6 +724,33 @@ def _mut_tile_no_variance(Qt, mu, sigma, beta):
     return OR.tile_scores(Qt, mu, sigma, 0.0)
 
 
+def _mut_bwd_no_D(q, K, V, S, scale, dO):
+    dq, dK, dV = OR.attend_backward(q, K, V, S, scale, dO)
+    Ks = OR.as_f64(K)[S]
+    s_ = scale * (Ks @ OR.as_f64(q))
+    p_ = np.exp(s_ - s_.max())
+    p_ /= p_.sum()
+    dS = p_ * (OR.as_f64(V)[S] @ OR.as_f64(dO))       # the -D term dropped
+    return scale * (dS @ Ks), scale * np.outer(dS, OR.as_f64(q)), dV
+
+
+def _mut_bwd_dk_unscaled(q, K, V, S, scale, dO):
+    dq, dK, dV = OR.attend_backward(q, K, V, S, scale, dO)
+    return dq, dK / scale, dV
+
+
+def _mut_bwd_dv_unnormalised(q, K, V, S, scale, dO):
+    dq, dK, dV = OR.attend_backward(q, K, V, S, scale, dO)
+    s_ = scale * (OR.as_f64(K)[S] @ OR.as_f64(q))
+    w = np.exp(s_ - s_.max())
+    return dq, dK, np.outer(w, OR.as_f64(dO))
+
+
+def _mut_bwd_dq_uses_v(q, K, V, S, scale, dO):
+    dq, dK, dV = OR.attend_backward(q, K, V, S, scale, dO)
+    return OR.attend_backward(q, V, V, S, scale, dO)[0], dK, dV
+
+
 MUTANTS = {
     "sample_covariance": dict(block_stats=_mut_sample_cov),
     "beta_not_halved": dict(route_scores=_mut_full_beta),
@@ -639,6 +773,10 @@ MUTANTS = {
     "tile_first_row_only": dict(tile_scores=_mut_tile_first_row),
     "tile_max_over_rows": dict(tile_scores=_mut_tile_max_row),
     "tile_variance_dropped": dict(tile_scores=_mut_tile_no_variance),
+    "backward_D_dropped": dict(attend_backward=_mut_bwd_no_D),
+    "backward_dk_unscaled": dict(attend_backward=_mut_bwd_dk_unscaled),
+    "backward_dv_unnormalised": dict(attend_backward=_mut_bwd_dv_unnormalised),
+    "backward_dq_uses_values": dict(attend_backward=_mut_bwd_dq_uses_v),
 }
 
 
@@ -692,3 +830,12 @@ def test_oracle_compositions_match_pinned_copies():
             ra = OR.tile_prefill_row(Q[t], K, V, a["idx"], p, t)
             rb = ns.tile_prefill_row(Q[t], K, V, b["idx"], p, t)
             assert ra["S"].tolist() == rb["S"].tolist() and np.array_equal(ra["O"], rb["O"])
+    rng2 = np.random.default_rng(22)
+    Qg = rng2.normal(size=(2, n, d))
+    dO = rng2.normal(size=(2, n, d))
+    idx = np.stack([np.stack([OR.prefill_row(Qg[j, t], K, V, mu, sigma, p, t)["idx"]
+                              for t in range(n)]) for j in range(2)])
+    a_ = OR.head_backward(Qg, K, V, idx, p, dO)
+    b_ = ns.head_backward(Qg, K, V, idx, p, dO)
+    for x, y in zip(a_, b_):
+        assert np.array_equal(x, y)
