@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     ssa_route_tempered,
     ssa_route_tiles,
     ssa_route_topk,
+    ssa_sparse_attn_bwd,
     ssa_sparse_attn_fwd,
     ssa_tile_attn_fwd,
     ssa_workspace_size,

@@ -20,7 +20,8 @@ LIB_PATH = os.environ.get("SSA_MI355X_LIB", os.path.join(HERE, "libssa_mi355x.so
 
 SSA_OK, SSA_ERR_INVALID_ARGUMENT, SSA_ERR_UNSUPPORTED, SSA_ERR_WORKSPACE_TOO_SMALL, SSA_ERR_HIP = range(5)
 SSA_F32, SSA_BF16 = 0, 1
-SSA_OP_ROUTE, SSA_OP_ATTN, SSA_OP_DECODE, SSA_OP_ROUTE_TILES, SSA_OP_TILE_ATTN = 1, 2, 3, 4, 5
+(SSA_OP_ROUTE, SSA_OP_ATTN, SSA_OP_DECODE, SSA_OP_ROUTE_TILES, SSA_OP_TILE_ATTN,
+ SSA_OP_ATTN_BWD) = 1, 2, 3, 4, 5, 6
 
 _vp = ctypes.c_void_p
 
@@ -69,11 +70,14 @@ def lib() -> ctypes.CDLL:
     L.ssa_route_tempered.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
     L.ssa_route_tiles.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_tile_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.ssa_sparse_attn_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _vp]
     L.ssa_sparse_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_decode_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
     for name in ("ssa_block_stats", "ssa_workspace_size", "ssa_route_topk", "ssa_route_tempered",
-                 "ssa_route_tiles", "ssa_tile_attn_fwd", "ssa_sparse_attn_fwd", "ssa_decode_step"):
+                 "ssa_route_tiles", "ssa_tile_attn_fwd", "ssa_sparse_attn_fwd",
+                 "ssa_sparse_attn_bwd", "ssa_decode_step"):
         getattr(L, name).restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
@@ -278,6 +282,37 @@ def ssa_sparse_attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: 
     _check(lib().ssa_sparse_attn_fwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx),
                                      _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
     return out, lse
+
+
+def ssa_sparse_attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,
+                        O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor, *, block_size: int,
+                        window: int, scale: float | None = None,
+                        workspace: torch.Tensor | None = None):
+    """Gradients through the sparse attention with fixed selections:
+    (dQ [b, Hq, n, d], dK, dV [b, Hkv, n, d]) float32, given the forward's O and lse
+    and the upstream gradient dO (same dtype as Q)."""
+    _dev_check(Q, K, V, idx, O, lse, dO)
+    b, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    if K.shape != (b, hkv, n, d) or V.shape != K.shape:
+        raise ValueError("K/V do not match Q")
+    if idx.dtype != torch.int32 or idx.shape[:3] != (b, hq, n):
+        raise ValueError("idx must be int32 [b, Hq, n, k]")
+    if O.shape != Q.shape or dO.shape != Q.shape or dO.dtype != Q.dtype:
+        raise ValueError("O and dO must be [b, Hq, n, d], dO in Q's dtype")
+    if lse.shape != (b, hq, n) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [b, Hq, n]")
+    p = make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=n,
+                    block_size=block_size, top_k=idx.shape[3], window=window, scale=scale,
+                    in_dtype=Q.dtype, out_dtype=O.dtype)
+    dQ = torch.empty((b, hq, n, d), dtype=torch.float32, device=Q.device)
+    dK = torch.empty((b, hkv, n, d), dtype=torch.float32, device=Q.device)
+    dV = torch.empty((b, hkv, n, d), dtype=torch.float32, device=Q.device)
+    ws = _workspace(p, SSA_OP_ATTN_BWD, Q.device, workspace)
+    _check(lib().ssa_sparse_attn_bwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(O),
+                                     _ptr(lse), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
+                                     ws.numel(), _stream()))
+    return dQ, dK, dV
 
 
 def ssa_decode_step(q, k_new, v_new, K_cache, V_cache, cache_len, mu, sigma, *, block_size: int,

@@ -1,0 +1,650 @@
+// Backward of the sparse attention over fixed selections (prefill).
+//
+// Write-up "Subquadratic Sparse Attention (SSA)": its module list trains SSA
+// models and its "Selected results" adapt a dense model swapped to SSA, so
+// gradients flow through the layer; the selection is a discrete choice and is
+// held fixed.  For every row t with key set S(t) (introduction steps ii-iii):
+//   p_j = softmax_j(scale q.k_j) = exp(scale q.k_j - LSE),  D = dO . O,
+//   dP_j = dO . v_j,  dS_j = p_j (dP_j - D),
+//   dq = scale sum_j dS_j k_j,  dk_j += scale dS_j q,  dv_j += p_j dO,
+// with the forward's LSE, so no softmax is re-normalised.
+//
+//  1. rowdot     -- D per row (float32), from the forward's O and dO;
+//  2. dq_task    -- the forward's block-major tasks again (lanes on rows, as in
+//     the forward): per 64-key chunk of the task's block, S^T = K Q^T and
+//     dP^T = V dO^T on MFMA, dS^T on the vector units, dQ^T += K^T dS^T on
+//     MFMA; one float32 dQ partial per (row, selected block);
+//  3. dkv_chunk  -- one workgroup per 64-key chunk of a KV head owns those
+//     keys' dK and dV (no atomics across workgroups): it streams every row
+//     that attends to them -- the block's selected rows from the dispatch,
+//     then the window rows whose window reaches the chunk and whose selection
+//     does not hold the block -- and, with lanes on keys, computes S = Q K^T,
+//     dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS on MFMA;
+//  4. dq_window  -- per tile of 128 rows, the window part of dQ (window keys
+//     outside the row's selected blocks) plus the row's dQ partials.
+//
+// Operands: K and V rows (bf16, exact) as they are; K^T, Q^T, dO^T and the
+// probabilities / dS enter their products as float16, each tensor scaled by an
+// exact power of two that keeps its largest value below 2^15 (bf16 values in
+// the float16 normal range convert exactly); float32 inputs use float32 MFMA
+// throughout.  Chunk images come from kv_image_kernel: image A = (K rows,
+// V^T), image B = (V rows, K^T).
+#include <algorithm>
+#include <type_traits>
+
+#include "kv_chunks.hpp"
+#include "ssa_common.hpp"
+#include "ssa_internal.hpp"
+
+namespace ssa {
+namespace {
+
+constexpr int kBwdThreads = 512;     // 8 waves
+constexpr int kKvRows = 128;         // rows staged per iteration of the key pass
+constexpr int kWinTile = 128;        // rows per tile of the window pass (4 waves x 32)
+
+// ------------------------------------------------------------------ rowdot --
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const InT* __restrict__ dO,
+                                                         const OutT* __restrict__ O,
+                                                         float* __restrict__ Drow, int64_t rows,
+                                                         int D) {
+  const int lane = threadIdx.x % 64;
+  const int64_t r = int64_t(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (r >= rows) return;
+  float acc = 0.f;
+  for (int i = lane; i < D; i += 64) acc += load_f32(dO, r * D + i) * load_f32(O, r * D + i);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += wave_shfl_xor(acc, o);
+  if (lane == 0) Drow[r] = acc;
+}
+
+// float16 fragment of 8 values (or float32 for float32 inputs)
+template <bool F32>
+using VF = typename std::conditional<F32, floatx8, f16x8>::type;
+
+template <bool F32>
+__device__ __forceinline__ void set_vf(VF<F32>& f, int e, float v) {
+  if constexpr (F32) f[e] = v; else f[e] = static_cast<_Float16>(v);
+}
+
+// ----------------------------------------------------------------- dq_task --
+// One workgroup (8 waves x 32 rows) per task; chunk images of the task's
+// block double-buffered in LDS (image A's K part, then all of image B).
+template <bool F32, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_task_kernel(
+    const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Drow, const uint8_t* __restrict__ img_a,
+    const uint8_t* __restrict__ img_b, const uint32_t* __restrict__ kmax, int64_t n_chunks,
+    const int4* __restrict__ tasks, const int32_t* __restrict__ task_count,
+    const uint32_t* __restrict__ entries, float* __restrict__ dq_part, int64_t n, int g, int hq,
+    int hkv, int B, int64_t nb, float scale2, float scale) {
+  using A = AT<F32, D>;
+  using Frag = typename A::Frag;
+  constexpr int BUF = A::KBYTES + A::CHUNK;
+  constexpr int NBUF = 2 * BUF <= 128 * 1024 ? 2 : 1;   // float32, d = 128: one buffer
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * BUF];
+  const int64_t task = blockIdx.x;
+  if (task >= task_count[0]) return;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int4 tk = tasks[task];
+  const int64_t seg = tk.x, e0 = tk.y;
+  const int rows = tk.z;
+  const int64_t bkv = seg / nb, c = seg % nb, b = bkv / hkv, kv = bkv % hkv;
+  const int r = 32 * wave + ln;
+  const bool valid = r < rows;
+  int64_t row = 0;
+  if (valid) {
+    const uint32_t en = entries[e0 + r];
+    const int64_t rho = en >> 5, t = rho / g, jg = rho % g;
+    row = (b * hq + kv * g + jg) * n + t;
+  }
+  Frag bq[A::NS], bdo[A::NS];
+#pragma unroll
+  for (int s = 0; s < A::NS; ++s) {
+    bq[s] = load_row_frag<F32, D>(Q + row * D, s, h, valid);
+    bdo[s] = load_row_frag<F32, D>(dO + row * D, s, h, valid);
+  }
+  const float l2 = valid ? lse[row] * kLog2e : 0.f;
+  const float dr = valid ? Drow[row] : 0.f;
+  const bool wave_active = 32 * wave < rows;
+  const int cpb = B / kKeyChunk;
+  const int64_t ch0 = c * cpb;
+  const uint8_t* srca = img_a + bkv * n_chunks * A::CHUNK;
+  const uint8_t* srcb = img_b + bkv * n_chunks * A::CHUNK;
+  floatx16 dq[A::MTD];
+#pragma unroll
+  for (int i = 0; i < A::MTD; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dq[i][j] = 0.f;
+
+  dma_copy(lds, srca + ch0 * A::CHUNK, A::KBYTES, tid, kBwdThreads);
+  dma_copy(lds + A::KBYTES, srcb + ch0 * A::CHUNK, A::CHUNK, tid, kBwdThreads);
+  __syncthreads();
+  for (int q = 0; q < cpb; ++q) {
+    uint8_t* L = lds + (q % NBUF) * BUF;
+    if (NBUF == 2 && q + 1 < cpb) {
+      uint8_t* Ln = lds + ((q + 1) % NBUF) * BUF;
+      dma_copy(Ln, srca + (ch0 + q + 1) * A::CHUNK, A::KBYTES, tid, kBwdThreads);
+      dma_copy(Ln + A::KBYTES, srcb + (ch0 + q + 1) * A::CHUNK, A::CHUNK, tid, kBwdThreads);
+    }
+    if (wave_active) {
+      auto fa = [&](const uint8_t* base, int mt, int s) {
+        return *reinterpret_cast<const Frag*>(base + (mt * A::NS + s) * A::FRAG + lane * 8 * A::ES);
+      };
+      floatx16 sacc[2], pacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[mt][j] = pacc[mt][j] = 0.f;
+#pragma unroll
+      for (int s = 0; s < A::NS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          sacc[mt] = mma16(fa(L, mt, s), bq[s], sacc[mt]);                  // K rows . q
+          pacc[mt] = mma16(fa(L + A::KBYTES, mt, s), bdo[s], pacc[mt]);     // V rows . dO
+        }
+      // dS^T in the accumulators (keys 32mt + 8a + 4h + b of this lane's row)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][j], scale2, -l2));
+          sacc[mt][j] = p * (pacc[mt][j] - dr);
+        }
+      // dQ^T += K^T dS^T: image B's transposed part as A, dS^T as B (frag_k)
+      const uint8_t* kt = L + A::KBYTES + A::KBYTES;
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp) {
+        VF<F32> pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          set_vf<F32>(pf, e, sacc[sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)]);
+#pragma unroll
+        for (int mt = 0; mt < A::MTD; ++mt)
+          dq[mt] = mma16(*reinterpret_cast<const typename A::VFrag*>(kt + (mt * 4 + sp) * A::FRAG +
+                                                                      lane * 8 * A::ES),
+                         pf, dq[mt]);
+      }
+    }
+    __syncthreads();
+    if (NBUF == 1 && q + 1 < cpb) {
+      dma_copy(lds, srca + (ch0 + q + 1) * A::CHUNK, A::KBYTES, tid, kBwdThreads);
+      dma_copy(lds + A::KBYTES, srcb + (ch0 + q + 1) * A::CHUNK, A::CHUNK, tid, kBwdThreads);
+      __syncthreads();
+    }
+  }
+  if (!valid) return;
+  const float f = ldexpf(scale, F32 ? 0 : value_exponent(kmax[bkv]));
+  float* out = dq_part + (e0 + r) * D;
+#pragma unroll
+  for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      *reinterpret_cast<floatx4*>(out + 32 * mt + 8 * a + 4 * h) =
+          floatx4{dq[mt][4 * a] * f, dq[mt][4 * a + 1] * f, dq[mt][4 * a + 2] * f,
+                  dq[mt][4 * a + 3] * f};
+}
+
+// --------------------------------------------------------------- dkv_chunk --
+// One workgroup (8 waves: key half kh = wave % 2, row group rg = wave / 2) per
+// 64-key chunk of one (sequence, KV head).  Rows are staged kKvRows at a time
+// (Q and dO rows as they are, plus per row the log2-domain LSE, D, position
+// and mode: 0 = every key counts, 1 = window keys (t - W, t], 2 = none).
+template <bool F32, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(
+    const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Drow, const int32_t* __restrict__ idx,
+    const uint8_t* __restrict__ img_a, const uint8_t* __restrict__ img_b,
+    const uint32_t* __restrict__ qmax, const uint32_t* __restrict__ domax, int64_t n_chunks,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ cursor,
+    const uint32_t* __restrict__ entries, float* __restrict__ dK, float* __restrict__ dV, int64_t n,
+    int g, int hq, int hkv, int B, int64_t nb, int k, int W, float scale2, float scale) {
+  using A = AT<F32, D>;
+  using In = typename A::In;
+  using Frag = typename A::Frag;
+  constexpr int ES = A::ES;
+  constexpr int ROWB = D * ES;
+  constexpr int ROWS = (F32 && D == 128) ? kKvRows / 2 : kKvRows;   // LDS: float32, d = 128
+  constexpr int RG = ROWS / 32;                                      // row groups in use
+  __shared__ __attribute__((aligned(1024))) uint8_t img[2 * A::KBYTES];   // K rows, V rows
+  __shared__ __attribute__((aligned(16))) uint8_t rq[ROWS * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t rdo[ROWS * ROWB];
+  __shared__ float rl2[ROWS], rd[ROWS];
+  __shared__ int64_t rt[ROWS];
+  __shared__ int32_t rmode[ROWS];
+  static_assert(ROWS * ROWB >= kKeyChunk * D * 4, "reduction buffer");
+
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int kh = wave % 2, rg = wave / 2;
+  const int64_t ch = blockIdx.x % n_chunks, bkv = blockIdx.x / n_chunks;
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  const int64_t key0 = ch * kKeyChunk;
+  const int64_t c = key0 / B;
+  int64_t sel_start = 0, sel_cnt = 0;
+  if (c < nb) {
+    const int64_t sg = bkv * nb + c;
+    sel_cnt = counts[sg];
+    sel_start = cursor[sg] - sel_cnt;
+  }
+  const int64_t t_hi = min(n - 1, key0 + kKeyChunk - 1 + W - 1);
+  const int64_t win_cnt = (t_hi - key0 + 1) * g;
+  const int64_t total = sel_cnt + win_cnt;
+  // float16 scales of Q^T and dO^T for this KV head's group of q-heads
+  int eq = 0, edo = 0;
+  if constexpr (!F32) {
+    uint32_t mq = 0, md = 0;
+    for (int j = 0; j < g; ++j) {
+      mq = max(mq, qmax[b * hq + kv * g + j]);
+      md = max(md, domax[b * hq + kv * g + j]);
+    }
+    eq = value_exponent(mq);
+    edo = value_exponent(md);
+  }
+  const float sq = ldexpf(1.f, -eq), sdo = ldexpf(1.f, -edo);
+
+  dma_copy(img, img_a + (bkv * n_chunks + ch) * A::CHUNK, A::KBYTES, tid, kBwdThreads);
+  dma_copy(img + A::KBYTES, img_b + (bkv * n_chunks + ch) * A::CHUNK, A::KBYTES, tid, kBwdThreads);
+
+  floatx16 dk[A::MTD], dv[A::MTD];
+#pragma unroll
+  for (int i = 0; i < A::MTD; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dk[i][j] = dv[i][j] = 0.f;
+  const int64_t my_key = key0 + 32 * kh + ln;
+
+  for (int64_t i0 = 0; i0 < total; i0 += ROWS) {
+    // stage rows [i0, i0 + ROWS): the selected rows first, then the window rows
+    if (tid < ROWS) {
+      const int64_t i = i0 + tid;
+      int mode = 2;
+      int64_t t = 0, row = -1;
+      if (i < sel_cnt) {
+        const uint32_t en = entries[sel_start + i];
+        const int64_t rho = en >> 5, jg = rho % g;
+        t = rho / g;
+        row = (b * hq + kv * g + jg) * n + t;
+        mode = 0;
+      } else if (i < total) {
+        const int64_t w = i - sel_cnt, jg = w % g;
+        t = key0 + w / g;
+        row = (b * hq + kv * g + jg) * n + t;
+        bool sel = false;
+        for (int q = 0; q < k; ++q) sel |= idx[row * k + q] == int32_t(c);
+        mode = sel ? 2 : 1;
+      }
+      rt[tid] = row;            // the row index first, the position below
+      rl2[tid] = row >= 0 ? lse[row] * kLog2e : 0.f;
+      rd[tid] = row >= 0 ? Drow[row] : 0.f;
+      rmode[tid] = mode;
+      (void)t;
+    }
+    __syncthreads();
+    constexpr int PIECES = ROWB / 16;
+    for (int w = tid; w < ROWS * PIECES; w += kBwdThreads) {
+      const int rr = w / PIECES, pc = w % PIECES;
+      const int64_t row = rt[rr];
+      u32x4 vq = {0u, 0u, 0u, 0u}, vd = vq;
+      if (row >= 0 && rmode[rr] != 2) {
+        vq = reinterpret_cast<const u32x4*>(Q + row * D)[pc];
+        vd = reinterpret_cast<const u32x4*>(dO + row * D)[pc];
+      }
+      reinterpret_cast<u32x4*>(rq + rr * ROWB)[pc] = vq;
+      reinterpret_cast<u32x4*>(rdo + rr * ROWB)[pc] = vd;
+    }
+    __syncthreads();
+    if (tid < ROWS) rt[tid] = rt[tid] >= 0 ? rt[tid] % n : -1;   // position t of the row
+    __syncthreads();
+
+    const int r0 = 32 * rg;
+    if (rg < RG && i0 + r0 < total) {
+      // S = Q K^T and dP = dO V^T for this wave's 32 rows x 32 keys (lanes on keys)
+      floatx16 sacc, pacc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
+#pragma unroll
+      for (int s = 0; s < A::NS; ++s) {
+        const Frag kf = *reinterpret_cast<const Frag*>(img + (kh * A::NS + s) * A::FRAG + lane * 8 * ES);
+        const Frag vf = *reinterpret_cast<const Frag*>(img + A::KBYTES + (kh * A::NS + s) * A::FRAG +
+                                                       lane * 8 * ES);
+        const Frag qa = *reinterpret_cast<const Frag*>(rq + (r0 + ln) * ROWB + (16 * s + 8 * h) * ES);
+        const Frag da = *reinterpret_cast<const Frag*>(rdo + (r0 + ln) * ROWB + (16 * s + 8 * h) * ES);
+        sacc = mma16(qa, kf, sacc);
+        pacc = mma16(da, vf, pacc);
+      }
+      // element j: row r0 + 8(j/4) + 4h + j%4, key my_key
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int rr = r0 + 8 * (j / 4) + 4 * h + j % 4;
+        const int mode = rmode[rr];
+        const int64_t t = rt[rr];
+        const bool on = my_key < n && (mode == 0 || (mode == 1 && my_key <= t && my_key > t - W));
+        const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[j], scale2, -rl2[rr])) : 0.f;
+        sacc[j] = p;
+        pacc[j] = p * (pacc[j] - rd[rr]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: rows contracted in frag_k order
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        VF<F32> pf, sf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 4 * (2 * sp + (e >> 2)) + (e & 3);
+          set_vf<F32>(pf, e, sacc[j]);
+          set_vf<F32>(sf, e, pacc[j]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < A::MTD; ++mt) {
+          VF<F32> qt, dt;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int rr = r0 + frag_k(sp, h, e);
+            const int col = 32 * mt + ln;
+            set_vf<F32>(qt, e, load_f32(reinterpret_cast<const In*>(rq + rr * ROWB), col) * sq);
+            set_vf<F32>(dt, e, load_f32(reinterpret_cast<const In*>(rdo + rr * ROWB), col) * sdo);
+          }
+          dv[mt] = mma16(dt, pf, dv[mt]);
+          dk[mt] = mma16(qt, sf, dk[mt]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // the row groups' partial sums, added in LDS in a fixed order (float32,
+  // 64 keys x D): the result does not depend on scheduling
+  float* red = reinterpret_cast<float*>(rq);   // ROWS * ROWB >= 64 * D * 4 bytes
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int round = 0; round < RG; ++round) {
+      if (rg == round) {
+#pragma unroll
+        for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int col = 32 * mt + 8 * (j / 4) + 4 * h + j % 4;
+            float* slot = &red[(32 * kh + ln) * D + col];
+            const float v = pass == 0 ? dk[mt][j] : dv[mt][j];
+            *slot = round == 0 ? v : *slot + v;
+          }
+      }
+      __syncthreads();
+    }
+    const float f = pass == 0 ? ldexpf(scale, eq) : ldexpf(1.f, edo);
+    float* dst = (pass == 0 ? dK : dV) + (bkv * n + key0) * D;
+    for (int w = tid; w < kKeyChunk * D; w += kBwdThreads)
+      if (key0 + w / D < n) dst[w] = red[w] * f;
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------- dq_window --
+// One workgroup (4 waves x 32 rows) per tile of 128 rows (rho = t g + jg) of
+// one (sequence, KV head): the window part of dQ over window keys outside the
+// row's selected blocks, then the row's dQ partials added.
+template <bool F32, int D>
+__global__ __launch_bounds__(256) void bwd_dq_window_kernel(
+    const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Drow, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ pos, const float* __restrict__ dq_part,
+    const uint8_t* __restrict__ img_a, const uint8_t* __restrict__ img_b,
+    const uint32_t* __restrict__ kmax, int64_t n_chunks, float* __restrict__ dQ, int64_t n, int g,
+    int hq, int hkv, int B, int k, int W, float scale2, float scale, int64_t n_tiles) {
+  using A = AT<F32, D>;
+  using Frag = typename A::Frag;
+  constexpr int BUF = A::KBYTES + A::CHUNK;
+  constexpr int NBUF = 2 * BUF <= 128 * 1024 ? 2 : 1;   // float32, d = 128: one buffer
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * BUF];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int64_t bkv = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  const int64_t rho0 = tile * kWinTile, rows_total = n * g;
+  const int64_t rho = rho0 + 32 * wave + ln;
+  const bool valid = rho < rows_total;
+  const int64_t t = valid ? rho / g : 0, jg = valid ? rho % g : 0;
+  const int64_t row = (b * hq + kv * g + jg) * n + t;
+  Frag bq[A::NS], bdo[A::NS];
+#pragma unroll
+  for (int s = 0; s < A::NS; ++s) {
+    bq[s] = load_row_frag<F32, D>(Q + row * D, s, h, valid);
+    bdo[s] = load_row_frag<F32, D>(dO + row * D, s, h, valid);
+  }
+  const float l2 = valid ? lse[row] * kLog2e : 0.f;
+  const float dr = valid ? Drow[row] : 0.f;
+  const int64_t t_lo = rho0 / g, t_hi = min(n - 1, (rho0 + kWinTile - 1) / g);
+  const int64_t ch_lo = max(int64_t(0), t_lo - W + 1) / kKeyChunk, ch_hi = t_hi / kKeyChunk;
+  const int64_t wave_t_lo = min(n - 1, (rho0 + 32 * wave) / g);
+  const int64_t wave_t_hi = min(n - 1, (rho0 + 32 * wave + 31) / g);
+  const bool wave_active = rho0 + 32 * wave < rows_total;
+  const uint8_t* srca = img_a + bkv * n_chunks * A::CHUNK;
+  const uint8_t* srcb = img_b + bkv * n_chunks * A::CHUNK;
+  floatx16 dq[A::MTD];
+#pragma unroll
+  for (int i = 0; i < A::MTD; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dq[i][j] = 0.f;
+
+  dma_copy(lds, srca + ch_lo * A::CHUNK, A::KBYTES, tid, 256);
+  dma_copy(lds + A::KBYTES, srcb + ch_lo * A::CHUNK, A::CHUNK, tid, 256);
+  __syncthreads();
+  for (int64_t ch = ch_lo; ch <= ch_hi; ++ch) {
+    const int buf = int((ch - ch_lo) % NBUF);
+    uint8_t* L = lds + buf * BUF;
+    if (NBUF == 2 && ch + 1 <= ch_hi) {
+      uint8_t* Ln = lds + (buf ^ 1) * BUF;
+      dma_copy(Ln, srca + (ch + 1) * A::CHUNK, A::KBYTES, tid, 256);
+      dma_copy(Ln + A::KBYTES, srcb + (ch + 1) * A::CHUNK, A::CHUNK, tid, 256);
+    }
+    const int64_t key0 = ch * kKeyChunk;
+    if (wave_active && key0 <= wave_t_hi && key0 + kKeyChunk - 1 > wave_t_lo - W) {
+      const int32_t blk = int32_t(key0 / B);
+      bool excl = false;
+      if (valid)
+        for (int i = 0; i < k; ++i) excl |= idx[row * k + i] == blk;
+      const int64_t tv = valid && !excl ? t : -(int64_t(1) << 40);
+      auto fa = [&](const uint8_t* base, int mt, int s) {
+        return *reinterpret_cast<const Frag*>(base + (mt * A::NS + s) * A::FRAG + lane * 8 * A::ES);
+      };
+      floatx16 sacc[2], pacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[mt][j] = pacc[mt][j] = 0.f;
+#pragma unroll
+      for (int s = 0; s < A::NS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          sacc[mt] = mma16(fa(L, mt, s), bq[s], sacc[mt]);
+          pacc[mt] = mma16(fa(L + A::KBYTES, mt, s), bdo[s], pacc[mt]);
+        }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int64_t kj = key0 + 32 * mt + 8 * (j / 4) + 4 * h + j % 4;
+          const bool on = kj <= tv && kj > tv - W;
+          const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[mt][j], scale2, -l2)) : 0.f;
+          sacc[mt][j] = p * (pacc[mt][j] - dr);
+        }
+      const uint8_t* kt = L + A::KBYTES + A::KBYTES;
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp) {
+        VF<F32> pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          set_vf<F32>(pf, e, sacc[sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)]);
+#pragma unroll
+        for (int mt = 0; mt < A::MTD; ++mt)
+          dq[mt] = mma16(*reinterpret_cast<const typename A::VFrag*>(kt + (mt * 4 + sp) * A::FRAG +
+                                                                      lane * 8 * A::ES),
+                         pf, dq[mt]);
+      }
+    }
+    __syncthreads();
+    if (NBUF == 1 && ch + 1 <= ch_hi) {
+      dma_copy(lds, srca + (ch + 1) * A::CHUNK, A::KBYTES, tid, 256);
+      dma_copy(lds + A::KBYTES, srcb + (ch + 1) * A::CHUNK, A::CHUNK, tid, 256);
+      __syncthreads();
+    }
+  }
+  if (!valid) return;
+  const float f = ldexpf(scale, F32 ? 0 : value_exponent(kmax[bkv]));
+#pragma unroll
+  for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dq[mt][j] *= f;
+  // the row's partials from its selected blocks
+  for (int i = 0; i < k; ++i) {
+    if (idx[row * k + i] < 0) continue;
+    const float* src = dq_part + int64_t(pos[row * k + i]) * D;
+#pragma unroll
+    for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const floatx4 v = *reinterpret_cast<const floatx4*>(src + 32 * mt + 8 * a + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dq[mt][4 * a + e] += v[e];
+      }
+  }
+  float* out = dQ + row * D;
+#pragma unroll
+  for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      *reinterpret_cast<floatx4*>(out + 32 * mt + 8 * a + 4 * h) =
+          floatx4{dq[mt][4 * a], dq[mt][4 * a + 1], dq[mt][4 * a + 2], dq[mt][4 * a + 3]};
+}
+
+struct BwdWs {
+  DispatchWs disp;
+  uint8_t* img_a;
+  uint8_t* img_b;
+  uint32_t* kmax;
+  uint32_t* qmax;
+  uint32_t* domax;
+  float* Drow;
+  float* dq_part;
+  int64_t n_chunks;
+  size_t bytes;
+};
+
+BwdWs bwd_ws_layout(const Shape& s, void* base) {
+  BwdWs w{};
+  const size_t es = s.in_bf16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const bool use_disp = s.k > 0 && s.nb > 0;
+  const DispatchWs dl = use_disp ? dispatch_ws_layout(s, nullptr) : DispatchWs{};
+  const size_t o_disp = take(use_disp ? dl.bytes : 0);
+  w.n_chunks = (s.n + kKeyChunk - 1) / kKeyChunk;
+  const size_t img_bytes = size_t(s.b) * s.hkv * size_t(w.n_chunks) * kKeyChunk * s.d * 2 * es;
+  const size_t o_a = take(img_bytes), o_b = take(img_bytes);
+  const size_t o_km = take(size_t(s.b) * s.hkv * 4), o_qm = take(size_t(s.b) * s.hq * 4);
+  const size_t o_dm = take(size_t(s.b) * s.hq * 4);
+  const size_t o_D = take(size_t(s.b) * s.hq * size_t(s.n) * 4);
+  const size_t o_part = take(use_disp ? size_t(dl.slots) * s.d * 4 : 0);
+  w.bytes = off;
+  if (base != nullptr) {
+    uint8_t* p = static_cast<uint8_t*>(base);
+    if (use_disp) w.disp = dispatch_ws_layout(s, p + o_disp);
+    w.img_a = p + o_a;
+    w.img_b = p + o_b;
+    w.kmax = reinterpret_cast<uint32_t*>(p + o_km);
+    w.qmax = reinterpret_cast<uint32_t*>(p + o_qm);
+    w.domax = reinterpret_cast<uint32_t*>(p + o_dm);
+    w.Drow = reinterpret_cast<float*>(p + o_D);
+    w.dq_part = reinterpret_cast<float*>(p + o_part);
+  }
+  return w;
+}
+
+template <bool F32, int D, typename OutT>
+hipError_t launch_bwd_t(const Shape& s, const void* Qv, const void* Kv, const void* Vv,
+                        const int32_t* idx, const void* Ov, const float* lse, const void* dOv,
+                        float* dQ, float* dK, float* dV, void* ws, hipStream_t st) {
+  using A = AT<F32, D>;
+  using In = typename A::In;
+  const In* Q = static_cast<const In*>(Qv);
+  const In* K = static_cast<const In*>(Kv);
+  const In* V = static_cast<const In*>(Vv);
+  const In* dO = static_cast<const In*>(dOv);
+  BwdWs w = bwd_ws_layout(s, ws);
+  const int64_t n_bkv = int64_t(s.b) * s.hkv, n_bh = int64_t(s.b) * s.hq;
+  const int64_t rows = n_bh * s.n;
+  const float scale2 = s.scale * kLog2e;
+  hipError_t e;
+  hipLaunchKernelGGL((bwd_rowdot_kernel<In, OutT>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, st,
+                     dO, static_cast<const OutT*>(Ov), w.Drow, rows, D);
+  // float16 scales: largest |K| per KV head, |Q| and |dO| per q-head
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<int32_t*>(w.kmax),
+                     n_bkv, 0);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<int32_t*>(w.qmax),
+                     n_bh, 0);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st,
+                     reinterpret_cast<int32_t*>(w.domax), n_bh, 0);
+  if (!F32) {
+    const int64_t per_head = s.n * D;
+    const unsigned gx = unsigned(std::min<int64_t>((per_head / 8 + 255) / 256, 64));
+    hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
+                       reinterpret_cast<const bf16_t*>(Kv), w.kmax, per_head);
+    hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bh)), dim3(256), 0, st,
+                       reinterpret_cast<const bf16_t*>(Qv), w.qmax, per_head);
+    hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bh)), dim3(256), 0, st,
+                       reinterpret_cast<const bf16_t*>(dOv), w.domax, per_head);
+  }
+  // image A = (K rows, V^T; the V part unused), image B = (V rows, K^T scaled)
+  hipLaunchKernelGGL((kv_image_kernel<F32, D>), dim3(unsigned(w.n_chunks), unsigned(n_bkv)),
+                     dim3(kAttnThreads), 0, st, K, V, w.kmax, w.img_a, s.n, w.n_chunks);
+  hipLaunchKernelGGL((kv_image_kernel<F32, D>), dim3(unsigned(w.n_chunks), unsigned(n_bkv)),
+                     dim3(kAttnThreads), 0, st, V, K, w.kmax, w.img_b, s.n, w.n_chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const bool use_disp = s.k > 0 && s.nb > 0;
+  if (use_disp) {
+    if ((e = launch_dispatch(s, idx, w.disp, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_task_kernel<F32, D>), dim3(unsigned(w.disp.max_tasks)),
+                       dim3(kBwdThreads), 0, st, Q, dO, lse, w.Drow, w.img_a, w.img_b, w.kmax,
+                       w.n_chunks, w.disp.tasks, w.disp.task_count, w.disp.entries, w.dq_part, s.n,
+                       s.g, s.hq, s.hkv, s.B, s.nb, scale2, s.scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((bwd_dkv_kernel<F32, D>), dim3(unsigned(n_bkv * w.n_chunks)), dim3(kBwdThreads),
+                     0, st, Q, dO, lse, w.Drow, idx, w.img_a, w.img_b, w.qmax, w.domax, w.n_chunks,
+                     use_disp ? w.disp.counts : nullptr, use_disp ? w.disp.cursor : nullptr,
+                     use_disp ? w.disp.entries : nullptr, dK, dV, s.n, s.g, s.hq, s.hkv, s.B,
+                     use_disp ? s.nb : 0, s.k, s.W, scale2, s.scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t n_tiles = (s.n * s.g + kWinTile - 1) / kWinTile;
+  hipLaunchKernelGGL((bwd_dq_window_kernel<F32, D>), dim3(unsigned(n_tiles * n_bkv)), dim3(256), 0,
+                     st, Q, dO, lse, w.Drow, idx, use_disp ? w.disp.pos : nullptr, w.dq_part,
+                     w.img_a, w.img_b, w.kmax, w.n_chunks, dQ, s.n, s.g, s.hq, s.hkv, s.B,
+                     use_disp ? s.k : 0, s.W, scale2, s.scale, n_tiles);
+  return hipGetLastError();
+}
+
+template <bool F32, int D>
+hipError_t launch_bwd_d(const Shape& s, const void* Q, const void* K, const void* V,
+                        const int32_t* idx, const void* O, const float* lse, const void* dO,
+                        float* dQ, float* dK, float* dV, void* ws, hipStream_t st) {
+  if (s.out_bf16) return launch_bwd_t<F32, D, bf16_t>(s, Q, K, V, idx, O, lse, dO, dQ, dK, dV, ws, st);
+  return launch_bwd_t<F32, D, float>(s, Q, K, V, idx, O, lse, dO, dQ, dK, dV, ws, st);
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(const Shape& s) { return bwd_ws_layout(s, nullptr).bytes; }
+
+hipError_t launch_sparse_attn_bwd(const Shape& s, const void* Q, const void* K, const void* V,
+                                  const int32_t* idx, const void* O, const float* lse,
+                                  const void* dO, float* dQ, float* dK, float* dV, void* ws,
+                                  hipStream_t st) {
+  if (s.in_bf16)
+    return s.d == 64 ? launch_bwd_d<false, 64>(s, Q, K, V, idx, O, lse, dO, dQ, dK, dV, ws, st)
+                     : launch_bwd_d<false, 128>(s, Q, K, V, idx, O, lse, dO, dQ, dK, dV, ws, st);
+  return s.d == 64 ? launch_bwd_d<true, 64>(s, Q, K, V, idx, O, lse, dO, dQ, dK, dV, ws, st)
+                   : launch_bwd_d<true, 128>(s, Q, K, V, idx, O, lse, dO, dQ, dK, dV, ws, st);
+}
+
+}  // namespace ssa

@@ -737,6 +737,56 @@ hipError_t launch_attn_d(const Shape& s, const void* Q, const void* K, const voi
 
 size_t attn_workspace_bytes(const Shape& s) { return attn_ws_layout(s, nullptr).bytes; }
 
+DispatchWs dispatch_ws_layout(const Shape& s, void* base) {
+  DispatchWs w{};
+  const int64_t nseg = int64_t(s.b) * s.hkv * s.nb;
+  const int64_t pairs = int64_t(s.b) * s.hq * s.n * s.k;
+  w.max_tasks = (pairs + kTaskRows - 1) / kTaskRows + nseg;
+  w.slots = w.max_tasks * kTaskRows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t o_counts = take(size_t(nseg) * 4), o_cursor = take(size_t(nseg) * 4);
+  const size_t o_tc = take(4), o_tasks = take(size_t(w.max_tasks) * 16);
+  const size_t o_entries = take(size_t(w.slots) * 4), o_pos = take(size_t(pairs) * 4);
+  w.bytes = off;
+  if (base != nullptr) {
+    uint8_t* p = static_cast<uint8_t*>(base);
+    w.counts = reinterpret_cast<int32_t*>(p + o_counts);
+    w.cursor = reinterpret_cast<int32_t*>(p + o_cursor);
+    w.task_count = reinterpret_cast<int32_t*>(p + o_tc);
+    w.tasks = reinterpret_cast<int4*>(p + o_tasks);
+    w.entries = reinterpret_cast<uint32_t*>(p + o_entries);
+    w.pos = reinterpret_cast<int32_t*>(p + o_pos);
+  }
+  return w;
+}
+
+hipError_t launch_dispatch(const Shape& s, const int32_t* idx, const DispatchWs& w, hipStream_t st) {
+  const int64_t n_bkv = int64_t(s.b) * s.hkv;
+  const int64_t nseg = n_bkv * s.nb;
+  hipError_t e;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((nseg + 255) / 256, 4096))),
+                     dim3(256), 0, st, w.counts, nseg, 0);
+  const dim3 hgrid(unsigned((s.n + kHistTokens - 1) / kHistTokens), unsigned(n_bkv));
+  const size_t hshm = size_t(s.nb) * 4;
+  for (const void* f : {reinterpret_cast<const void*>(dispatch_kernel<false>),
+                        reinterpret_cast<const void*>(dispatch_kernel<true>)})
+    if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(hshm))) !=
+        hipSuccess)
+      return e;
+  hipLaunchKernelGGL(dispatch_kernel<false>, hgrid, dim3(256), hshm, st, idx, w.counts,
+                     (uint32_t*)nullptr, (int32_t*)nullptr, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
+  hipLaunchKernelGGL(scan_tasks_kernel, dim3(1), dim3(kScanThreads), 0, st, w.counts, w.cursor,
+                     w.tasks, w.task_count, nseg);
+  hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(256), hshm, st, idx, w.cursor, w.entries,
+                     w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
+  return hipGetLastError();
+}
+
 int64_t attn_entry_slots(const Shape& s) {
   return attn_ws_layout(s, nullptr).max_tasks * kTaskRows;
 }

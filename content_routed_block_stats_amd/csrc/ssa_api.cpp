@@ -174,6 +174,38 @@ ssa_status ssa_tile_attn_fwd(const ssa_params* p, const void* Q, const void* K, 
                   "ssa_tile_attn_fwd");
 }
 
+ssa_status ssa_sparse_attn_bwd(const ssa_params* p, const void* Q, const void* K, const void* V,
+                               const int32_t* idx, const void* O, const float* lse, const void* dO,
+                               float* dQ, float* dK, float* dV, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  ssa::Shape s;
+  ssa_status st = check_params(p, &s);
+  if (st != SSA_OK) return st;
+  SSA_NONNULL(Q);
+  SSA_NONNULL(K);
+  SSA_NONNULL(V);
+  SSA_NONNULL(O);
+  SSA_NONNULL(lse);
+  SSA_NONNULL(dO);
+  SSA_NONNULL(dQ);
+  SSA_NONNULL(dK);
+  SSA_NONNULL(dV);
+  if (s.k > 0) SSA_NONNULL(idx);
+  if (s.k > 0 && s.nb > kMaxBlocksAttn)
+    return fail(SSA_ERR_UNSUPPORTED, "%lld blocks per sequence exceed %lld", (long long)s.nb,
+                (long long)kMaxBlocksAttn);
+  if (s.k > 0 && ssa::attn_entry_slots(s) >= (int64_t(1) << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "too many (row, block) selections for 32-bit positions");
+  const int64_t chunks = (s.n + 63) / 64;
+  if (int64_t(s.b) * s.hkv * chunks >= (int64_t(1) << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "too many key chunks for one launch");
+  st = check_ws(ssa::attn_bwd_workspace_bytes(s), workspace, workspace_bytes);
+  if (st != SSA_OK) return st;
+  return from_hip(ssa::launch_sparse_attn_bwd(s, Q, K, V, idx, O, lse, dO, dQ, dK, dV, workspace,
+                                              (hipStream_t)stream),
+                  "ssa_sparse_attn_bwd");
+}
+
 ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes) {
   ssa::Shape s;
   ssa_status st = check_params(p, &s);
@@ -185,6 +217,7 @@ ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes) {
     case SSA_OP_DECODE: *bytes = ssa::decode_workspace_bytes(s); break;
     case SSA_OP_ROUTE_TILES: *bytes = ssa::route_tiles_workspace_bytes(s); break;
     case SSA_OP_TILE_ATTN: *bytes = ssa::tile_attn_workspace_bytes(s); break;
+    case SSA_OP_ATTN_BWD: *bytes = ssa::attn_bwd_workspace_bytes(s); break;
     default: return fail(SSA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
   return ok();

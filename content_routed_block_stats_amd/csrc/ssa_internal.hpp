@@ -60,6 +60,33 @@ int64_t attn_entry_slots(const Shape& s);
 hipError_t launch_sparse_attn(const Shape& s, const void* Q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse, void* ws, hipStream_t st);
 
+// The block-major dispatch of the sparse attention (a counting sort of the
+// (row, slot) selections by (sequence, KV head, block)), for other passes over
+// the same selections.  Segment s = (b * hkv + kv) * nb + c holds counts[s]
+// entries, at [cursor[s] - counts[s], cursor[s]) after the dispatch; task j
+// = {segment, first entry j * 256, rows, 0} for j < task_count[0]; entry =
+// (t * g + j) << 5 | slot; pos[row * k + slot] = the entry's index.
+struct DispatchWs {
+  int32_t* counts;
+  int32_t* cursor;
+  int32_t* task_count;
+  int4* tasks;
+  uint32_t* entries;
+  int32_t* pos;
+  int64_t max_tasks;
+  int64_t slots;
+  size_t bytes;
+};
+DispatchWs dispatch_ws_layout(const Shape& s, void* base);
+hipError_t launch_dispatch(const Shape& s, const int32_t* idx, const DispatchWs& w, hipStream_t st);
+
+// backward of the sparse attention over fixed selections (prefill)
+size_t attn_bwd_workspace_bytes(const Shape& s);
+hipError_t launch_sparse_attn_bwd(const Shape& s, const void* Q, const void* K, const void* V,
+                                  const int32_t* idx, const void* O, const float* lse,
+                                  const void* dO, float* dQ, float* dK, float* dV, void* ws,
+                                  hipStream_t st);
+
 // decode step
 size_t decode_workspace_bytes(const Shape& s);
 hipError_t launch_decode_step(const Shape& s, const void* q, const void* k_new, const void* v_new,

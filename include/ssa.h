@@ -54,7 +54,8 @@ typedef enum ssa_op {
   SSA_OP_ATTN = 2,    /* workspace of ssa_sparse_attn_fwd */
   SSA_OP_DECODE = 3,  /* workspace of ssa_decode_step */
   SSA_OP_ROUTE_TILES = 4,  /* workspace of ssa_route_tiles */
-  SSA_OP_TILE_ATTN = 5     /* workspace of ssa_tile_attn_fwd */
+  SSA_OP_TILE_ATTN = 5,    /* workspace of ssa_tile_attn_fwd */
+  SSA_OP_ATTN_BWD = 6      /* workspace of ssa_sparse_attn_bwd */
 } ssa_op;
 
 /* Shapes and method parameters.  Limits checked by every call:
@@ -202,6 +203,30 @@ ssa_status ssa_tile_attn_fwd(const ssa_params* p, const void* Q, const void* K, 
 ssa_status ssa_sparse_attn_fwd(const ssa_params* p, const void* Q, const void* K,
                                const void* V, const int32_t* idx, void* O, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of the sparse attention over fixed selections (training through
+ * the layer: the write-up's module list trains SSA models and its "Selected
+ * results" adapt a dense model swapped to SSA; the selection is discrete and
+ * is held fixed).  With p_j = exp(scale q.k_j - LSE) over S(t) (the forward's
+ * key set and LSE), D = dO . O, dP_j = dO . v_j, dS_j = p_j (dP_j - D):
+ *   dQ_t = scale sum_j dS_j k_j;  dK_j = scale sum_t dS_j q_t;  dV_j = sum_t p_j dO_t
+ * (dK, dV summed over every row of the KV head's group that attends to j).
+ *   Q, K, V, idx  as for ssa_sparse_attn_fwd
+ *   O     [b, Hq, n, d]  out_dtype, lse [b, Hq, n] float32: that call's outputs
+ *   dO    [b, Hq, n, d]  in_dtype, the upstream gradient
+ *   dQ    [b, Hq, n, d], dK, dV [b, Hkv, n, d]  float32, written (not added to)
+ *   workspace >= ssa_workspace_size(p, SSA_OP_ATTN_BWD) bytes
+ * Limits: those of ssa_sparse_attn_fwd; b * Hkv * ceil(n/64) below 2^31.
+ * Arithmetic: q.k and dO.v on MFMA as in the forward (bf16 products exact);
+ * K^T, Q^T, dO^T, p and dS enter their products as float16 after scaling by
+ * an exact power of two (float32 MFMA for float32 inputs); float32
+ * accumulation.  dQ is bitwise repeatable; dK and dV add a block's rows in
+ * the dispatch's order, which follows atomic reservations, so repeated calls
+ * agree to float32 rounding, not bit for bit. */
+ssa_status ssa_sparse_attn_bwd(const ssa_params* p, const void* Q, const void* K, const void* V,
+                               const int32_t* idx, const void* O, const float* lse, const void* dO,
+                               float* dQ, float* dK, float* dV, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* One decode step per sequence (write-up, module table: the decode path routes
  * and attends one new query per step against the cache).  With
