@@ -40,7 +40,8 @@ namespace ssa {
 namespace {
 
 constexpr int kBwdThreads = 512;     // 8 waves
-constexpr int kKvRows = 128;         // rows staged per iteration of the key pass
+constexpr int kDkvThreads = 256;     // key pass: 4 waves, two workgroups per CU
+constexpr int kDkvRows = 64;         // rows staged per iteration of the key pass
 constexpr int kWinTile = 128;        // rows per tile of the window pass (4 waves x 32)
 
 // ------------------------------------------------------------------ rowdot --
@@ -187,37 +188,46 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_task_kernel(
 }
 
 // --------------------------------------------------------------- dkv_chunk --
-// One workgroup (8 waves: key half kh = wave % 2, row group rg = wave / 2) per
-// 64-key chunk of one (sequence, KV head).  Rows are staged kKvRows at a time
-// (Q and dO rows as they are, plus per row the log2-domain LSE, D, position
-// and mode: 0 = every key counts, 1 = window keys (t - W, t], 2 = none).
+// One workgroup (4 waves: key half kh = wave % 2, row group rg = wave / 2) per
+// 64-key chunk of one (sequence, KV head); two workgroups share a CU.  Rows
+// are staged kDkvRows at a time: Q and dO rows as they are, and per row its
+// index, position, log2-domain LSE, D and mode (0 = every key counts, 1 =
+// window keys (t - W, t], 2 = none).  The next rows' information is fetched
+// while the current rows are computed, so an iteration waits for one gather.
 template <bool F32, int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(
+__global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Drow, const int32_t* __restrict__ idx,
     const uint8_t* __restrict__ img_a, const uint8_t* __restrict__ img_b,
     const uint32_t* __restrict__ qmax, const uint32_t* __restrict__ domax, int64_t n_chunks,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ cursor,
     const uint32_t* __restrict__ entries, float* __restrict__ dK, float* __restrict__ dV, int64_t n,
-    int g, int hq, int hkv, int B, int64_t nb, int k, int W, float scale2, float scale) {
+    int g, int hq, int hkv, int B, int64_t nb, int k, int W, float scale2, float scale,
+    int64_t n_work) {
   using A = AT<F32, D>;
   using In = typename A::In;
   using Frag = typename A::Frag;
   constexpr int ES = A::ES;
   constexpr int ROWB = D * ES;
-  constexpr int ROWS = (F32 && D == 128) ? kKvRows / 2 : kKvRows;   // LDS: float32, d = 128
-  constexpr int RG = ROWS / 32;                                      // row groups in use
+  constexpr int ROWS = kDkvRows;
   __shared__ __attribute__((aligned(1024))) uint8_t img[2 * A::KBYTES];   // K rows, V rows
-  __shared__ __attribute__((aligned(16))) uint8_t rq[ROWS * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t rdo[ROWS * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t rbuf[2 * ROWS * ROWB];  // Q rows, dO rows
   __shared__ float rl2[ROWS], rd[ROWS];
-  __shared__ int64_t rt[ROWS];
+  __shared__ int64_t rrow[ROWS], rpos[ROWS];
   __shared__ int32_t rmode[ROWS];
-  static_assert(ROWS * ROWB >= kKeyChunk * D * 4, "reduction buffer");
+  static_assert(2 * ROWS * ROWB >= kKeyChunk * D * 4, "reduction buffer");
+  uint8_t* rq = rbuf;
+  uint8_t* rdo = rbuf + ROWS * ROWB;
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int kh = wave % 2, rg = wave / 2;
-  const int64_t ch = blockIdx.x % n_chunks, bkv = blockIdx.x / n_chunks;
+  // consecutive work items (the chunks of one block, which stream the same
+  // selected rows) go to one XCD (workgroup i runs on XCD i % 8), so the
+  // repeated row gathers hit that XCD's L2
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t wi = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (wi >= n_work) return;
+  const int64_t ch = wi % n_chunks, bkv = wi / n_chunks;
   const int64_t b = bkv / hkv, kv = bkv % hkv;
   const int64_t key0 = ch * kKeyChunk;
   const int64_t c = key0 / B;
@@ -243,8 +253,45 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(
   }
   const float sq = ldexpf(1.f, -eq), sdo = ldexpf(1.f, -edo);
 
-  dma_copy(img, img_a + (bkv * n_chunks + ch) * A::CHUNK, A::KBYTES, tid, kBwdThreads);
-  dma_copy(img + A::KBYTES, img_b + (bkv * n_chunks + ch) * A::CHUNK, A::KBYTES, tid, kBwdThreads);
+  // row i of this work item: the block's selected rows, then the window rows
+  struct Info {
+    int64_t row, pos;
+    float l2, dd;
+    int mode;
+  };
+  auto info = [&](int64_t i) {
+    Info r{-1, -1, 0.f, 0.f, 2};
+    if (i < sel_cnt) {
+      const uint32_t en = entries[sel_start + i];
+      const int64_t rho = en >> 5;
+      r.pos = rho / g;
+      r.row = (b * hq + kv * g + rho % g) * n + r.pos;
+      r.mode = 0;
+    } else if (i < total) {
+      const int64_t w = i - sel_cnt;
+      r.pos = key0 + w / g;
+      r.row = (b * hq + kv * g + w % g) * n + r.pos;
+      bool sel = false;
+      for (int q = 0; q < k; ++q) sel |= idx[r.row * k + q] == int32_t(c);
+      r.mode = sel ? 2 : 1;
+    }
+    if (r.row >= 0) {
+      r.l2 = lse[r.row] * kLog2e;
+      r.dd = Drow[r.row];
+    }
+    return r;
+  };
+  auto put = [&](const Info& r) {
+    rrow[tid] = r.mode == 2 ? -1 : r.row;
+    rpos[tid] = r.pos;
+    rl2[tid] = r.l2;
+    rd[tid] = r.dd;
+    rmode[tid] = r.mode;
+  };
+
+  dma_copy(img, img_a + (bkv * n_chunks + ch) * A::CHUNK, A::KBYTES, tid, kDkvThreads);
+  dma_copy(img + A::KBYTES, img_b + (bkv * n_chunks + ch) * A::CHUNK, A::KBYTES, tid, kDkvThreads);
+  if (tid < ROWS) put(info(tid));
 
   floatx16 dk[A::MTD], dv[A::MTD];
 #pragma unroll
@@ -254,50 +301,27 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(
   const int64_t my_key = key0 + 32 * kh + ln;
 
   for (int64_t i0 = 0; i0 < total; i0 += ROWS) {
-    // stage rows [i0, i0 + ROWS): the selected rows first, then the window rows
-    if (tid < ROWS) {
-      const int64_t i = i0 + tid;
-      int mode = 2;
-      int64_t t = 0, row = -1;
-      if (i < sel_cnt) {
-        const uint32_t en = entries[sel_start + i];
-        const int64_t rho = en >> 5, jg = rho % g;
-        t = rho / g;
-        row = (b * hq + kv * g + jg) * n + t;
-        mode = 0;
-      } else if (i < total) {
-        const int64_t w = i - sel_cnt, jg = w % g;
-        t = key0 + w / g;
-        row = (b * hq + kv * g + jg) * n + t;
-        bool sel = false;
-        for (int q = 0; q < k; ++q) sel |= idx[row * k + q] == int32_t(c);
-        mode = sel ? 2 : 1;
-      }
-      rt[tid] = row;            // the row index first, the position below
-      rl2[tid] = row >= 0 ? lse[row] * kLog2e : 0.f;
-      rd[tid] = row >= 0 ? Drow[row] : 0.f;
-      rmode[tid] = mode;
-      (void)t;
-    }
-    __syncthreads();
+    __syncthreads();   // this iteration's row information is in LDS
     constexpr int PIECES = ROWB / 16;
-    for (int w = tid; w < ROWS * PIECES; w += kBwdThreads) {
+    for (int w = tid; w < ROWS * PIECES; w += kDkvThreads) {
       const int rr = w / PIECES, pc = w % PIECES;
-      const int64_t row = rt[rr];
+      const int64_t row = rrow[rr];
       u32x4 vq = {0u, 0u, 0u, 0u}, vd = vq;
-      if (row >= 0 && rmode[rr] != 2) {
+      if (row >= 0) {
         vq = reinterpret_cast<const u32x4*>(Q + row * D)[pc];
         vd = reinterpret_cast<const u32x4*>(dO + row * D)[pc];
       }
       reinterpret_cast<u32x4*>(rq + rr * ROWB)[pc] = vq;
       reinterpret_cast<u32x4*>(rdo + rr * ROWB)[pc] = vd;
     }
-    __syncthreads();
-    if (tid < ROWS) rt[tid] = rt[tid] >= 0 ? rt[tid] % n : -1;   // position t of the row
-    __syncthreads();
+    __syncthreads();   // rows staged
+    // the next rows' information, fetched while these rows are computed (the
+    // loads go out after the barrier above, whose fence would wait for them)
+    Info nx{-1, -1, 0.f, 0.f, 2};
+    if (tid < ROWS && i0 + ROWS < total) nx = info(i0 + ROWS + tid);
 
     const int r0 = 32 * rg;
-    if (rg < RG && i0 + r0 < total) {
+    if (i0 + r0 < total) {
       // S = Q K^T and dP = dO V^T for this wave's 32 rows x 32 keys (lanes on keys)
       floatx16 sacc, pacc;
 #pragma unroll
@@ -317,7 +341,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(
       for (int j = 0; j < 16; ++j) {
         const int rr = r0 + 8 * (j / 4) + 4 * h + j % 4;
         const int mode = rmode[rr];
-        const int64_t t = rt[rr];
+        const int64_t t = rpos[rr];
         const bool on = my_key < n && (mode == 0 || (mode == 1 && my_key <= t && my_key > t - W));
         const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[j], scale2, -rl2[rr])) : 0.f;
         sacc[j] = p;
@@ -348,14 +372,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(
         }
       }
     }
-    __syncthreads();
+    __syncthreads();   // done with this iteration's rows and information
+    if (tid < ROWS) put(nx);
   }
+  __syncthreads();
 
-  // the row groups' partial sums, added in LDS in a fixed order (float32,
+  // the two row groups' partial sums, added in LDS in a fixed order (float32,
   // 64 keys x D): the result does not depend on scheduling
-  float* red = reinterpret_cast<float*>(rq);   // ROWS * ROWB >= 64 * D * 4 bytes
+  float* red = reinterpret_cast<float*>(rbuf);
   for (int pass = 0; pass < 2; ++pass) {
-    for (int round = 0; round < RG; ++round) {
+    for (int round = 0; round < 2; ++round) {
       if (rg == round) {
 #pragma unroll
         for (int mt = 0; mt < A::MTD; ++mt)
@@ -371,7 +397,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(
     }
     const float f = pass == 0 ? ldexpf(scale, eq) : ldexpf(1.f, edo);
     float* dst = (pass == 0 ? dK : dV) + (bkv * n + key0) * D;
-    for (int w = tid; w < kKeyChunk * D; w += kBwdThreads)
+    for (int w = tid; w < kKeyChunk * D; w += kDkvThreads)
       if (key0 + w / D < n) dst[w] = red[w] * f;
     __syncthreads();
   }
@@ -610,11 +636,13 @@ hipError_t launch_bwd_t(const Shape& s, const void* Qv, const void* Kv, const vo
                        s.g, s.hq, s.hkv, s.B, s.nb, scale2, s.scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_dkv_kernel<F32, D>), dim3(unsigned(n_bkv * w.n_chunks)), dim3(kBwdThreads),
-                     0, st, Q, dO, lse, w.Drow, idx, w.img_a, w.img_b, w.qmax, w.domax, w.n_chunks,
-                     use_disp ? w.disp.counts : nullptr, use_disp ? w.disp.cursor : nullptr,
-                     use_disp ? w.disp.entries : nullptr, dK, dV, s.n, s.g, s.hq, s.hkv, s.B,
-                     use_disp ? s.nb : 0, s.k, s.W, scale2, s.scale);
+  const int64_t n_kv_work = n_bkv * w.n_chunks;
+  hipLaunchKernelGGL((bwd_dkv_kernel<F32, D>), dim3(unsigned((n_kv_work + 7) / 8 * 8)),
+                     dim3(kDkvThreads), 0, st, Q, dO, lse, w.Drow, idx, w.img_a, w.img_b, w.qmax,
+                     w.domax, w.n_chunks, use_disp ? w.disp.counts : nullptr,
+                     use_disp ? w.disp.cursor : nullptr, use_disp ? w.disp.entries : nullptr, dK,
+                     dV, s.n, s.g, s.hq, s.hkv, s.B, use_disp ? s.nb : 0, s.k, s.W, scale2, s.scale,
+                     n_kv_work);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t n_tiles = (s.n * s.g + kWinTile - 1) / kWinTile;
   hipLaunchKernelGGL((bwd_dq_window_kernel<F32, D>), dim3(unsigned(n_tiles * n_bkv)), dim3(256), 0,
