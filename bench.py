@@ -10,7 +10,8 @@ ssa_sparse_attn_fwd.  The default workload is the n = 131072 GQA prefill
 (32 q-heads / 8 KV heads, d = 128, bf16, B = 256, k = 16, W = 256, beta = 2).
 Prints ONE JSON line: query-tokens/s, per-stage times from HIP events on the
 launch stream, the routing kernel against the bf16 MFMA roofline, the gather
-against the HBM roofline, the query-tile-shared variant (ssa_route_tiles +
+against the HBM roofline, the backward through the attention (ssa_sparse_attn_bwd on the step's
+selections, against the MFMA roofline), the query-tile-shared variant (ssa_route_tiles +
 ssa_tile_attn_fwd on the same workload: its step time, planted recall and the
 tile attention against the MFMA roofline), the exact tempered router
 (ssa_route_tempered, same workload and beta, outside the step) against the
@@ -211,6 +212,27 @@ def tile_attn_flops(wl, idx_t) -> float:
             keys = valid.sum(-1) * B + win - overlap.sum(-1)
             total += float(keys.sum())
     return 4.0 * d * total
+
+
+def attn_pairs(wl, idx) -> float:
+    """(row, key) pairs of S(t) summed over all rows, on the actual selections:
+    the selected blocks' keys plus the window keys outside them."""
+    import torch
+
+    n, B, W = wl.seq_len, wl.block, wl.window
+    dev = idx.device
+    t = torch.arange(n, device=dev)
+    win = torch.clamp(t + 1, max=W).to(torch.float64)
+    total = 0.0
+    for b in range(idx.shape[0]):
+        for h in range(idx.shape[1]):
+            sel = idx[b, h].to(torch.int64)                       # [n, k]
+            valid = sel >= 0
+            lo = torch.maximum(sel * B, (t - W + 1)[:, None])
+            hi = torch.minimum(sel * B + B - 1, t[:, None])
+            overlap = torch.clamp(hi - lo + 1, min=0) * valid
+            total += float((valid.sum(-1) * B + win - overlap.sum(-1)).sum())
+    return total
 
 
 def recall_sweep(wl, seed: int, betas: list[float]) -> dict:
@@ -445,6 +467,35 @@ def main() -> int:
                      "algorithmic_flops_per_launch": ta_fl},
         "steps": treps}
     del ws_rt, ws_ta, idx_t
+
+    # the backward through the attention with the step's selections (training);
+    # the tile-shared step above overwrote O and lse, so the forward runs again
+    ssa.ssa_sparse_attn_fwd(Q, K, V, idx, block_size=wl.block, window=wl.window, scale=wl.scale,
+                            out=O, lse=lse, workspace=ws_a)
+    dO = torch.randn(Q.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
+                     dtype=torch.float32).to(Q.dtype)
+    ws_b = torch.empty(ssa.ssa_workspace_size(p, 6), dtype=torch.uint8, device=dev)
+    bwd = lambda: ssa.ssa_sparse_attn_bwd(Q, K, V, idx, O, lse, dO, block_size=wl.block,
+                                          window=wl.window, scale=wl.scale, workspace=ws_b)
+    bwd()
+    torch.cuda.synchronize()
+    tb0, tb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    breps = 2
+    tb0.record()
+    for _ in range(breps):
+        bwd()
+    tb1.record()
+    torch.cuda.synchronize()
+    t_bwd = tb0.elapsed_time(tb1) / breps
+    pairs = attn_pairs(wl, idx)
+    bwd_fl = 14.0 * wl.head_dim * pairs
+    res["backward"] = {"what": "dQ, dK, dV through the attention over the step's selections",
+                       "ms": round(t_bwd, 3), "ms_vs_forward_attention": round(t_bwd / t_attn, 2),
+                       "bound": "mfma", "achieved": round(bwd_fl / (t_bwd * 1e-3) / 1e12, 1),
+                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(bwd_fl / (t_bwd * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "algorithmic_flops_per_launch": bwd_fl, "reps": breps}
+    del ws_b, dO
 
     # the exact tempered score (same workload and beta), outside the step
     ssa.ssa_route_tempered(Q, K, block_size=wl.block, top_k=wl.top_k, beta=wl.beta, idx=idx)
