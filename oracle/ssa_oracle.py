@@ -203,6 +203,82 @@ def tile_prefill_row(q, K, V, tile_idx: np.ndarray, p: Params, t: int) -> dict:
     return dict(S=S, O=O, lse=lse)
 
 
+# -- hierarchical routing: the exact top-k by branch and bound over groups ------
+#
+# The write-up's module list pairs the flat router with branch-and-bound exact
+# selection under an admissible bound and a tree router with a recursive
+# radius (Barnes-Hut style), and "Selected results" report lossless
+# branch-and-bound selection costs as a fraction of keys.  Reading: groups of
+# m consecutive blocks carry a summary from which an upper bound on every
+# member's routing score follows; groups are visited in decreasing bound order
+# and skipped when their bound is strictly below the running k-th best score,
+# so the selection is exactly the flat top-k and only the cost changes.
+#   UB_G(q) = q.mu_G + ||q|| R_G + (beta/2) (q^T S_G q + lam_G ||q||^2)   (beta >= 0)
+# with mu_G the mean of the members' mu_c, R_G = max ||mu_c - mu_G||, S_G the
+# mean of their Sigma_c and lam_G = max (tr (Sigma_c - S_G)^4)^(1/4), which is
+# at least the spectral norm ||Sigma_c - S_G||_2: then q.mu_c <= q.mu_G +
+# ||q|| R_G (Cauchy-Schwarz) and q^T Sigma_c q <= q^T S_G q + lam_G ||q||^2.
+
+def group_summaries(mu: np.ndarray, sigma: np.ndarray, m: int) -> dict:
+    """Summaries of the groups of m consecutive blocks (the last may be partial)."""
+    mu, sigma = as_f64(mu), as_f64(sigma)
+    nb, d = mu.shape
+    G = -(-nb // m)
+    out = dict(mu=np.zeros((G, d)), R=np.zeros(G), S=np.zeros((G, d, d)), lam=np.zeros(G))
+    for gi in range(G):
+        c0, c1 = gi * m, min(nb, (gi + 1) * m)
+        mg = mu[c0:c1].mean(0)
+        Sg = sigma[c0:c1].mean(0)
+        out["mu"][gi] = mg
+        out["S"][gi] = Sg
+        out["R"][gi] = max(np.linalg.norm(mu[c] - mg) for c in range(c0, c1))
+        lam = 0.0
+        for c in range(c0, c1):
+            A = sigma[c] - Sg
+            A2 = A @ A
+            lam = max(lam, float(np.sum(A2 * A2)) ** 0.25)      # (tr A^4)^(1/4)
+        out["lam"][gi] = lam
+    return out
+
+
+def group_bound(q: np.ndarray, gs: dict, beta: float) -> np.ndarray:
+    """UB_G(q) for every group (beta >= 0)."""
+    q = as_f64(q)
+    nq = float(np.linalg.norm(q))
+    quad = np.einsum("i,gij,j->g", q, gs["S"], q)
+    return gs["mu"] @ q + nq * gs["R"] + 0.5 * beta * (quad + gs["lam"] * nq * nq)
+
+
+def route_hier(q: np.ndarray, mu: np.ndarray, sigma: np.ndarray, gs: dict, m: int, k: int,
+               beta: float, C: int) -> dict:
+    """Exact top-k of r_c(q) over the blocks c < C by branch and bound over the
+    groups of m blocks: returns idx (as select_topk) and the number of blocks
+    whose score was evaluated."""
+    if beta < 0:
+        raise ValueError("the group bound needs beta >= 0")
+    ub = group_bound(q, gs, beta)
+    G = -(-C // m)
+    order = sorted(range(G), key=lambda gi: (-ub[gi], gi))
+    scores: dict[int, float] = {}
+    for gi in order:
+        if len(scores) >= k > 0:
+            tau = sorted(scores.values(), reverse=True)[k - 1]
+            if ub[gi] < tau:
+                continue
+        elif k == 0:
+            break
+        blocks = list(range(gi * m, min(C, (gi + 1) * m)))
+        r = route_scores(q, as_f64(mu)[blocks], as_f64(sigma)[blocks], beta)
+        scores.update(zip(blocks, r.tolist()))
+    cs = np.array(sorted(scores), dtype=np.int64)
+    r_eval = np.array([scores[c] for c in cs])
+    sel, _, _ = select_topk(r_eval, k)
+    idx = np.full(k, -1, dtype=np.int32)
+    chosen = np.sort(cs[sel[sel >= 0]]) if cs.size else np.zeros(0, dtype=np.int64)
+    idx[:chosen.size] = chosen
+    return dict(idx=idx, evaluated=len(scores))
+
+
 # -- step 3: top-k selection ---------------------------------------------------
 
 def select_topk(r: np.ndarray, k: int) -> tuple[np.ndarray, float, float]:

@@ -29,7 +29,8 @@ def _impl(**overrides):
         routable_blocks=OR.routable_blocks, key_set=OR.key_set, attend=OR.attend,
         dropped_mass=OR.dropped_mass, recovery_weight=OR.recovery_weight,
         tempered_scores=OR.tempered_scores, tile_routable_blocks=OR.tile_routable_blocks,
-        tile_scores=OR.tile_scores, attend_backward=OR.attend_backward)
+        tile_scores=OR.tile_scores, attend_backward=OR.attend_backward,
+        group_summaries=OR.group_summaries, group_bound=OR.group_bound, route_hier=OR.route_hier)
     for k, v in overrides.items():
         setattr(ns, k, v)
 
@@ -596,13 +597,96 @@ def check_backward_dense(ns, seed=17):
     np.testing.assert_allclose(dV, Vt.grad[0, 0].numpy(), rtol=1e-10, atol=1e-12)
 
 
+def _clustered(rng, nb, m, B, d, group_std=3.0, block_std=0.1, noise=0.3):
+    G = -(-nb // m)
+    gc = rng.normal(size=(G, d)) * group_std
+    bc = np.repeat(gc, m, 0)[:nb] + rng.normal(size=(nb, d)) * block_std
+    return np.repeat(bc, B, 0) + rng.normal(size=(nb * B, d)) * noise
+
+
+def check_group_bound_admissible(ns, seed=18):
+    """UB_G(q) >= every member's score (brute force over random queries, random
+    and clustered keys, beta in {0, 0.5, 2, 8}), and lam_G >= the spectral norm
+    of every member's Sigma_c - S_G (NumPy eigvalsh)."""
+    rng = np.random.default_rng(seed)
+    for geo in ("random", "clustered"):
+        B, d, nb, m = 6, 5, 22, 4
+        K = rng.normal(size=(nb * B, d)) if geo == "random" else _clustered(rng, nb, m, B, d)
+        mu, sigma = ns.block_stats(K, B)
+        gs = ns.group_summaries(mu, sigma, m)
+        for gi in range(gs["mu"].shape[0]):
+            for c in range(gi * m, min(nb, (gi + 1) * m)):
+                spec = np.abs(np.linalg.eigvalsh(sigma[c] - gs["S"][gi])).max()
+                assert gs["lam"][gi] >= spec - 1e-12
+                assert np.linalg.norm(mu[c] - gs["mu"][gi]) <= gs["R"][gi] + 1e-12
+        for beta in (0.0, 0.5, 2.0, 8.0):
+            for _ in range(40):
+                q = rng.normal(size=d) * rng.uniform(0.2, 3.0)
+                ub = ns.group_bound(q, gs, beta)
+                r = OR.route_scores(q, mu, sigma, beta)
+                for gi in range(gs["mu"].shape[0]):
+                    assert ub[gi] >= r[gi * m:(gi + 1) * m].max() - 1e-9, (geo, beta, gi)
+
+
+def check_route_hier_exact(ns, seed=19):
+    """Branch and bound returns the flat top-k (select_topk over all routable
+    scores) for random and clustered keys, every k, partial routable ranges;
+    on the clustered keys it evaluates fewer blocks than exist."""
+    rng = np.random.default_rng(seed)
+    B, d, nb, m = 4, 6, 40, 5
+    pruned = 0
+    for geo in ("random", "clustered"):
+        K = rng.normal(size=(nb * B, d)) if geo == "random" else _clustered(rng, nb, m, B, d)
+        mu, sigma = ns.block_stats(K, B)
+        gs = ns.group_summaries(mu, sigma, m)
+        for trial in range(60):
+            q = rng.normal(size=d)
+            k = int(rng.integers(0, 9))
+            C = int(rng.integers(0, nb + 1))
+            out = ns.route_hier(q, mu, sigma, gs, m, k, 2.0, C)
+            want, _, _ = OR.select_topk(OR.route_scores(q, mu[:C], sigma[:C], 2.0), k)
+            assert out["idx"].tolist() == want.tolist(), (geo, k, C, out, want)
+            assert out["evaluated"] <= C
+            if geo == "clustered" and k > 0 and out["evaluated"] < C:
+                pruned += 1
+    assert pruned > 20, pruned
+
+
+def check_route_hier_hand(ns):
+    """Hand-worked pruning: groups of identical blocks (R = lam = 0, so the bound
+    is the score).  Scores (q = e_1, beta = 0): group 0 blocks 1, group 1
+    blocks 5, group 2 blocks 3, m = 2.  k = 2 visits group 1 (bound 5, two
+    blocks evaluated), then prunes group 2 (3 < 5) and group 0 (1 < 5).  Then a
+    tie: group 0 blocks 2 (bound 2), group 1 blocks {3, 2} (bound 3 + radius);
+    with k = 2 the second pick is block 0 (score 2, lower index than block 3),
+    which a prune on equality (2 <= tau = 2) would lose."""
+    d, B = 3, 2
+    def blocks(vals):
+        K = np.zeros((len(vals) * B, d))
+        for c, v in enumerate(vals):
+            K[c * B:(c + 1) * B, 0] = v
+        return K
+    q = np.array([1.0, 0.0, 0.0])
+    K = blocks([1, 1, 5, 5, 3, 3])
+    mu, sigma = ns.block_stats(K, B)
+    gs = ns.group_summaries(mu, sigma, 2)
+    out = ns.route_hier(q, mu, sigma, gs, 2, 2, 0.0, 6)
+    assert out["idx"].tolist() == [2, 3] and out["evaluated"] == 2, out
+    K = blocks([2, 2, 3, 2])
+    mu, sigma = ns.block_stats(K, B)
+    gs = ns.group_summaries(mu, sigma, 2)
+    out = ns.route_hier(q, mu, sigma, gs, 2, 2, 0.0, 4)
+    assert out["idx"].tolist() == [0, 2], out
+
+
 CHECKS = [check_golden, check_stats_vs_library, check_scores_two_ways, check_centroid_limit,
           check_topk_brute, check_dense_reduction, check_window_only, check_gather_equals_mask,
           check_recovery_law, check_recovery_law_pipeline, check_dropped_mass,
           check_decode_equals_prefill, check_invariances, check_tempered_closed_form,
           check_tempered_limits, check_tile_scores_moments, check_tile_select_brute,
           check_tile_single_row, check_tile_dense_reduction, check_backward_finite_differences,
-          check_backward_autograd, check_backward_dense]
+          check_backward_autograd, check_backward_dense, check_group_bound_admissible,
+          check_route_hier_exact, check_route_hier_hand]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda f: f.__name__)
@@ -751,6 +835,46 @@ def _mut_bwd_dq_uses_v(q, K, V, S, scale, dO):
     return OR.attend_backward(q, V, V, S, scale, dO)[0], dK, dV
 
 
+def _mut_bound_no_radius(q, gs, beta):
+    g2 = dict(gs)
+    g2["R"] = np.zeros_like(gs["R"])
+    return OR.group_bound(q, g2, beta)
+
+
+def _mut_bound_no_lam(q, gs, beta):
+    g2 = dict(gs)
+    g2["lam"] = np.zeros_like(gs["lam"])
+    return OR.group_bound(q, g2, beta)
+
+
+def _mut_hier_prune_on_equal(q, mu, sigma, gs, m, k, beta, C):
+    ub = OR.group_bound(q, gs, beta)
+    G = -(-C // m)
+    scores = {}
+    for gi in sorted(range(G), key=lambda x: (-ub[x], x)):
+        if k == 0:
+            break
+        if len(scores) >= k and ub[gi] <= sorted(scores.values(), reverse=True)[k - 1]:
+            continue
+        blocks = list(range(gi * m, min(C, (gi + 1) * m)))
+        scores.update(zip(blocks, OR.route_scores(q, OR.as_f64(mu)[blocks],
+                                                  OR.as_f64(sigma)[blocks], beta).tolist()))
+    cs = np.array(sorted(scores), dtype=np.int64)
+    sel, _, _ = OR.select_topk(np.array([scores[c] for c in cs]), k)
+    idx = np.full(k, -1, dtype=np.int32)
+    ch = np.sort(cs[sel[sel >= 0]]) if cs.size else np.zeros(0, dtype=np.int64)
+    idx[:ch.size] = ch
+    return dict(idx=idx, evaluated=len(scores))
+
+
+def _mut_hier_bound_unused(q, mu, sigma, gs, m, k, beta, C):
+    # a route_hier whose bounds come from the mutated group_bound in ns is
+    # exercised by the other mutants; this one ignores the group order
+    out = OR.route_hier(q, mu, sigma, gs, m, k, beta, C)
+    out["evaluated"] = C
+    return out
+
+
 MUTANTS = {
     "sample_covariance": dict(block_stats=_mut_sample_cov),
     "beta_not_halved": dict(route_scores=_mut_full_beta),
@@ -777,6 +901,10 @@ MUTANTS = {
     "backward_dk_unscaled": dict(attend_backward=_mut_bwd_dk_unscaled),
     "backward_dv_unnormalised": dict(attend_backward=_mut_bwd_dv_unnormalised),
     "backward_dq_uses_values": dict(attend_backward=_mut_bwd_dq_uses_v),
+    "group_bound_no_radius": dict(group_bound=_mut_bound_no_radius),
+    "group_bound_no_covariance_slack": dict(group_bound=_mut_bound_no_lam),
+    "hier_prune_on_equal": dict(route_hier=_mut_hier_prune_on_equal),
+    "hier_never_prunes": dict(route_hier=_mut_hier_bound_unused),
 }
 
 
