@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     make_params,
     ssa_block_stats,
     ssa_decode_step,
+    ssa_group_stats,
+    ssa_route_hier,
     ssa_route_tempered,
     ssa_route_tiles,
     ssa_route_topk,

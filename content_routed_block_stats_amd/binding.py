@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("SSA_MI355X_LIB", os.path.join(HERE, "libssa_mi355x.so
 SSA_OK, SSA_ERR_INVALID_ARGUMENT, SSA_ERR_UNSUPPORTED, SSA_ERR_WORKSPACE_TOO_SMALL, SSA_ERR_HIP = range(5)
 SSA_F32, SSA_BF16 = 0, 1
 (SSA_OP_ROUTE, SSA_OP_ATTN, SSA_OP_DECODE, SSA_OP_ROUTE_TILES, SSA_OP_TILE_ATTN,
- SSA_OP_ATTN_BWD) = 1, 2, 3, 4, 5, 6
+ SSA_OP_ATTN_BWD, SSA_OP_ROUTE_HIER) = 1, 2, 3, 4, 5, 6, 7
 
 _vp = ctypes.c_void_p
 
@@ -75,9 +75,13 @@ def lib() -> ctypes.CDLL:
     L.ssa_sparse_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_decode_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
+    L.ssa_group_stats.argtypes = [P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp]
+    L.ssa_route_hier.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                 _vp, ctypes.c_size_t, _vp]
     for name in ("ssa_block_stats", "ssa_workspace_size", "ssa_route_topk", "ssa_route_tempered",
                  "ssa_route_tiles", "ssa_tile_attn_fwd", "ssa_sparse_attn_fwd",
-                 "ssa_sparse_attn_bwd", "ssa_decode_step"):
+                 "ssa_sparse_attn_bwd", "ssa_decode_step", "ssa_group_stats",
+                 "ssa_route_hier"):
         getattr(L, name).restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
@@ -347,3 +351,58 @@ def ssa_decode_step(q, k_new, v_new, K_cache, V_cache, cache_len, mu, sigma, *, 
                                  _ptr(V_cache), _ptr(cache_len), _ptr(mu), _ptr(sigma), _ptr(idx),
                                  _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
     return (o, lse, idx) if return_idx else (o, lse)
+
+
+def ssa_group_stats(mu: torch.Tensor, sigma: torch.Tensor, *, block_size: int, group_blocks: int):
+    """Stats mu [b, Hkv, nb, d], sigma [b, Hkv, nb, d, d] -> group summaries
+    (gmu [b, Hkv, G, d], gsigma [b, Hkv, G, d, d], grl [b, Hkv, G, 2]) float32,
+    G = ceil(nb / group_blocks)."""
+    _dev_check(mu, sigma)
+    b, hkv, nb, d = mu.shape
+    if sigma.shape != (*mu.shape, d) or mu.dtype != torch.float32 or sigma.dtype != torch.float32:
+        raise ValueError("mu/sigma must be float32 [b, Hkv, nb, d] / [b, Hkv, nb, d, d]")
+    if group_blocks < 1:
+        raise ValueError("group_blocks must be positive")
+    G = -(-nb // group_blocks)
+    gmu = torch.empty((b, hkv, G, d), dtype=torch.float32, device=mu.device)
+    gsigma = torch.empty((b, hkv, G, d, d), dtype=torch.float32, device=mu.device)
+    grl = torch.empty((b, hkv, G, 2), dtype=torch.float32, device=mu.device)
+    if nb == 0:
+        return gmu, gsigma, grl
+    p = make_params(batch=b, n_q_heads=hkv, n_kv_heads=hkv, head_dim=d, seq_len=nb * block_size,
+                    block_size=block_size, in_dtype=torch.float32)
+    _check(lib().ssa_group_stats(ctypes.byref(p), _ptr(mu), _ptr(sigma), group_blocks, _ptr(gmu),
+                                 _ptr(gsigma), _ptr(grl), _stream()))
+    return gmu, gsigma, grl
+
+
+def ssa_route_hier(q: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, gmu: torch.Tensor,
+                   gsigma: torch.Tensor, grl: torch.Tensor, pos: torch.Tensor, *, block_size: int,
+                   group_blocks: int, top_k: int, beta: float = 2.0, want_evaluated: bool = False,
+                   idx: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Exact top-k of decode queries q [b, Hq, d] at positions pos [b] (int32)
+    by branch and bound over block groups -> idx [b, Hq, k] int32 (, evaluated
+    [b, Hkv] int32).  mu/sigma hold nb block slots; gmu/gsigma/grl come from
+    ssa_group_stats with the same group_blocks."""
+    _dev_check(q, mu, sigma, gmu, gsigma, grl, pos)
+    b, hq, d = q.shape
+    hkv, nb = mu.shape[1], mu.shape[2]
+    if mu.shape != (b, hkv, nb, d) or sigma.shape != (*mu.shape, d):
+        raise ValueError("mu/sigma do not match q")
+    if group_blocks < 1:
+        raise ValueError("group_blocks must be positive")
+    G = -(-nb // group_blocks)
+    if gmu.shape != (b, hkv, G, d) or gsigma.shape != (b, hkv, G, d, d) or grl.shape != (b, hkv, G, 2):
+        raise ValueError("group summaries do not match mu")
+    if pos.dtype != torch.int32 or pos.shape != (b,):
+        raise ValueError("pos must be int32 [b]")
+    p = make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=nb * block_size,
+                    block_size=block_size, top_k=top_k, beta=beta, in_dtype=q.dtype)
+    if idx is None:
+        idx = torch.empty((b, hq, top_k), dtype=torch.int32, device=q.device)
+    ev = torch.empty((b, hkv), dtype=torch.int32, device=q.device) if want_evaluated else None
+    ws = _workspace(p, SSA_OP_ROUTE_HIER, q.device, workspace)
+    _check(lib().ssa_route_hier(ctypes.byref(p), _ptr(q), _ptr(mu), _ptr(sigma), _ptr(gmu),
+                                _ptr(gsigma), _ptr(grl), group_blocks, _ptr(pos), _ptr(idx),
+                                _ptr(ev), _ptr(ws), ws.numel(), _stream()))
+    return (idx, ev) if want_evaluated else idx

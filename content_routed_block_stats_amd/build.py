@@ -22,7 +22,7 @@ LIB_NAME = "libssa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["ssa_api.cpp", "block_stats.hip", "route_topk.hip", "tempered_route.hip", "tile_route.hip", "tile_attn.hip", "sparse_attn.hip", "attn_bwd.hip", "decode.hip"]
+SOURCES = ["ssa_api.cpp", "block_stats.hip", "route_topk.hip", "tempered_route.hip", "tile_route.hip", "tile_attn.hip", "sparse_attn.hip", "attn_bwd.hip", "hier_route.hip", "decode.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -407,17 +407,9 @@ hipError_t launch_decode_t(const Shape& s, const void* q, const void* k_new, con
     hipLaunchKernelGGL((decode_route_kernel<TIn, D>), rgrid, dim3(kDecThreads),
                        size_t(s.g) * D * 4, st, static_cast<const TIn*>(q), mu, sigma, cache_len,
                        w.scores, s.g, s.hq, s.hkv, s.B, s.nb, s.beta);
-    const dim3 tgrid(unsigned((rows + 3) / 4));
-    if (s.k <= 8)
-      hipLaunchKernelGGL(decode_topk_kernel<8>, tgrid, dim3(256), 0, st, w.scores, cache_len, sel,
-                         s.k, s.nb, s.hq, s.B, rows);
-    else if (s.k <= 16)
-      hipLaunchKernelGGL(decode_topk_kernel<16>, tgrid, dim3(256), 0, st, w.scores, cache_len, sel,
-                         s.k, s.nb, s.hq, s.B, rows);
-    else
-      hipLaunchKernelGGL(decode_topk_kernel<32>, tgrid, dim3(256), 0, st, w.scores, cache_len, sel,
-                         s.k, s.nb, s.hq, s.B, rows);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_decode_topk(w.scores, cache_len, sel, s.k, s.nb, s.hq, s.B, rows, st)) !=
+        hipSuccess)
+      return e;
   } else if (s.k > 0) {
     hipLaunchKernelGGL(fill_neg1_kernel, dim3(unsigned(std::min<int64_t>((rows * s.k + 255) / 256, 1024))),
                        dim3(256), 0, st, sel, rows * s.k);
@@ -444,6 +436,21 @@ hipError_t launch_decode_o(const Shape& s, const void* q, const void* kn, const 
 }
 
 }  // namespace
+
+hipError_t launch_decode_topk(const float* scores, const int32_t* pos, int32_t* idx, int k,
+                              int64_t n_slots, int hq, int B, int64_t rows, hipStream_t st) {
+  const dim3 tgrid(unsigned((rows + 3) / 4));
+  if (k <= 8)
+    hipLaunchKernelGGL(decode_topk_kernel<8>, tgrid, dim3(256), 0, st, scores, pos, idx, k,
+                       n_slots, hq, B, rows);
+  else if (k <= 16)
+    hipLaunchKernelGGL(decode_topk_kernel<16>, tgrid, dim3(256), 0, st, scores, pos, idx, k,
+                       n_slots, hq, B, rows);
+  else
+    hipLaunchKernelGGL(decode_topk_kernel<32>, tgrid, dim3(256), 0, st, scores, pos, idx, k,
+                       n_slots, hq, B, rows);
+  return hipGetLastError();
+}
 
 size_t decode_workspace_bytes(const Shape& s) { return dec_ws_layout(s, nullptr).bytes; }
 

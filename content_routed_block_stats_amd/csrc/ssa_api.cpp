@@ -206,6 +206,69 @@ ssa_status ssa_sparse_attn_bwd(const ssa_params* p, const void* Q, const void* K
                   "ssa_sparse_attn_bwd");
 }
 
+ssa_status ssa_group_stats(const ssa_params* p, const float* mu, const float* sigma,
+                           int32_t group_blocks, float* gmu, float* gsigma, float* grl,
+                           void* stream) {
+  ssa::Shape s;
+  ssa_status st = check_params(p, &s);
+  if (st != SSA_OK) return st;
+  if (group_blocks < 1 || group_blocks > ssa::hier_max_group())
+    return fail(SSA_ERR_INVALID_ARGUMENT, "group_blocks %d out of [1, %d]", group_blocks,
+                ssa::hier_max_group());
+  if (s.nb == 0) return ok();
+  SSA_NONNULL(mu);
+  SSA_NONNULL(sigma);
+  SSA_NONNULL(gmu);
+  SSA_NONNULL(gsigma);
+  SSA_NONNULL(grl);
+  if (int64_t(s.b) * s.hkv > 65535)
+    return fail(SSA_ERR_UNSUPPORTED, "more than 65535 (sequence, KV head) pairs");
+  return from_hip(ssa::launch_group_stats(s, mu, sigma, group_blocks, gmu, gsigma, grl,
+                                          (hipStream_t)stream),
+                  "ssa_group_stats");
+}
+
+ssa_status ssa_route_hier(const ssa_params* p, const void* q, const float* mu, const float* sigma,
+                          const float* gmu, const float* gsigma, const float* grl,
+                          int32_t group_blocks, const int32_t* pos, int32_t* idx,
+                          int32_t* evaluated, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  ssa::Shape s;
+  ssa_status st = check_params(p, &s);
+  if (st != SSA_OK) return st;
+  if (!(p->beta >= 0.f))
+    return fail(SSA_ERR_INVALID_ARGUMENT, "the group bound needs beta >= 0");
+  if (group_blocks < 1 || group_blocks > ssa::hier_max_group())
+    return fail(SSA_ERR_INVALID_ARGUMENT, "group_blocks %d out of [1, %d]", group_blocks,
+                ssa::hier_max_group());
+  if (s.g > ssa::hier_max_rows())
+    return fail(SSA_ERR_UNSUPPORTED, "more than %d q-heads per KV head", ssa::hier_max_rows());
+  const int64_t G = (s.nb + group_blocks - 1) / group_blocks;
+  if (G * s.g > ssa::hier_max_bounds())
+    return fail(SSA_ERR_UNSUPPORTED, "groups x q-heads per KV head = %lld exceeds %d",
+                (long long)(G * s.g), ssa::hier_max_bounds());
+  if (int64_t(s.b) * s.hkv > 65535)
+    return fail(SSA_ERR_UNSUPPORTED, "more than 65535 (sequence, KV head) pairs");
+  SSA_NONNULL(q);
+  SSA_NONNULL(pos);
+  if (s.k > 0) SSA_NONNULL(idx);
+  if (s.nb > 0) {
+    SSA_NONNULL(mu);
+    SSA_NONNULL(sigma);
+    SSA_NONNULL(gmu);
+    SSA_NONNULL(gsigma);
+    SSA_NONNULL(grl);
+  }
+  if (s.k == 0 && evaluated == nullptr) return ok();
+  if (s.k > 0) {
+    st = check_ws(ssa::route_hier_workspace_bytes(s), workspace, workspace_bytes);
+    if (st != SSA_OK) return st;
+  }
+  return from_hip(ssa::launch_route_hier(s, q, mu, sigma, gmu, gsigma, grl, group_blocks, pos, idx,
+                                         evaluated, workspace, (hipStream_t)stream),
+                  "ssa_route_hier");
+}
+
 ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes) {
   ssa::Shape s;
   ssa_status st = check_params(p, &s);
@@ -218,6 +281,7 @@ ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes) {
     case SSA_OP_ROUTE_TILES: *bytes = ssa::route_tiles_workspace_bytes(s); break;
     case SSA_OP_TILE_ATTN: *bytes = ssa::tile_attn_workspace_bytes(s); break;
     case SSA_OP_ATTN_BWD: *bytes = ssa::attn_bwd_workspace_bytes(s); break;
+    case SSA_OP_ROUTE_HIER: *bytes = ssa::route_hier_workspace_bytes(s); break;
     default: return fail(SSA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
   return ok();

@@ -87,8 +87,24 @@ hipError_t launch_sparse_attn_bwd(const Shape& s, const void* Q, const void* K, 
                                   const void* dO, float* dQ, float* dK, float* dV, void* ws,
                                   hipStream_t st);
 
+// exact hierarchical routing (branch and bound over groups of m blocks)
+int hier_max_rows();
+int hier_max_bounds();
+int hier_max_group();
+size_t route_hier_workspace_bytes(const Shape& s);   // any group size
+hipError_t launch_group_stats(const Shape& s, const float* mu, const float* sigma, int m, float* gmu,
+                              float* gS, float* grl, hipStream_t st);
+hipError_t launch_route_hier(const Shape& s, const void* q, const float* mu, const float* sigma,
+                             const float* gmu, const float* gS, const float* grl, int m,
+                             const int32_t* pos, int32_t* idx, int32_t* evaluated, void* ws,
+                             hipStream_t st);
+
 // decode step
 size_t decode_workspace_bytes(const Shape& s);
+// wave top-k of scores [rows, n_slots] over the blocks c < min(n_slots,
+// (pos[row / hq] + 1) / B), ascending, -1 padded (k <= 32)
+hipError_t launch_decode_topk(const float* scores, const int32_t* pos, int32_t* idx, int k,
+                              int64_t n_slots, int hq, int B, int64_t rows, hipStream_t st);
 hipError_t launch_decode_step(const Shape& s, const void* q, const void* k_new, const void* v_new,
                               void* K_cache, void* V_cache, int32_t* cache_len, float* mu,
                               float* sigma, int32_t* idx, void* o, float* lse, void* ws,

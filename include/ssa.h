@@ -55,7 +55,8 @@ typedef enum ssa_op {
   SSA_OP_DECODE = 3,  /* workspace of ssa_decode_step */
   SSA_OP_ROUTE_TILES = 4,  /* workspace of ssa_route_tiles */
   SSA_OP_TILE_ATTN = 5,    /* workspace of ssa_tile_attn_fwd */
-  SSA_OP_ATTN_BWD = 6      /* workspace of ssa_sparse_attn_bwd */
+  SSA_OP_ATTN_BWD = 6,     /* workspace of ssa_sparse_attn_bwd */
+  SSA_OP_ROUTE_HIER = 7    /* workspace of ssa_route_hier (any group_blocks) */
 } ssa_op;
 
 /* Shapes and method parameters.  Limits checked by every call:
@@ -227,6 +228,42 @@ ssa_status ssa_sparse_attn_bwd(const ssa_params* p, const void* Q, const void* K
                                const int32_t* idx, const void* O, const float* lse, const void* dO,
                                float* dQ, float* dK, float* dV, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* Exact hierarchical routing, decode queries (write-up: the module list pairs
+ * the flat router with branch-and-bound exact selection under an admissible
+ * bound and a tree router with a recursive radius; "Selected results" report
+ * lossless branch-and-bound selection costs).  Groups of m = group_blocks
+ * consecutive blocks (G = ceil(nb / m) per (sequence, KV head), nb the
+ * complete block slots of seq_len) are summarised by ssa_group_stats:
+ *   gmu    [b, Hkv, G, d]     mean of the members' mu_c
+ *   gsigma [b, Hkv, G, d, d]  mean of the members' Sigma_c (S_G)
+ *   grl    [b, Hkv, G, 2]     R_G = max ||mu_c - mu_G||, lam_G = max (tr (Sigma_c - S_G)^4)^(1/4)
+ * (all float32, written; one-time work, recomputed when blocks change).  For
+ * beta >= 0 every member's score is at most
+ *   UB_G(q) = q.mu_G + ||q|| R_G + (beta/2)(q^T S_G q + lam_G ||q||^2).
+ * ssa_route_hier selects, for every (sequence b, q-head h) with query q
+ * [b, Hq, d] at position pos[b] (int32, device), the min(k, #routable) blocks
+ * c < nb with (c+1)B-1 <= pos[b] of highest r_c = <q, mu_c> + (beta/2) q^T
+ * Sigma_c q, ties to the lower c -- the flat top-k, exactly -- visiting groups
+ * by decreasing bound (largest over the KV head's q-heads) and skipping a group
+ * when its bound is below every row's running k-th score (with a relative
+ * margin of 1e-4 over float32 rounding).
+ *   idx        [b, Hq, k] int32, written: ascending, -1 padded
+ *   evaluated  [b, Hkv] int32, written if not NULL: blocks scored exactly
+ *   workspace  >= ssa_workspace_size(p, SSA_OP_ROUTE_HIER) bytes (k > 0)
+ * Scores in float32 from Sigma_c's upper triangle (Sigma_c symmetric).
+ * gmu/gsigma/grl must summarise the current mu/sigma with the same
+ * group_blocks, or the selection may be wrong.  Limits: group_blocks in
+ * [1, 64] and beta >= 0 (SSA_ERR_INVALID_ARGUMENT); at most 16 q-heads per KV
+ * head, G * (Hq / Hkv) <= 8192 and b * Hkv <= 65535 (SSA_ERR_UNSUPPORTED). */
+ssa_status ssa_group_stats(const ssa_params* p, const float* mu, const float* sigma,
+                           int32_t group_blocks, float* gmu, float* gsigma, float* grl,
+                           void* stream);
+ssa_status ssa_route_hier(const ssa_params* p, const void* q, const float* mu, const float* sigma,
+                          const float* gmu, const float* gsigma, const float* grl,
+                          int32_t group_blocks, const int32_t* pos, int32_t* idx,
+                          int32_t* evaluated, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* One decode step per sequence (write-up, module table: the decode path routes
  * and attends one new query per step against the cache).  With

@@ -10,7 +10,11 @@ screen"): Q and V are iid N(0, 1).  K is built per block: a block centre
 m_c ~ N(0, center_std^2 I) plus per-key noise N(0, noise_std^2 I).  A number of
 "planted outliers" replace single keys by 3 * q_t / ||q_t|| for a query t that
 lies after the key's block, so that the block is routable for that query.
-These plants play the role of single-needle targets.
+These plants play the role of single-needle targets.  With group_std > 0 each
+run of group_blocks consecutive block centres also shares a group centre
+N(0, group_std^2 I), a geometry in which whole groups of blocks can be ruled out
+for a query (the hierarchical router's test case); group_std = 0, the default,
+leaves every existing stream unchanged.
 
 Everything is drawn with torch generators seeded per tensor, so a workload is a
 pure function of (config, seed, device).  CPU and GPU generators give different

@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 _TAG_Q, _TAG_K_CENTRE, _TAG_K_NOISE, _TAG_V, _TAG_PLANT = 11, 13, 17, 19, 23
-_TAG_QNEW, _TAG_VNEW = 29, 31
+_TAG_QNEW, _TAG_VNEW, _TAG_K_GROUP = 29, 31, 37
 
 
 def _mix(*parts: int) -> int:
@@ -42,6 +42,8 @@ class Workload:
     plants: int           # planted outliers per (sequence, KV head)
     plant_mode: str       # "blocks" | "positions" | "decode"
     decode: bool = False
+    group_std: float = 0.0    # std of a centre shared by group_blocks consecutive blocks
+    group_blocks: int = 16    # (0 std: no group structure, the default)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -147,6 +149,11 @@ def _keys(wl: Workload, seed: int, b: int, kv: int, n_keys: int, device) -> torc
     B, d = wl.block, wl.head_dim
     nbp = -(-n_keys // B)
     centre = _randn((nbp, d), device, seed, _TAG_K_CENTRE, b, kv) * wl.center_std
+    if wl.group_std > 0:
+        # routable geometry: block centres scattered around shared group centres
+        ngp = -(-nbp // wl.group_blocks)
+        grp = _randn((ngp, d), device, seed, _TAG_K_GROUP, b, kv) * wl.group_std
+        centre = centre + grp.repeat_interleave(wl.group_blocks, dim=0)[:nbp]
     noise = _randn((n_keys, d), device, seed, _TAG_K_NOISE, b, kv) * wl.noise_std
     return noise.add_(centre.repeat_interleave(B, dim=0)[:n_keys])
 

@@ -121,3 +121,54 @@ def test_tempered_route_checks_pointers_on_host():
     # nothing requested (k = 0, no kth): returns before any launch
     p0 = _p(beta=2.0, top_k=0)
     assert L.ssa_route_tempered(ctypes.byref(p0), 256, 256, None, None, None) == B.SSA_OK
+
+
+@pytest.mark.parametrize("m", [0, -3, 65])
+def test_group_calls_reject_group_size_out_of_range(m):
+    L = ssa.lib()
+    p = _p()
+    assert L.ssa_group_stats(ctypes.byref(p), 256, 256, m, 256, 256, 256, None) == \
+        B.SSA_ERR_INVALID_ARGUMENT
+    assert "group_blocks" in L.ssa_last_error().decode()
+    assert L.ssa_route_hier(ctypes.byref(p), 256, 256, 256, 256, 256, 256, m, 256, 256, None,
+                            256, 1 << 30, None) == B.SSA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("beta", [-0.5, float("nan")])
+def test_hier_route_needs_non_negative_beta(beta):
+    p = _p()
+    p.beta = beta  # make_params validation is the library's job
+    got = ssa.lib().ssa_route_hier(ctypes.byref(p), 256, 256, 256, 256, 256, 256, 8, 256, 256,
+                                   None, 256, 1 << 30, None)
+    assert got == B.SSA_ERR_INVALID_ARGUMENT, B.status_string(got)
+
+
+def test_hier_route_limits_and_pointers_on_host():
+    L = ssa.lib()
+    # more than 16 q-heads per KV head
+    p = _p(n_q_heads=32, n_kv_heads=1)
+    assert L.ssa_route_hier(ctypes.byref(p), 256, 256, 256, 256, 256, 256, 8, 256, 256, None,
+                            256, 1 << 30, None) == B.SSA_ERR_UNSUPPORTED
+    # G * g beyond the bound table: 2^20 tokens / B 64 = 16384 blocks, m = 1, g = 2
+    p = _p(seq_len=1 << 20, block_size=64)
+    assert L.ssa_route_hier(ctypes.byref(p), 256, 256, 256, 256, 256, 256, 1, 256, 256, None,
+                            256, 1 << 30, None) == B.SSA_ERR_UNSUPPORTED
+    p = _p()
+    # q, mu, sigma, gmu, gsigma, grl, group_blocks, pos, idx, evaluated, workspace
+    need = B.ssa_workspace_size(p, B.SSA_OP_ROUTE_HIER)
+    assert need > 0
+    good = [256, 256, 256, 256, 256, 256, 8, 256, 256, None, 256]
+    for i in (0, 1, 2, 3, 4, 5, 7, 8, 10):
+        args = list(good)
+        args[i] = None
+        got = L.ssa_route_hier(ctypes.byref(p), *args, need, None)
+        assert got == B.SSA_ERR_INVALID_ARGUMENT, (i, B.status_string(got))
+    got = L.ssa_route_hier(ctypes.byref(p), *good, need - 1, None)
+    assert got == B.SSA_ERR_WORKSPACE_TOO_SMALL
+    # nothing requested (k = 0, no counts): returns before any launch
+    p0 = _p(top_k=0)
+    assert L.ssa_route_hier(ctypes.byref(p0), 256, 256, 256, 256, 256, 256, 8, 256, None, None,
+                            None, 0, None) == B.SSA_OK
+    # group stats: NULL outputs
+    assert L.ssa_group_stats(ctypes.byref(p), 256, 256, 8, None, 256, 256, None) == \
+        B.SSA_ERR_INVALID_ARGUMENT
