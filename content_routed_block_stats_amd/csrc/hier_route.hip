@@ -63,6 +63,7 @@ template <int D>
 __global__ __launch_bounds__(kHierThreads) void group_stats_kernel(
     const float* __restrict__ mu, const float* __restrict__ sigma, float* __restrict__ gmu,
     float* __restrict__ gS, float* __restrict__ grl, int64_t nb, int m, int64_t G) {
+  constexpr int PER = D * D / kHierThreads;      // covariance entries per thread (tid + 256 i)
   __shared__ float A[D * D];
   __shared__ float mg[D];
   __shared__ float red[kHierThreads / 64];
@@ -72,18 +73,26 @@ __global__ __launch_bounds__(kHierThreads) void group_stats_kernel(
   const float inv = 1.f / float(c1 - c0);
   const float* mu_b = mu + bkv * nb * D;
   const float* sg_b = sigma + bkv * nb * D * D;
-  // mean centroid and mean covariance
+  // mean centroid and mean covariance (the latter kept in registers)
   for (int i = tid; i < D; i += kHierThreads) {
     float s = 0.f;
     for (int64_t c = c0; c < c1; ++c) s += mu_b[c * D + i];
     mg[i] = s * inv;
     gmu[(bkv * G + gi) * D + i] = s * inv;
   }
+  float sg[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sg[i] = 0.f;
+  for (int64_t c = c0; c < c1; ++c) {
+    const float* S = sg_b + c * D * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) sg[i] += S[tid + kHierThreads * i];
+  }
   float* Sg = gS + (bkv * G + gi) * D * D;
-  for (int e = tid; e < D * D; e += kHierThreads) {
-    float s = 0.f;
-    for (int64_t c = c0; c < c1; ++c) s += sg_b[c * D * D + e];
-    Sg[e] = s * inv;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    sg[i] *= inv;
+    Sg[tid + kHierThreads * i] = sg[i];
   }
   __syncthreads();
   float R = 0.f, lam = 0.f;
@@ -99,7 +108,9 @@ __global__ __launch_bounds__(kHierThreads) void group_stats_kernel(
     }
     const float r2 = hier_block_sum(dv, red);
     R = fmaxf(R, sqrtf(r2));
-    for (int e = tid; e < D * D; e += kHierThreads) A[e] = sg_b[c * D * D + e] - Sg[e];
+    const float* S = sg_b + c * D * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) A[tid + kHierThreads * i] = S[tid + kHierThreads * i] - sg[i];
     __syncthreads();
     float acc[TS][TS];
 #pragma unroll
