@@ -174,12 +174,37 @@ def bench_decode(steps: int, warmup: int) -> dict:
     tiles = (d // 32) * (d // 32 + 1) // 2
     sig = wl.batch * wl.n_kv_heads * nbc * (tiles * 32 * 32 * 4 + d * 4)
     gat = wl.batch * wl.n_q_heads * (wl.top_k * wl.block + wl.window) * d * 2 * 2
+    # exact hierarchical routing of the same queries over the same statistics
+    m = 16
+    e0.record()
+    gs = ssa.ssa_group_stats(mu, sigma, block_size=wl.block, group_blocks=m)
+    e1.record()
+    torch.cuda.synchronize()
+    gs_ms = e0.elapsed_time(e1)
+    pos = cache_len.clone()
+    hws = torch.empty(ssa.ssa_workspace_size(p, 7), dtype=torch.uint8, device="cuda")
+    idx, ev = ssa.ssa_route_hier(q, mu, sigma, *gs, pos, block_size=wl.block, group_blocks=m,
+                                 top_k=wl.top_k, beta=wl.beta, want_evaluated=True,
+                                 workspace=hws)
+    e0.record()
+    for _ in range(steps):
+        ssa.ssa_route_hier(q, mu, sigma, *gs, pos, block_size=wl.block, group_blocks=m,
+                           top_k=wl.top_k, beta=wl.beta, idx=idx, workspace=hws)
+    e1.record()
+    torch.cuda.synchronize()
+    hier_ms = e0.elapsed_time(e1) / steps
+    routable = int(((pos.long() + 1) // wl.block).clamp(max=mu.shape[2]).sum()) * wl.n_kv_heads
+    scored = int(ev.long().sum())
     del data
     return {"workload": wl.name, "ms_per_step": round(ms, 4),
             "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
             "hbm_gbs_algorithmic": round((sig + gat) / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round((sig + gat) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "steps": steps}
+            "steps": steps,
+            "hier_route": {"group_blocks": m, "ms": round(hier_ms, 4),
+                           "group_stats_ms_once": round(gs_ms, 3),
+                           "blocks_scored_frac": round(scored / max(1, routable), 4),
+                           "keys": "standard decode keys (no group structure)"}}
 
 
 def tempered_flops(wl) -> float:
@@ -494,7 +519,9 @@ def main() -> int:
                        "bound": "mfma", "achieved": round(bwd_fl / (t_bwd * 1e-3) / 1e12, 1),
                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": round(bwd_fl / (t_bwd * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                       "algorithmic_flops_per_launch": bwd_fl, "reps": breps}
+                       "algorithmic_flops_per_launch": bwd_fl, "reps": breps,
+                       "traffic_dkv_kernel": counted_traffic("attn_bwd_dkv", kernel_source_digest(
+                           "attn_bwd.hip", "kv_chunks.hpp", "ssa_common.hpp"))}
     del ws_b, dO
 
     # the exact tempered score (same workload and beta), outside the step
