@@ -209,15 +209,18 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
   using Frag = typename A::Frag;
   constexpr int ES = A::ES;
   constexpr int ROWB = D * ES;
+  constexpr int RSTR = ROWB + 16;      // padded row stride: a wave's row reads spread over banks
   constexpr int ROWS = kDkvRows;
+  constexpr int TRS = ROWS + 4;        // transposed float16 copy: halves per column
   __shared__ __attribute__((aligned(1024))) uint8_t img[2 * A::KBYTES];   // K rows, V rows
-  __shared__ __attribute__((aligned(16))) uint8_t rbuf[2 * ROWS * ROWB];  // Q rows, dO rows
+  __shared__ __attribute__((aligned(16))) uint8_t rbuf[2 * ROWS * RSTR];  // Q rows, dO rows
   __shared__ float rl2[ROWS], rd[ROWS];
   __shared__ int64_t rrow[ROWS], rpos[ROWS];
   __shared__ int32_t rmode[ROWS];
-  static_assert(2 * ROWS * ROWB >= kKeyChunk * D * 4, "reduction buffer");
+  static_assert(2 * ROWS * RSTR >= kKeyChunk * D * 4, "reduction buffer");
+  static_assert(D * TRS * 2 <= ROWS * RSTR, "transposed copy");
   uint8_t* rq = rbuf;
-  uint8_t* rdo = rbuf + ROWS * ROWB;
+  uint8_t* rdo = rbuf + ROWS * RSTR;
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int kh = wave % 2, rg = wave / 2;
@@ -311,8 +314,8 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
         vq = reinterpret_cast<const u32x4*>(Q + row * D)[pc];
         vd = reinterpret_cast<const u32x4*>(dO + row * D)[pc];
       }
-      reinterpret_cast<u32x4*>(rq + rr * ROWB)[pc] = vq;
-      reinterpret_cast<u32x4*>(rdo + rr * ROWB)[pc] = vd;
+      reinterpret_cast<u32x4*>(rq + rr * RSTR)[pc] = vq;
+      reinterpret_cast<u32x4*>(rdo + rr * RSTR)[pc] = vd;
     }
     __syncthreads();   // rows staged
     // the next rows' information, fetched while these rows are computed (the
@@ -321,9 +324,10 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
     if (tid < ROWS && i0 + ROWS < total) nx = info(i0 + ROWS + tid);
 
     const int r0 = 32 * rg;
-    if (i0 + r0 < total) {
+    const bool active = i0 + r0 < total;
+    floatx16 sacc, pacc;
+    if (active) {
       // S = Q K^T and dP = dO V^T for this wave's 32 rows x 32 keys (lanes on keys)
-      floatx16 sacc, pacc;
 #pragma unroll
       for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
 #pragma unroll
@@ -331,8 +335,8 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
         const Frag kf = *reinterpret_cast<const Frag*>(img + (kh * A::NS + s) * A::FRAG + lane * 8 * ES);
         const Frag vf = *reinterpret_cast<const Frag*>(img + A::KBYTES + (kh * A::NS + s) * A::FRAG +
                                                        lane * 8 * ES);
-        const Frag qa = *reinterpret_cast<const Frag*>(rq + (r0 + ln) * ROWB + (16 * s + 8 * h) * ES);
-        const Frag da = *reinterpret_cast<const Frag*>(rdo + (r0 + ln) * ROWB + (16 * s + 8 * h) * ES);
+        const Frag qa = *reinterpret_cast<const Frag*>(rq + (r0 + ln) * RSTR + (16 * s + 8 * h) * ES);
+        const Frag da = *reinterpret_cast<const Frag*>(rdo + (r0 + ln) * RSTR + (16 * s + 8 * h) * ES);
         sacc = mma16(qa, kf, sacc);
         pacc = mma16(da, vf, pacc);
       }
@@ -347,6 +351,47 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
         sacc[j] = p;
         pacc[j] = p * (pacc[j] - rd[rr]);
       }
+    }
+    if constexpr (!F32) {
+      // Q^T and dO^T as scaled float16, [column][row] (TRS halves per column),
+      // written over the row-major copy once every wave has read it.  Thread
+      // unit: rows 2 rp, 2 rp + 1 and columns [8 pc, 8 pc + 8); a wave takes 8
+      // row pairs x 8 column groups, D / 64 units per thread.
+      static_assert(ROWS == 64 && kDkvThreads == 256, "unit map: 32 row pairs over 4 waves");
+      constexpr int UNITS = D / 64;
+      u32x4 pq[UNITS][2], pd[UNITS][2];
+#pragma unroll
+      for (int j = 0; j < UNITS; ++j) {
+        const int rp = 8 * wave + lane % 8, pc = lane / 8 + 8 * j;
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          pq[j][o] = *reinterpret_cast<const u32x4*>(rq + (2 * rp + o) * RSTR + pc * 16);
+          pd[j][o] = *reinterpret_cast<const u32x4*>(rdo + (2 * rp + o) * RSTR + pc * 16);
+        }
+      }
+      __syncthreads();   // every wave has read the row-major copy
+#pragma unroll
+      for (int j = 0; j < UNITS; ++j) {
+        const int rp = 8 * wave + lane % 8, pc = lane / 8 + 8 * j;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int sh = 16 * (i % 2);
+          const float q0 = __builtin_bit_cast(float, ((pq[j][0][i / 2] >> sh) & 0xFFFFu) << 16) * sq;
+          const float q1 = __builtin_bit_cast(float, ((pq[j][1][i / 2] >> sh) & 0xFFFFu) << 16) * sq;
+          const float d0 = __builtin_bit_cast(float, ((pd[j][0][i / 2] >> sh) & 0xFFFFu) << 16) * sdo;
+          const float d1 = __builtin_bit_cast(float, ((pd[j][1][i / 2] >> sh) & 0xFFFFu) << 16) * sdo;
+          const uint32_t wq = uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(q0))) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(q1))) << 16);
+          const uint32_t wd = uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(d0))) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(d1))) << 16);
+          const int at = ((8 * pc + i) * TRS + 2 * rp) * 2;
+          *reinterpret_cast<uint32_t*>(rq + at) = wq;
+          *reinterpret_cast<uint32_t*>(rdo + at) = wd;
+        }
+      }
+      __syncthreads();   // the transposed copies are complete
+    }
+    if (active) {
       // dV^T += dO^T P and dK^T += Q^T dS: rows contracted in frag_k order
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
@@ -360,12 +405,23 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int mt = 0; mt < A::MTD; ++mt) {
           VF<F32> qt, dt;
+          const int col = 32 * mt + ln;
+          if constexpr (F32) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int rr = r0 + frag_k(sp, h, e);
-            const int col = 32 * mt + ln;
-            set_vf<F32>(qt, e, load_f32(reinterpret_cast<const In*>(rq + rr * ROWB), col) * sq);
-            set_vf<F32>(dt, e, load_f32(reinterpret_cast<const In*>(rdo + rr * ROWB), col) * sdo);
+            for (int e = 0; e < 8; ++e) {
+              const int rr = r0 + frag_k(sp, h, e);
+              set_vf<F32>(qt, e, load_f32(reinterpret_cast<const In*>(rq + rr * RSTR), col) * sq);
+              set_vf<F32>(dt, e, load_f32(reinterpret_cast<const In*>(rdo + rr * RSTR), col) * sdo);
+            }
+          } else {
+            // rows r0 + frag_k(sp, h, e): 4 consecutive rows, then 4 more 8 rows on
+            const int at = (col * TRS + r0 + 16 * sp + 4 * h) * 2;
+            const uint2 q_lo = *reinterpret_cast<const uint2*>(rq + at);
+            const uint2 q_hi = *reinterpret_cast<const uint2*>(rq + at + 16);
+            const uint2 d_lo = *reinterpret_cast<const uint2*>(rdo + at);
+            const uint2 d_hi = *reinterpret_cast<const uint2*>(rdo + at + 16);
+            qt = __builtin_bit_cast(f16x8, u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y});
+            dt = __builtin_bit_cast(f16x8, u32x4{d_lo.x, d_lo.y, d_hi.x, d_hi.y});
           }
           dv[mt] = mma16(dt, pf, dv[mt]);
           dk[mt] = mma16(qt, sf, dk[mt]);
