@@ -194,3 +194,50 @@ def test_gqa_prefill_128k_tiles_fullsize():
             assert eo <= O_TOL[wl.dtype] and el <= LSE_TOL, (h, j, t, eo, el)
         say(f"  head {h} tile {j}: selection ok, rows ok")
 
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("keys", ["standard", "clustered"])
+def test_decode_256k_hier_fullsize(keys):
+    """Exact hierarchical routing on the 32 x 256K decode caches (groups of 16
+    blocks): every row's selection equals the flat decode router's up to
+    near-ties, and sampled (sequence, KV head) pairs equal the oracle's flat
+    top-k; on clustered keys at most 60% of the blocks are scored."""
+    wl = CONFIGS["decode_256k"]
+    if keys == "clustered":
+        wl = wl.replace(center_std=0.05, noise_std=0.05, group_std=1.0, plants=2)
+    L, m = wl.seq_len, 16
+    say(f"case decode_256k hierarchical routing, {keys} keys: generating on the GPU")
+    data = make_decode(wl, seed=0, device=DEV, capacity=L + 1)
+    Kc, Vc, q = data["K_cache"], data["V_cache"], data["q"]
+    mu, sigma = ssa.ssa_block_stats(Kc, wl.block)
+    gs = ssa.ssa_group_stats(mu, sigma, block_size=wl.block, group_blocks=m)
+    pos = torch.full((wl.batch,), L, dtype=torch.int32, device=DEV)
+    idx, ev = ssa.ssa_route_hier(q, mu, sigma, *gs, pos, block_size=wl.block, group_blocks=m,
+                                 top_k=wl.top_k, beta=wl.beta, want_evaluated=True)
+    cache_len = torch.full((wl.batch,), L, dtype=torch.int32, device=DEV)
+    _, _, idx_flat = ssa.ssa_decode_step(q, data["k_new"], data["v_new"], Kc, Vc, cache_len, mu,
+                                         sigma, block_size=wl.block, top_k=wl.top_k,
+                                         window=wl.window, beta=wl.beta, scale=wl.scale,
+                                         return_idx=True)
+    torch.cuda.synchronize()
+    idx_h, flat_h, ev_h = idx.cpu().numpy(), idx_flat.cpu().numpy(), ev.cpu().numpy()
+    nbc = (L + 1) // wl.block
+    frac = ev_h.sum() / (ev_h.size * nbc)
+    agree = (idx_h == flat_h).all(-1).mean()
+    say(f"  blocks scored {frac:.3f}; rows equal to the flat router {agree:.4f}")
+    assert np.all((idx_h >= 0).sum(-1) == min(wl.top_k, nbc))
+    assert np.all(np.diff(idx_h, axis=-1) > 0) and np.all(idx_h < nbc)
+    assert agree >= 0.99
+    assert np.all(ev_h <= nbc)
+    if keys == "clustered":
+        assert frac <= 0.6
+    rng = np.random.default_rng(1)
+    for b, kv in [(int(rng.integers(wl.batch)), int(rng.integers(wl.n_kv_heads))) for _ in range(2)]:
+        muo, sgo = O.block_stats(O.as_f64(Kc[b, kv, :nbc * wl.block].cpu()), wl.block)
+        for h in range(kv * wl.group, (kv + 1) * wl.group):
+            r = O.route_scores(O.as_f64(q[b, h].cpu()), muo, sgo, wl.beta)
+            sel, rk, rk1 = O.select_topk(r, wl.top_k)
+            ok, _ = idx_ok(idx_h[b, h], dict(idx=sel, scores=r, r_k=rk, r_k1=rk1))
+            assert ok, f"hierarchical selection mismatch b={b} h={h}"
+        say(f"  sequence {b} kv head {kv}: {wl.group} rows ok")
