@@ -15,11 +15,16 @@
 // MFMA's own register layout (see frag_k in ssa_common.hpp), so Q is read
 // once per tile and stays in registers for the whole sweep over blocks.
 //
-// Precision.  Q is exact in bfloat16.  T_c (float32) is split into a high
-// and a low bfloat16 part and both are contracted, with float32
-// accumulation, so scores carry ~2^-17 relative error instead of the 2^-9 of
-// a single bfloat16 rounding -- enough to reproduce the exact top-k except
-// where two scores are nearly tied.  float32 inputs use the float32 MFMA.
+// Precision.  Q is bfloat16, which float16 holds exactly in its normal
+// range, so Q enters the float16 MFMA after an exact power-of-two scaling per
+// (sequence, KV head) that brings its largest |q| into [2^14, 2^15).  T_c (float32) is scaled per block by a power
+// of two that brings its largest entry to [2^14, 2^15) and split into a high
+// and a low float16 part; both are contracted with float32 accumulation, so
+// scores carry ~2^-22 relative error instead of the 2^-11 of a single float16
+// rounding -- enough to reproduce the exact top-k except where two scores are
+// nearly tied.  The row-dot reads q from the same float16 registers (mixed
+// float16 x float32 fused multiply-adds, no conversions).  float32 inputs use
+// the float32 MFMA.
 //
 // Work split.  A workgroup of 8 waves owns 512 consecutive query rows of one
 // (sequence, KV head), ordered (token, group member), so one Sigma_c tile in
@@ -27,6 +32,9 @@
 // streamed in order c = 0, 1, ... through a double-buffered LDS copy of a
 // prepared fragment image; ties in the top-k therefore keep the lower block.
 // Workgroups are issued longest (most routable blocks) first.
+#include <algorithm>
+
+#include "kv_chunks.hpp"
 #include "ssa_common.hpp"
 #include "ssa_internal.hpp"
 
@@ -44,20 +52,34 @@ struct RouteLayout {
   static constexpr int NF = MT * (MT + 1);          // chunks on or above the diagonal
   static constexpr int MU_OFF = NF * kFragBytes;
   static constexpr int MU_BYTES = 2 * MT * 16 * 4;  // mu in accumulator order, both lane halves
-  static constexpr int BLOCK_BYTES = (MU_OFF + MU_BYTES + 255) / 256 * 256;
+  static constexpr int SCALE_OFF = MU_OFF + MU_BYTES;  // float: 2^e, T_c and mu are stored times 2^-e
+  static constexpr int BLOCK_BYTES = (SCALE_OFF + 16 + 255) / 256 * 256;
   // LDS copy of one image, whole 1 KB DMA rows (the last row reads past the image)
   static constexpr int DMA_ROWS = (BLOCK_BYTES + 1023) / 1024;
   static constexpr int LDS_BYTES = DMA_ROWS * 1024;
   __host__ __device__ static constexpr int frag(int mt, int s) { return mt * (mt + 1) + s; }
 };
 
+// Exponent eq with max|q| * 2^-eq in [2^14, 2^15) for the largest |q| given as
+// bfloat16 bits (0 for zero, infinite or NaN maxima): the float16 scale of Q.
+__device__ __forceinline__ int query_exponent(uint32_t qmax_bits) {
+  const float v = bf16_bits_to_f32(qmax_bits & 0x7FFFu);
+  if (!(v > 0.f) || !(v < __builtin_inff())) return 0;
+  int E = 0;
+  (void)frexpf(v, &E);   // v < 2^E
+  return E - 15;
+}
+
 // Prepared image of one block (workspace): for every output tile mt and
 // chunk s <= 2mt+1, lane (m, h) of the fragment holds T_c[frag_k(s,h,e)][32mt+m]
-// for e = 0..7 -- as bf16 hi (bytes 0..1023) and lo (1024..2047), or float32;
-// then mu_c in accumulator order: [h][mt][4a+b] = mu_c[32mt + 8a + 4h + b].
+// for e = 0..7 -- times 2^-e as float16 hi (bytes 0..1023) and lo
+// (1024..2047), or float32 (e = 0); then mu_c times 2^-(e + eq) in accumulator
+// order: [h][mt][4a+b] = mu_c[32mt + 8a + 4h + b], where 2^-eq is the float16
+// scale of the KV head's query rows; then the float 2^e.
 template <bool F32, int D>
 __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ mu,
                                                           const float* __restrict__ sigma,
+                                                          const uint32_t* __restrict__ qmax,
                                                           uint8_t* __restrict__ prep, int64_t nb,
                                                           float beta) {
   using Lay = RouteLayout<D>;
@@ -66,6 +88,26 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
   const float* M = mu + blk * D;
   uint8_t* out = prep + blk * Lay::BLOCK_BYTES;
   const float half_beta = 0.5f * beta;
+  // float16 parts: scale by 2^-e so that the largest |T_ij| lies in [2^14, 2^15)
+  float scale = 1.f, unscale = 1.f;
+  if constexpr (!F32) {
+    __shared__ float red[4];
+    float mx = 0.f;
+    for (int w = threadIdx.x; w < D * D; w += blockDim.x) {
+      const int i = w / D, j = w % D;
+      if (i <= j) mx = fmaxf(mx, fabsf((i < j ? beta : half_beta) * S[w]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, wave_shfl_xor(mx, o));
+    if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (mx > 0.f && mx == mx && mx < __builtin_inff()) {
+      const int e = ilogbf(mx) - 14;
+      scale = ldexpf(1.f, -e);
+      unscale = ldexpf(1.f, e);
+    }
+  }
   for (int w = threadIdx.x; w < Lay::NF * 64; w += blockDim.x) {
     const int f = w / 64, lane = w % 64, m = lane % 32, h = lane / 32;
     int mt = 0;
@@ -85,30 +127,31 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
       for (int e = 0; e < 8; ++e) v[e] = x[e];
       *reinterpret_cast<floatx8*>(out + f * kFragBytes + lane * 32) = v;
     } else {
-      u32x4 hi, lo;
+      f16x8 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const u16 h0 = f32_to_bf16_bits(x[e]), h1 = f32_to_bf16_bits(x[e + 1]);
-        const u16 l0 = f32_to_bf16_bits(x[e] - bf16_bits_to_f32(h0));
-        const u16 l1 = f32_to_bf16_bits(x[e + 1] - bf16_bits_to_f32(h1));
-        hi[e / 2] = uint32_t(h0) | (uint32_t(h1) << 16);
-        lo[e / 2] = uint32_t(l0) | (uint32_t(l1) << 16);
+      for (int e = 0; e < 8; ++e) {
+        const float v = x[e] * scale;
+        const _Float16 hv = static_cast<_Float16>(v);
+        hi[e] = hv;
+        lo[e] = static_cast<_Float16>(v - static_cast<float>(hv));
       }
-      *reinterpret_cast<u32x4*>(out + f * kFragBytes + lane * 16) = hi;
-      *reinterpret_cast<u32x4*>(out + f * kFragBytes + 1024 + lane * 16) = lo;
+      *reinterpret_cast<f16x8*>(out + f * kFragBytes + lane * 16) = hi;
+      *reinterpret_cast<f16x8*>(out + f * kFragBytes + 1024 + lane * 16) = lo;
     }
   }
+  const float mscale = F32 ? scale : scale * ldexpf(1.f, -query_exponent(qmax[blockIdx.y]));
   for (int w = threadIdx.x; w < 2 * Lay::MT * 16; w += blockDim.x) {
     const int h = w / (Lay::MT * 16), mt = (w / 16) % Lay::MT, i = w % 16;
-    reinterpret_cast<float*>(out + Lay::MU_OFF)[w] = M[32 * mt + 8 * (i / 4) + 4 * h + (i % 4)];
+    reinterpret_cast<float*>(out + Lay::MU_OFF)[w] = M[32 * mt + 8 * (i / 4) + 4 * h + (i % 4)] * mscale;
   }
+  if (threadIdx.x == 0) *reinterpret_cast<float*>(out + Lay::SCALE_OFF) = unscale;
 }
 
 template <bool F32>
 struct QFrag;
 template <>
 struct QFrag<false> {
-  using T = bf16x8;
+  using T = f16x8;      // bfloat16 rows held as float16 (exact in the normal range)
   using In = bf16_t;
   __device__ static float elem(const T& v, int e) { return static_cast<float>(v[e]); }
 };
@@ -135,23 +178,26 @@ __device__ __forceinline__ typename QFrag<F32>::T load_q_frag(const typename QFr
       v[e] = a[e];
       v[e + 4] = b[e];
     }
-  } else {
-    u32x2 a = {0u, 0u}, b = a;
-    if (valid) {
-      a = *reinterpret_cast<const u32x2*>(row + 16 * s + 4 * h);
-      b = *reinterpret_cast<const u32x2*>(row + 16 * s + 8 + 4 * h);
-    }
-    u32x4 w = {a[0], a[1], b[0], b[1]};
-    v = __builtin_bit_cast(bf16x8, w);
   }
   return v;
+}
+
+// The bfloat16 bits of the same fragment (converted to float16 by the caller).
+__device__ __forceinline__ u32x4 load_q_bits(const bf16_t* row, int s, int h, bool valid) {
+  u32x2 a = {0u, 0u}, b = a;
+  if (valid) {
+    a = *reinterpret_cast<const u32x2*>(row + 16 * s + 4 * h);
+    b = *reinterpret_cast<const u32x2*>(row + 16 * s + 8 + 4 * h);
+  }
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 template <bool F32, int D, int KMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const typename QFrag<F32>::In* __restrict__ Q, const uint8_t* __restrict__ prep,
-    int32_t* __restrict__ idx, float* __restrict__ kth, int64_t n, int g, int hq, int hkv,
-    int B, int64_t nb, int k, int64_t n_tiles, int64_t n_bkv) {
+    const uint32_t* __restrict__ qmax, int32_t* __restrict__ idx, float* __restrict__ kth,
+    int64_t n, int g, int hq, int hkv, int B, int64_t nb, int k, int64_t n_tiles,
+    int64_t n_bkv) {
   using Lay = RouteLayout<D>;
   using QT = typename QFrag<F32>::T;
   constexpr int MT = Lay::MT, NS = Lay::NS, BYTES = Lay::BLOCK_BYTES;
@@ -165,16 +211,48 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int64_t rows_total = n * g;
   const int64_t rho0 = tile * kRouteRows;
 
-  // query fragments of this lane's two 32-row tiles
+  // query fragments of this lane's two 32-row tiles.  bfloat16 rows become
+  // float16 (exact in the normal range) after scaling by 2^-eq, which brings
+  // the KV head's largest |q| into [2^14, 2^15); the images' mu carry the same
+  // factor.
   QT bq[2][NS];
+  float qsc = 1.f, qsq = 1.f;   // 2^-eq and 2^(2 eq)
+  if constexpr (!F32) {
+    const int eq = query_exponent(qmax[bkv]);
+    qsc = ldexpf(1.f, -eq);
+    qsq = ldexpf(1.f, 2 * eq);
+  }
+  {
+    const int64_t rows_of[2] = {rho0 + 64 * wave + ln, rho0 + 64 * wave + 32 + ln};
+    if constexpr (F32) {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t rho = rho0 + 64 * wave + 32 * nt + ln;
-    const bool valid = rho < rows_total;
-    const int64_t t = valid ? rho / g : 0, jg = valid ? rho % g : 0;
-    const auto* row = Q + (((b * hq + kv * g + jg) * n) + t) * D;
+      for (int nt = 0; nt < 2; ++nt) {
+        const int64_t rho = rows_of[nt];
+        const bool valid = rho < rows_total;
+        const int64_t t = valid ? rho / g : 0, jg = valid ? rho % g : 0;
+        const auto* row = Q + (((b * hq + kv * g + jg) * n) + t) * D;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) bq[nt][s] = load_q_frag<F32>(row, s, h, valid);
+        for (int s = 0; s < NS; ++s) bq[nt][s] = load_q_frag<F32>(row, s, h, valid);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int64_t rho = rows_of[nt];
+        const bool valid = rho < rows_total;
+        const int64_t t = valid ? rho / g : 0, jg = valid ? rho % g : 0;
+        const auto* row = Q + (((b * hq + kv * g + jg) * n) + t) * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const u32x4 raw = load_q_bits(row, s, h, valid);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t u = raw[w];
+            bq[nt][s][2 * w] = static_cast<_Float16>(bf16_bits_to_f32(u & 0xFFFFu) * qsc);
+            bq[nt][s][2 * w + 1] = static_cast<_Float16>(bf16_bits_to_f32(u >> 16) * qsc);
+          }
+        }
+      }
+    }
   }
   // the row this lane scores and ranks
   const int64_t my_rho = rho0 + 64 * wave + 32 * h + ln;
@@ -255,12 +333,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     pt[nt] = fmaf(acc[set][nt][j], QFrag<F32>::elem(bq[nt][2 * mt + (a >> 1)], 4 * (a & 1) + bb),
                   pt[nt]);
   };
-  // both lane halves combined: the score of this lane's row for block cb
+  // both lane halves combined: the score of this lane's row for block cb,
+  // times cb's image scale (blk_scale; the wave's common 2^(2 eq) stays out)
+  float blk_scale = 1.f;
   auto reduce = [&](int64_t cb) {
     const float p0 = pt[0] + wave_shfl_xor(pt[0], 32);
     const float p1 = pt[1] + wave_shfl_xor(pt[1], 32);
     pt[0] = pt[1] = 0.f;
-    sc_ins = (cb >= 0 && cb < my_C) ? (h ? p1 : p0) : -__builtin_inff();
+    sc_ins = (cb >= 0 && cb < my_C) ? (h ? p1 : p0) * blk_scale : -__builtin_inff();
     ci_ins = int(cb);
   };
   // one step of the running top-(k+1) insertion; strict > keeps the earlier
@@ -276,6 +356,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   };
 
   auto sweep = [&](int64_t c, const uint8_t* L) {
+    const float scale_c = *reinterpret_cast<const float*>(L + Lay::SCALE_OFF);
     // the query fragments are loop-invariant; an empty register constraint
     // stops the compiler from hoisting their float32 conversions (for the
     // row-dot) out of the loop, which would need 128 more registers
@@ -338,6 +419,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
       }
       pslot = (pslot + mt + 1) & 1;
     }
+    blk_scale = scale_c;   // the next reduction is this block's
   };
   for (int64_t c = 0; c < C_wg; ++c) {
     if (c + 1 < C_wg) stage(c + 1, lds + ((c + 1) & 1) * Lay::LDS_BYTES);
@@ -378,8 +460,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     float r_k = -__builtin_inff(), r_k1 = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i <= KMAX; ++i) {
-      if (i == k - 1) r_k = ls[i];
-      if (i == k) r_k1 = ls[i];
+      if (i == k - 1) r_k = ls[i] * qsq;
+      if (i == k) r_k1 = ls[i] * qsq;
     }
     kth[orow * 2] = r_k;
     kth[orow * 2 + 1] = r_k1;
@@ -392,9 +474,21 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
   using Lay = RouteLayout<D>;
   const int64_t n_bkv = int64_t(s.b) * s.hkv;
   uint8_t* prep = static_cast<uint8_t*>(ws);
+  // per (sequence, KV head): the largest |q| of its query rows (bfloat16
+  // bits), which sets the float16 scale of Q (the group's rows are contiguous)
+  uint32_t* qmax =
+      reinterpret_cast<uint32_t*>(prep + align_up(size_t(n_bkv * s.nb) * Lay::BLOCK_BYTES + 1024));
+  if constexpr (!F32) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<int32_t*>(qmax),
+                       n_bkv, 0);
+    const int64_t per_group = int64_t(s.g) * s.n * D;
+    const unsigned gx = unsigned(std::min<int64_t>((per_group / 8 + 255) / 256, 64));
+    hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
+                       static_cast<const bf16_t*>(Q), qmax, per_group);
+  }
   if (s.nb > 0) {
     hipLaunchKernelGGL((route_prep_kernel<F32, D>), dim3(unsigned(s.nb), unsigned(n_bkv)),
-                       dim3(256), 0, st, mu, sigma, prep, s.nb, s.beta);
+                       dim3(256), 0, st, mu, sigma, qmax, prep, s.nb, s.beta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -403,8 +497,8 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
   constexpr size_t shmem = 0;   // the kernel's LDS buffers are static
   using In = typename QFrag<F32>::In;
   hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles * n_bkv)), dim3(kRouteThreads), shmem, st,
-                     static_cast<const In*>(Q), prep, idx, kth, s.n, s.g, s.hq, s.hkv, s.B, s.nb,
-                     s.k, n_tiles, n_bkv);
+                     static_cast<const In*>(Q), prep, qmax, idx, kth, s.n, s.g, s.hq, s.hkv, s.B,
+                     s.nb, s.k, n_tiles, n_bkv);
   return hipGetLastError();
 }
 
@@ -420,8 +514,10 @@ hipError_t launch_route_d(const Shape& s, const void* Q, const float* mu, const 
 
 size_t route_workspace_bytes(const Shape& s) {
   const size_t per = s.d == 64 ? RouteLayout<64>::BLOCK_BYTES : RouteLayout<128>::BLOCK_BYTES;
-  // + 1 KB: the DMA of the last image reads up to one row past its end
-  return align_up(size_t(s.b) * s.hkv * size_t(s.nb) * per + 1024);
+  // + 1 KB: the DMA of the last image reads up to one row past its end; then
+  // the largest |q| of every (sequence, KV head)
+  return align_up(size_t(s.b) * s.hkv * size_t(s.nb) * per + 1024) +
+         align_up(size_t(s.b) * s.hkv * 4);
 }
 
 hipError_t launch_route_topk(const Shape& s, const void* Q, const float* mu, const float* sigma,

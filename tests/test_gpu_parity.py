@@ -255,3 +255,37 @@ def test_decode_f32_d64():
                                         dtype="f32", block=128, top_k=3, window=100, plants=3)
     say("case decode f32 d64 L=700")
     _decode_case(wl, 700, cap=1024, steps=2)
+
+
+@pytest.mark.parametrize("qexp", [18, -30])
+def test_route_query_scale(qexp):
+    """Routing of a KV head whose queries are scaled by 2^qexp (|q| far above
+    the float16 range, or far below its normal range): the selections equal
+    the oracle's on the scaled inputs (the router rescales Q per (sequence,
+    KV head) by an exact power of two)."""
+    wl = SMALL["bf16_gqa"].replace(top_k=4)
+    say(f"case route with queries of KV head 1 scaled by 2^{qexp}")
+    data = make_prefill(wl, seed=9)
+    g = wl.group
+    data["Q"][:, g:2 * g] = (data["Q"][:, g:2 * g].float() * 2.0 ** qexp).to(torch.bfloat16)
+    Q, K = data["Q"].to(DEV), data["K"].to(DEV)
+    mu, sigma = ssa.ssa_block_stats(K, wl.block)
+    idx, kth = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta,
+                                  want_kth=True)
+    torch.cuda.synchronize()
+    idx_h, kth_h = idx.cpu().numpy(), kth.cpu().numpy()
+    n_exact = n_tie = 0
+    for kv in range(wl.n_kv_heads):
+        muo, sgo = O.block_stats(O.as_f64(data["K"][0, kv]), wl.block)
+        for h in range(kv * g, (kv + 1) * g):
+            for t in range(0, wl.seq_len, 7):
+                C = O.routable_blocks(t, wl.block, muo.shape[0])
+                r = O.route_scores(O.as_f64(data["Q"][0, h, t]), muo[:C], sgo[:C], wl.beta)
+                sel, rk, rk1 = O.select_topk(r, wl.top_k)
+                ok, exact = idx_ok(idx_h[0, h, t], dict(idx=sel, scores=r, r_k=rk, r_k1=rk1))
+                assert ok, f"selection mismatch at {(h, t)}: {idx_h[0, h, t]} vs {sel}"
+                n_exact += exact
+                n_tie += not exact
+                if C > wl.top_k:   # the k-th score, in the scaled inputs' own units
+                    assert abs(kth_h[0, h, t, 0] - rk) <= 1e-5 * np.abs(r).max(), (h, t)
+    say(f"  exact {n_exact}, near-ties {n_tie}")
