@@ -112,10 +112,12 @@ ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes);
  *   kth        [b, Hq, n, 2]   float32, written if not NULL: the k-th and
  *                              (k+1)-th largest scores (-inf where absent)
  *   workspace  >= ssa_workspace_size(p, SSA_OP_ROUTE) bytes of device memory
- * The scores are evaluated on MFMA in bfloat16 with float32 accumulation,
- * Sigma split into a high and a low bfloat16 part (float32 MFMA for
- * float32 inputs), so a selection can differ from an exact one only where
- * two scores are within a few 1e-6 relative of each other. */
+ * The scores are evaluated on the float16 MFMA with float32 accumulation:
+ * Q scaled by one power of two per (sequence, KV head) (exact for bfloat16
+ * values), Sigma scaled per block and split into a high and a low float16
+ * part (float32 MFMA for float32 inputs), so a selection can differ from an
+ * exact one only where two scores are within about 1e-6 relative of each
+ * other. */
 ssa_status ssa_route_topk(const ssa_params* p, const void* Q, const float* mu,
                           const float* sigma, int32_t* idx, float* kth, void* workspace,
                           size_t workspace_bytes, void* stream);
