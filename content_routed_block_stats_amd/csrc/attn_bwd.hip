@@ -39,7 +39,7 @@
 namespace ssa {
 namespace {
 
-constexpr int kBwdThreads = 512;     // 8 waves
+constexpr int kDqThreads = 256;      // dQ task pass: 4 waves, half a task; two workgroups per CU
 constexpr int kDkvThreads = 256;     // key pass: 4 waves, two workgroups per CU
 constexpr int kDkvRows = 64;         // rows staged per iteration of the key pass
 constexpr int kWinTile = 128;        // rows per tile of the window pass (4 waves x 32)
@@ -70,10 +70,11 @@ __device__ __forceinline__ void set_vf(VF<F32>& f, int e, float v) {
 }
 
 // ----------------------------------------------------------------- dq_task --
-// One workgroup (8 waves x 32 rows) per task; chunk images of the task's
-// block double-buffered in LDS (image A's K part, then all of image B).
+// Two workgroups (4 waves x 32 rows each) per task of up to 256 rows, two per
+// CU; chunk images of the task's block in LDS (image A's K part, then all of
+// image B), double-buffered where two workgroups still fit.
 template <bool F32, int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_task_kernel(
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_task_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Drow, const uint8_t* __restrict__ img_a,
     const uint8_t* __restrict__ img_b, const uint32_t* __restrict__ kmax, int64_t n_chunks,
@@ -83,16 +84,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_task_kernel(
   using A = AT<F32, D>;
   using Frag = typename A::Frag;
   constexpr int BUF = A::KBYTES + A::CHUNK;
-  constexpr int NBUF = 2 * BUF <= 128 * 1024 ? 2 : 1;   // float32, d = 128: one buffer
+  // double-buffered chunks only where two workgroups still fit a CU's LDS
+  constexpr int NBUF = 2 * BUF <= 64 * 1024 ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * BUF];
-  const int64_t task = blockIdx.x;
+  // two workgroups per task, 128 rows each, so that two share a CU and one's
+  // row gather overlaps the other's products
+  const int64_t task = blockIdx.x / 2;
+  const int half = blockIdx.x % 2;
   if (task >= task_count[0]) return;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int4 tk = tasks[task];
   const int64_t seg = tk.x, e0 = tk.y;
   const int rows = tk.z;
+  if (128 * half >= rows) return;
   const int64_t bkv = seg / nb, c = seg % nb, b = bkv / hkv, kv = bkv % hkv;
-  const int r = 32 * wave + ln;
+  const int r = 128 * half + 32 * wave + ln;
   const bool valid = r < rows;
   int64_t row = 0;
   if (valid) {
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_task_kernel(
   }
   const float l2 = valid ? lse[row] * kLog2e : 0.f;
   const float dr = valid ? Drow[row] : 0.f;
-  const bool wave_active = 32 * wave < rows;
+  const bool wave_active = 128 * half + 32 * wave < rows;
   const int cpb = B / kKeyChunk;
   const int64_t ch0 = c * cpb;
   const uint8_t* srca = img_a + bkv * n_chunks * A::CHUNK;
@@ -119,15 +125,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_task_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dq[i][j] = 0.f;
 
-  dma_copy(lds, srca + ch0 * A::CHUNK, A::KBYTES, tid, kBwdThreads);
-  dma_copy(lds + A::KBYTES, srcb + ch0 * A::CHUNK, A::CHUNK, tid, kBwdThreads);
+  dma_copy(lds, srca + ch0 * A::CHUNK, A::KBYTES, tid, kDqThreads);
+  dma_copy(lds + A::KBYTES, srcb + ch0 * A::CHUNK, A::CHUNK, tid, kDqThreads);
   __syncthreads();
   for (int q = 0; q < cpb; ++q) {
     uint8_t* L = lds + (q % NBUF) * BUF;
     if (NBUF == 2 && q + 1 < cpb) {
       uint8_t* Ln = lds + ((q + 1) % NBUF) * BUF;
-      dma_copy(Ln, srca + (ch0 + q + 1) * A::CHUNK, A::KBYTES, tid, kBwdThreads);
-      dma_copy(Ln + A::KBYTES, srcb + (ch0 + q + 1) * A::CHUNK, A::CHUNK, tid, kBwdThreads);
+      dma_copy(Ln, srca + (ch0 + q + 1) * A::CHUNK, A::KBYTES, tid, kDqThreads);
+      dma_copy(Ln + A::KBYTES, srcb + (ch0 + q + 1) * A::CHUNK, A::CHUNK, tid, kDqThreads);
     }
     if (wave_active) {
       auto fa = [&](const uint8_t* base, int mt, int s) {
@@ -170,8 +176,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_task_kernel(
     }
     __syncthreads();
     if (NBUF == 1 && q + 1 < cpb) {
-      dma_copy(lds, srca + (ch0 + q + 1) * A::CHUNK, A::KBYTES, tid, kBwdThreads);
-      dma_copy(lds + A::KBYTES, srcb + (ch0 + q + 1) * A::CHUNK, A::CHUNK, tid, kBwdThreads);
+      dma_copy(lds, srca + (ch0 + q + 1) * A::CHUNK, A::KBYTES, tid, kDqThreads);
+      dma_copy(lds + A::KBYTES, srcb + (ch0 + q + 1) * A::CHUNK, A::CHUNK, tid, kDqThreads);
       __syncthreads();
     }
   }
@@ -686,8 +692,8 @@ hipError_t launch_bwd_t(const Shape& s, const void* Qv, const void* Kv, const vo
   const bool use_disp = s.k > 0 && s.nb > 0;
   if (use_disp) {
     if ((e = launch_dispatch(s, idx, w.disp, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_task_kernel<F32, D>), dim3(unsigned(w.disp.max_tasks)),
-                       dim3(kBwdThreads), 0, st, Q, dO, lse, w.Drow, w.img_a, w.img_b, w.kmax,
+    hipLaunchKernelGGL((bwd_dq_task_kernel<F32, D>), dim3(unsigned(2 * w.disp.max_tasks)),
+                       dim3(kDqThreads), 0, st, Q, dO, lse, w.Drow, w.img_a, w.img_b, w.kmax,
                        w.n_chunks, w.disp.tasks, w.disp.task_count, w.disp.entries, w.dq_part, s.n,
                        s.g, s.hq, s.hkv, s.B, s.nb, scale2, s.scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
