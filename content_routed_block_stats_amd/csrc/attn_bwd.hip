@@ -470,7 +470,7 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
 // one (sequence, KV head): the window part of dQ over window keys outside the
 // row's selected blocks, then the row's dQ partials added.
 template <bool F32, int D>
-__global__ __launch_bounds__(256) void bwd_dq_window_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_window_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Drow, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ pos, const float* __restrict__ dq_part,
@@ -480,7 +480,8 @@ __global__ __launch_bounds__(256) void bwd_dq_window_kernel(
   using A = AT<F32, D>;
   using Frag = typename A::Frag;
   constexpr int BUF = A::KBYTES + A::CHUNK;
-  constexpr int NBUF = 2 * BUF <= 128 * 1024 ? 2 : 1;   // float32, d = 128: one buffer
+  // double-buffered chunks only where two workgroups still fit a CU's LDS
+  constexpr int NBUF = 2 * BUF <= 64 * 1024 ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * BUF];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int64_t bkv = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
