@@ -89,6 +89,22 @@ def counted_traffic(kernel: str, digest: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def counted_mfma_busy(prefix: str, digest: str):
+    """Share of SIMD cycles with the matrix core busy, from the committed
+    rocprofv3 counter summary of the routing kernel, or None if it changed."""
+    path = os.path.join(PROFILES, "gqa_prefill_128k_mfma_busy.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("route_topk_source_digest") != digest:
+        return None
+    for name, v in rec.get("kernels", {}).items():
+        if name.startswith(prefix):
+            return {"busy_frac": round(v["mfma_busy_frac"], 4), "clock_ghz": round(v["clock_ghz"], 3)}
+    return None
+
+
 def cpu_baseline(wl, data, seconds: float) -> dict:
     """Time the CPU oracle on a bounded sample of the workload (one thread)."""
     import numpy as np
@@ -431,6 +447,7 @@ def main() -> int:
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": counted_traffic("route_topk", route_digest),
+                     "mfma_busy_counted": counted_mfma_busy("route_topk_kernel", route_digest),
                      "algorithmic_flops_per_launch": rf},
         "roofline_gather": {"kernel": "sparse_attn_fwd", "bound": "hbm", "achieved": round(gbs, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
