@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   // while the vector units work, whatever the other wave on the SIMD does.
   // Operand fragments are read from LDS two steps ahead; each tile's first
   // MFMA takes mu as its accumulator input.
-  constexpr int PARTS = F32 ? 1 : 2;               // bf16: high and low part of T
+  constexpr int PARTS = F32 ? 1 : 2;               // float16: high and low part of T
   constexpr int NFR = Lay::NF * PARTS;             // fragment reads per block
   constexpr int NDOT = 32;                         // row-dot FMAs per tile (2 tiles x 16)
   floatx16 acc[2][2];                              // [set][nt]; tile mt uses set (MT-1-mt)&1
@@ -358,8 +358,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   auto sweep = [&](int64_t c, const uint8_t* L) {
     const float scale_c = *reinterpret_cast<const float*>(L + Lay::SCALE_OFF);
     // the query fragments are loop-invariant; an empty register constraint
-    // stops the compiler from hoisting their float32 conversions (for the
-    // row-dot) out of the loop, which would need 128 more registers
+    // keeps the compiler from hoisting float32 copies of them (for the
+    // row-dot) out of the loop, which would need 128 more registers -- the
+    // row-dot reads the float16 fragments with mixed-precision FMAs instead
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
