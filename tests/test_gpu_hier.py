@@ -52,6 +52,10 @@ CASES = {
     # m = 1: every group is one block (R = lam = 0, the bound is the score)
     "bf16_m1": (_DEC.replace(batch=1, n_q_heads=4, n_kv_heads=2, seq_len=128 * 40 + 100,
                              block=128, top_k=8, window=128, plants=2), 1),
+    # beta = 0 (the centroid score: no covariance term in score or bound), d = 64
+    "bf16_d64_beta0_m8": (_DEC.replace(batch=2, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                                       seq_len=64 * 200 + 3, block=64, top_k=8, window=64,
+                                       beta=0.0, plants=4), 8),
     # clustered keys, d = 128, g = 4, m = 16: most groups pruned
     "bf16_clustered_m16": (_DEC.replace(batch=2, n_q_heads=8, n_kv_heads=2, seq_len=64 * 512,
                                         block=64, top_k=8, window=64, **_CLUSTER), 16),
