@@ -22,11 +22,9 @@ template <typename TIn, int D>
 __global__ __launch_bounds__(kThreads) void block_stats_kernel(
     const TIn* __restrict__ K, float* __restrict__ mu, float* __restrict__ sigma, int64_t n,
     int B, int64_t n_slots, int hkv, const int32_t* __restrict__ cache_len) {
-  constexpr int G = kThreads / D;        // key groups in pass 1
   constexpr int TS = D / 16;             // Sigma tile per thread: TS x TS
-  __shared__ float red[kThreads];
   __shared__ float smu[D];
-  __shared__ float X[kChunk][D + 4];
+  __shared__ __attribute__((aligned(16))) float X[kChunk][D + 4];
 
   const int tid = threadIdx.x;
   const int64_t bkv = blockIdx.y;
@@ -41,18 +39,49 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(
   }
   const TIn* Kb = K + (bkv * n + c * B) * D;
 
-  // pass 1: mean
+  // 16-byte pieces of a key row: EP elements each, PPR per row
+  constexpr int EP = 16 / int(sizeof(TIn));
+  constexpr int PPR = D / EP;
+  constexpr int RSTEP = kThreads / PPR;  // rows per step of pass 1
+  static_assert(RSTEP * D <= kChunk * (D + 4), "pass-1 partial sums fit the chunk buffer");
+  auto piece = [&](int64_t j, int pc, float (&v)[EP]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(Kb + j * D + pc * EP);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (EP == 8) {
+        v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      } else {
+        // copy the element out first: bit-casting a vector element lvalue
+        // directly reads element 0 with this compiler
+        const uint32_t u = w[i];
+        v[i] = __builtin_bit_cast(float, u);
+      }
+    }
+  };
+
+  // pass 1: mean (each thread sums one piece column over every RSTEP-th row)
   {
-    const int col = tid % D, grp = tid / D;
-    float s = 0.f;
-    for (int j = grp; j < B; j += G) s += load_f32(Kb, int64_t(j) * D + col);
-    red[tid] = s;
+    const int pc = tid % PPR, rg = tid / PPR;
+    float sv[EP];
+#pragma unroll
+    for (int i = 0; i < EP; ++i) sv[i] = 0.f;
+    for (int j = rg; j < B; j += RSTEP) {
+      float v[EP];
+      piece(j, pc, v);
+#pragma unroll
+      for (int i = 0; i < EP; ++i) sv[i] += v[i];
+    }
+    float* part = &X[0][0];   // [rg][D]
+#pragma unroll
+    for (int i = 0; i < EP; ++i) part[rg * D + pc * EP + i] = sv[i];
   }
   __syncthreads();
   if (tid < D) {
+    const float* part = &X[0][0];
     float s = 0.f;
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) s += red[gi * D + tid];
+    for (int gi = 0; gi < RSTEP; ++gi) s += part[gi * D + tid];
     const float m = s / float(B);
     smu[tid] = m;
     mu[(bkv * n_slots + c) * D + tid] = m;
@@ -68,9 +97,15 @@ __global__ __launch_bounds__(kThreads) void block_stats_kernel(
     for (int j = 0; j < TS; ++j) acc[i][j] = 0.f;
 
   for (int j0 = 0; j0 < B; j0 += kChunk) {
-    for (int e = tid; e < kChunk * D; e += kThreads) {
-      const int r = e / D, col = e % D;
-      X[r][col] = load_f32(Kb, int64_t(j0 + r) * D + col) - smu[col];
+    for (int e = tid; e < kChunk * PPR; e += kThreads) {
+      const int r = e / PPR, pc = e % PPR;
+      float v[EP];
+      piece(j0 + r, pc, v);
+#pragma unroll
+      for (int i = 0; i < EP; i += 4)
+        *reinterpret_cast<floatx4*>(&X[r][pc * EP + i]) =
+            floatx4{v[i] - smu[pc * EP + i], v[i + 1] - smu[pc * EP + i + 1],
+                    v[i + 2] - smu[pc * EP + i + 2], v[i + 3] - smu[pc * EP + i + 3]};
     }
     __syncthreads();
 #pragma unroll 4
