@@ -43,6 +43,8 @@ constexpr int kDqThreads = 256;      // dQ task pass: 4 waves, half a task; two 
 constexpr int kDkvThreads = 256;     // key pass: 4 waves, two workgroups per CU
 constexpr int kDkvRows = 64;         // rows staged per iteration of the key pass
 constexpr int kWinTile = 128;        // rows per tile of the window pass (4 waves x 32)
+constexpr int kDkvWideThreads = 512;  // key pass over chunk pairs: 8 waves, one workgroup per CU
+constexpr int kDkvWideWinRows = 16384;  // window rows a chunk pair can have (a byte of LDS each)
 
 // ------------------------------------------------------------------ rowdot --
 template <typename InT, typename OutT>
@@ -465,6 +467,329 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
 }
 
+// ---------------------------------------------------------- dkv_chunk_pair --
+// The same pass for bfloat16 inputs at d = 128 when blocks hold a multiple of
+// 128 keys: one workgroup of 8 waves (key quarter kq = wave % 4, row group
+// rg = wave / 4) owns two consecutive chunks, so every staged row serves 128
+// keys and a CU holds one workgroup.  The LDS this frees holds a second row
+// buffer: the next batch's rows are copied global -> LDS directly (no
+// registers) during the whole of the current batch, whose barriers wait for
+// LDS traffic only.  No ordinary load is waited for while such a copy is in
+// flight except at the end of a batch, where the copy has to be complete
+// anyway (the compiler counts the copies as stores, so any such wait drains
+// them): row information is loaded two batches ahead and stored at the end
+// of a batch, and whether a window row's selection holds the block is
+// decided once, in the prologue, into a byte per window row.  Padded rows are copied whole: the padding
+// slot of a row repeats its last 16 bytes.
+
+// Workgroup barrier over LDS accesses only: global loads still in flight
+// (the global -> LDS row copies among them) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(kDkvWideThreads) void bwd_dkv_wide_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ Drow, const int32_t* __restrict__ idx,
+    const uint8_t* __restrict__ img_a, const uint8_t* __restrict__ img_b,
+    const uint32_t* __restrict__ qmax, const uint32_t* __restrict__ domax, int64_t n_chunks,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ cursor,
+    const uint32_t* __restrict__ entries, float* __restrict__ dK, float* __restrict__ dV, int64_t n,
+    int g, int hq, int hkv, int B, int64_t nb, int k, int W, float scale2, float scale,
+    int64_t n_work) {
+  using A = AT<false, D>;
+  using Frag = typename A::Frag;
+  constexpr int ES = 2;
+  constexpr int ROWB = D * ES;
+  constexpr int RSTR = ROWB + 16;           // padded row stride, as in the chunk pass
+  constexpr int SLOTS = RSTR / 16;          // 16-byte slots per staged row (the last is padding)
+  constexpr int ROWS = kDkvRows;
+  constexpr int TRS = ROWS + 4;
+  constexpr int TBYTES = ROWS * RSTR;       // one tensor's staged rows
+  constexpr int NCOPY = TBYTES / 1024;      // 1 KB global -> LDS copies per tensor
+  constexpr int KEYS = 2 * kKeyChunk;
+  constexpr int NW = kDkvWideThreads / 64;
+  static_assert(TBYTES % 1024 == 0, "row buffers are whole 1 KB copies");
+  static_assert(D * TRS * 2 <= TBYTES, "transposed copy");
+  static_assert(4 * A::KBYTES >= KEYS * D * 4, "reduction buffer");
+  static_assert(ROWS == 64 && NW == 8 && D == 128, "unit map: 32 row pairs x 16 column groups over 8 waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t img[4 * A::KBYTES];    // K rows of both chunks, then V rows
+  // row buffers of even and odd batches (Q rows, then dO rows); two separate
+  // arrays, so that reads of one are known not to touch the copy into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t rbuf0[2 * TBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t rbuf1[2 * TBYTES];
+  // per staged row: the keys it attends here, (lo, hi], its LSE and D; its
+  // index for the row copy
+  __shared__ __attribute__((aligned(16))) int32_t rlo[2][ROWS], rhi[2][ROWS];
+  __shared__ __attribute__((aligned(16))) float rlse[2][ROWS], rd[2][ROWS];
+  __shared__ int64_t rrow[2][ROWS];
+  __shared__ uint8_t wmode[kDkvWideWinRows];   // window row w: 1 = window keys count, 2 = none
+
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int kq = wave % 4, rg = wave / 4;
+  // consecutive work items (the chunk pairs of one block) go to one XCD
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t wi = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (wi >= n_work) return;
+  const int64_t n_pairs = (n_chunks + 1) / 2;
+  const int64_t ch = 2 * (wi % n_pairs), bkv = wi / n_pairs;
+  const bool two = ch + 1 < n_chunks;       // else the second chunk lies past the sequence
+  const bool keys_here = two || kq < 2;
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  const int64_t key0 = ch * kKeyChunk;
+  const int64_t c = key0 / B;
+  int64_t sel_start = 0, sel_cnt = 0;
+  if (c < nb) {
+    const int64_t sg = bkv * nb + c;
+    sel_cnt = counts[sg];
+    sel_start = cursor[sg] - sel_cnt;
+  }
+  const int64_t t_hi = min(n - 1, key0 + KEYS - 1 + W - 1);
+  const int64_t win_cnt = (t_hi - key0 + 1) * g;
+  const int64_t total = sel_cnt + win_cnt;
+  uint32_t mq = 0, md = 0;
+  for (int j = 0; j < g; ++j) {
+    mq = max(mq, qmax[b * hq + kv * g + j]);
+    md = max(md, domax[b * hq + kv * g + j]);
+  }
+  const int eq = value_exponent(mq), edo = value_exponent(md);
+  const float sq = ldexpf(1.f, -eq), sdo = ldexpf(1.f, -edo);
+
+  // Row i of this work item (the block's selected rows, then the window
+  // rows), in three steps: pre() loads a selected row's entry; issue() sends
+  // the remaining loads and only keeps their values; settle() stores them
+  // with the mode (0 = every key counts, 1 = window keys, 2 = none).
+  struct Pend {
+    int64_t row;   // -1 past the end
+    int32_t pos;
+    float l, dd;
+  };
+  // (every lane loads, from row 0 where it has no row: a load under a
+  // divergent branch would make the other branch's writes to its registers
+  // wait for it)
+  auto pre = [&](int64_t i) -> uint32_t {
+    return sel_cnt > 0 ? entries[sel_start + min(i, sel_cnt - 1)] : 0u;
+  };
+  auto issue = [&](int64_t i, uint32_t en) {
+    Pend p;
+    const bool is_sel = i < sel_cnt;
+    const int64_t rho = en >> 5, w = i - sel_cnt;
+    const int64_t pos = is_sel ? rho / g : key0 + w / g;
+    const int64_t row = (b * hq + kv * g + (is_sel ? rho % g : w % g)) * n + pos;
+    p.pos = int32_t(pos);
+    p.row = i < total ? row : -1;
+    const int64_t sr = i < total ? row : 0;
+    p.l = lse[sr];
+    p.dd = Drow[sr];
+    return p;
+  };
+  auto settle = [&](int slot, int64_t i, const Pend& p) {
+    const int mode = i < sel_cnt ? 0 : (i < total ? int(wmode[i - sel_cnt]) : 2);
+    // (the loaded values are stored as they are: arithmetic on them could be
+    // moved up to the loads, and its wait with it)
+    const int32_t last = int32_t(n - 1);   // keys past the sequence never count
+    rrow[slot][tid] = mode == 2 ? -1 : p.row;
+    rlo[slot][tid] = mode == 0 ? INT32_MIN : (mode == 1 ? p.pos - W : 0);
+    rhi[slot][tid] = mode == 0 ? last : (mode == 1 ? min(p.pos, last) : -1);
+    rlse[slot][tid] = p.l;
+    rd[slot][tid] = p.dd;
+  };
+  // Copy a batch's Q and dO rows into a row buffer (its row list is info
+  // slot `slot`): copy j fills 1 KB of staged rows, lane l one 16-byte slot.
+  // Rows that take no part read row 0; their p and dS are 0.  Every wave
+  // issues the same number of copies (the last ones repeat copies of other
+  // waves with identical bytes), so waits on later loads can count them.
+  constexpr int PER_WAVE = (2 * NCOPY + NW - 1) / NW;
+  auto stage_rows = [&](uint8_t* buf, int slot) {
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      int j = wave + NW * u;
+      if (j >= 2 * NCOPY) j -= 2 * NCOPY;
+      const int s = (j % NCOPY) * 64 + lane;
+      const int rr = s / SLOTS, pc = min(s % SLOTS, ROWB / 16 - 1);
+      const int64_t row = max(rrow[slot][rr], int64_t(0));
+      const bf16_t* src = (j < NCOPY ? Q : dO) + row * D;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + pc * 16,
+                                       (__attribute__((address_space(3))) void*)(buf + (j / NCOPY) * TBYTES +
+                                                                                 (j % NCOPY) * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  {
+    const uint8_t* ia = img_a + (bkv * n_chunks + ch) * A::CHUNK;
+    const uint8_t* ib = img_b + (bkv * n_chunks + ch) * A::CHUNK;
+    dma_copy(img, ia, A::KBYTES, tid, kDkvWideThreads);
+    dma_copy(img + 2 * A::KBYTES, ib, A::KBYTES, tid, kDkvWideThreads);
+    if (two) {
+      dma_copy(img + A::KBYTES, ia + A::CHUNK, A::KBYTES, tid, kDkvWideThreads);
+      dma_copy(img + 3 * A::KBYTES, ib + A::CHUNK, A::KBYTES, tid, kDkvWideThreads);
+    }
+  }
+  for (int64_t w = tid; w < win_cnt; w += kDkvWideThreads) {
+    const int64_t row = (b * hq + kv * g + w % g) * n + key0 + w / g;
+    bool sel = false;
+    for (int q = 0; q < k; ++q) sel |= idx[row * k + q] == int32_t(c);
+    wmode[w] = sel ? 2 : 1;
+  }
+  __syncthreads();   // window modes
+  uint32_t en_next = 0;
+  if (tid < ROWS) {
+    settle(0, tid, issue(tid, pre(tid)));
+    settle(1, ROWS + tid, issue(ROWS + tid, pre(ROWS + tid)));
+    en_next = pre(2 * ROWS + tid);
+  }
+  __syncthreads();   // row lists of batches 0 and 1
+  stage_rows(rbuf0, 0);
+
+  floatx16 dk[A::MTD], dv[A::MTD];
+#pragma unroll
+  for (int i = 0; i < A::MTD; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dk[i][j] = dv[i][j] = 0.f;
+  const int32_t mk = int32_t(key0 + 32 * kq + ln);   // this lane's key
+
+  // one batch; CUR = its parity (which row buffer and info slot it uses)
+  auto step = [&](auto parity, int64_t i0) {
+    constexpr int cur = decltype(parity)::value;
+    uint8_t* const rq = cur == 0 ? rbuf0 : rbuf1;
+    uint8_t* const rdo = rq + TBYTES;
+    __syncthreads();   // this batch's rows have landed; the next batch's row list is in
+    // the next batch's rows, into the other buffer (every wave finished with
+    // it in the last batch; past the last batch the copy lands where nobody
+    // reads), then the row information of the batch after it
+    stage_rows(cur == 0 ? rbuf1 : rbuf0, cur ^ 1);
+    Pend pend{-1, 0, 0.f, 0.f};
+    if (tid < ROWS) {
+      pend = issue(i0 + 2 * ROWS + tid, en_next);
+      en_next = pre(i0 + 3 * ROWS + tid);
+    }
+
+    const int r0 = 32 * rg;
+    const bool active = keys_here && i0 + r0 < total;
+    floatx16 sacc, pacc;
+    if (active) {
+      // S = Q K^T and dP = dO V^T for this wave's 32 rows x 32 keys (lanes on keys)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
+#pragma unroll
+      for (int s = 0; s < A::NS; ++s) {
+        const Frag kf = *reinterpret_cast<const Frag*>(img + (kq * A::NS + s) * A::FRAG + lane * 8 * ES);
+        const Frag vf = *reinterpret_cast<const Frag*>(img + 2 * A::KBYTES + (kq * A::NS + s) * A::FRAG +
+                                                       lane * 8 * ES);
+        const Frag qa = *reinterpret_cast<const Frag*>(rq + (r0 + ln) * RSTR + (16 * s + 8 * h) * ES);
+        const Frag da = *reinterpret_cast<const Frag*>(rdo + (r0 + ln) * RSTR + (16 * s + 8 * h) * ES);
+        sacc = mma16(qa, kf, sacc);
+        pacc = mma16(da, vf, pacc);
+      }
+      // element j: row r0 + 8(j/4) + 4h + j%4, key mk.  Everything is read
+      // and computed for every element and the mask applied by a select (a
+      // conditional exponential becomes a branch per element, each waiting
+      // for its own reads)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int rr = r0 + 8 * (j / 4) + 4 * h + j % 4;
+        const int32_t lo = rlo[cur][rr], hi = rhi[cur][rr];
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[j], scale2, -rlse[cur][rr] * kLog2e));
+        const float p = (mk > lo) & (mk <= hi) ? e : 0.f;
+        sacc[j] = p;
+        pacc[j] = p * (pacc[j] - rd[cur][rr]);
+        // four rows' reads in flight at a time: all sixteen at once would
+        // not fit in the registers left beside the accumulators
+        if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Q^T and dO^T as scaled float16, [column][row] (TRS halves per column),
+    // written over the row-major copy once every wave has read it.  Thread
+    // unit: rows 2 rp, 2 rp + 1 and columns [8 pc, 8 pc + 8).
+    const int rp = 8 * (wave % 4) + lane % 8, pc = lane / 8 + 8 * (wave / 4);
+    u32x4 pq[2], pd[2];
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      pq[o] = *reinterpret_cast<const u32x4*>(rq + (2 * rp + o) * RSTR + pc * 16);
+      pd[o] = *reinterpret_cast<const u32x4*>(rdo + (2 * rp + o) * RSTR + pc * 16);
+    }
+    lds_barrier();   // every wave has read the row-major copy
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sh = 16 * (i % 2);
+      const float q0 = __builtin_bit_cast(float, ((pq[0][i / 2] >> sh) & 0xFFFFu) << 16) * sq;
+      const float q1 = __builtin_bit_cast(float, ((pq[1][i / 2] >> sh) & 0xFFFFu) << 16) * sq;
+      const float d0 = __builtin_bit_cast(float, ((pd[0][i / 2] >> sh) & 0xFFFFu) << 16) * sdo;
+      const float d1 = __builtin_bit_cast(float, ((pd[1][i / 2] >> sh) & 0xFFFFu) << 16) * sdo;
+      const uint32_t wq = uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(q0))) |
+                          (uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(q1))) << 16);
+      const uint32_t wd = uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(d0))) |
+                          (uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(d1))) << 16);
+      const int at = ((8 * pc + i) * TRS + 2 * rp) * 2;
+      *reinterpret_cast<uint32_t*>(rq + at) = wq;
+      *reinterpret_cast<uint32_t*>(rdo + at) = wd;
+    }
+    lds_barrier();   // the transposed copies are complete
+    if (active) {
+      // dV^T += dO^T P and dK^T += Q^T dS: rows contracted in frag_k order
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        f16x8 pf, sf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 4 * (2 * sp + (e >> 2)) + (e & 3);
+          pf[e] = static_cast<_Float16>(sacc[j]);
+          sf[e] = static_cast<_Float16>(pacc[j]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < A::MTD; ++mt) {
+          // rows r0 + frag_k(sp, h, e): 4 consecutive rows, then 4 more 8 rows on
+          const int col = 32 * mt + ln;
+          const int at = (col * TRS + r0 + 16 * sp + 4 * h) * 2;
+          const uint2 q_lo = *reinterpret_cast<const uint2*>(rq + at);
+          const uint2 q_hi = *reinterpret_cast<const uint2*>(rq + at + 16);
+          const uint2 d_lo = *reinterpret_cast<const uint2*>(rdo + at);
+          const uint2 d_hi = *reinterpret_cast<const uint2*>(rdo + at + 16);
+          const f16x8 qt = __builtin_bit_cast(f16x8, u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y});
+          const f16x8 dt = __builtin_bit_cast(f16x8, u32x4{d_lo.x, d_lo.y, d_hi.x, d_hi.y});
+          dv[mt] = mma16(dt, pf, dv[mt]);
+          dk[mt] = mma16(qt, sf, dk[mt]);
+        }
+      }
+    }
+    // batch i0 / ROWS + 2 takes this batch's slot (its waits fall where the
+    // next barrier waits for the row copy anyway)
+    if (tid < ROWS) settle(cur, i0 + 2 * ROWS + tid, pend);
+  };
+  for (int64_t i0 = 0; i0 < total; i0 += 2 * ROWS) {
+    step(std::integral_constant<int, 0>{}, i0);
+    if (i0 + ROWS < total) step(std::integral_constant<int, 1>{}, i0 + ROWS);
+  }
+  __syncthreads();
+
+  // the two row groups' partial sums, added in LDS in a fixed order (float32,
+  // 128 keys x D, over the K/V rows): the result does not depend on scheduling
+  float* red = reinterpret_cast<float*>(img);
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int round = 0; round < 2; ++round) {
+      if (rg == round) {
+#pragma unroll
+        for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int col = 32 * mt + 8 * (j / 4) + 4 * h + j % 4;
+            float* slot = &red[(32 * kq + ln) * D + col];
+            const float v = pass == 0 ? dk[mt][j] : dv[mt][j];
+            *slot = round == 0 ? v : *slot + v;
+          }
+      }
+      __syncthreads();
+    }
+    const float f = pass == 0 ? ldexpf(scale, eq) : ldexpf(1.f, edo);
+    float* dst = (pass == 0 ? dK : dV) + (bkv * n + key0) * D;
+    for (int w = tid; w < KEYS * D; w += kDkvWideThreads)
+      if (key0 + w / D < n) dst[w] = red[w] * f;
+    __syncthreads();
+  }
+}
+
 // --------------------------------------------------------------- dq_window --
 // One workgroup (4 waves x 32 rows) per tile of 128 rows (rho = t g + jg) of
 // one (sequence, KV head): the window part of dQ over window keys outside the
@@ -700,6 +1025,25 @@ hipError_t launch_bwd_t(const Shape& s, const void* Qv, const void* Kv, const vo
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t n_kv_work = n_bkv * w.n_chunks;
+  if constexpr (!F32 && D == 128) {
+    if (s.B % (2 * kKeyChunk) == 0 &&
+        (int64_t(2 * kKeyChunk) + s.W - 1) * s.g <= kDkvWideWinRows) {
+      const int64_t n_pair_work = n_bkv * ((w.n_chunks + 1) / 2);
+      hipLaunchKernelGGL((bwd_dkv_wide_kernel<D>), dim3(unsigned((n_pair_work + 7) / 8 * 8)),
+                         dim3(kDkvWideThreads), 0, st, Q, dO, lse, w.Drow, idx, w.img_a, w.img_b,
+                         w.qmax, w.domax, w.n_chunks, use_disp ? w.disp.counts : nullptr,
+                         use_disp ? w.disp.cursor : nullptr, use_disp ? w.disp.entries : nullptr,
+                         dK, dV, s.n, s.g, s.hq, s.hkv, s.B, use_disp ? s.nb : 0, s.k, s.W, scale2,
+                         s.scale, n_pair_work);
+    } else {
+      hipLaunchKernelGGL((bwd_dkv_kernel<F32, D>), dim3(unsigned((n_kv_work + 7) / 8 * 8)),
+                         dim3(kDkvThreads), 0, st, Q, dO, lse, w.Drow, idx, w.img_a, w.img_b,
+                         w.qmax, w.domax, w.n_chunks, use_disp ? w.disp.counts : nullptr,
+                         use_disp ? w.disp.cursor : nullptr, use_disp ? w.disp.entries : nullptr,
+                         dK, dV, s.n, s.g, s.hq, s.hkv, s.B, use_disp ? s.nb : 0, s.k, s.W, scale2,
+                         s.scale, n_kv_work);
+    }
+  } else
   hipLaunchKernelGGL((bwd_dkv_kernel<F32, D>), dim3(unsigned((n_kv_work + 7) / 8 * 8)),
                      dim3(kDkvThreads), 0, st, Q, dO, lse, w.Drow, idx, w.img_a, w.img_b, w.qmax,
                      w.domax, w.n_chunks, use_disp ? w.disp.counts : nullptr,

@@ -42,6 +42,12 @@ CASES = {
                                        block=192, top_k=2, window=100, plants=2),
     "bf16_B128_W300_ragged": _P32.replace(n_q_heads=2, n_kv_heads=1, seq_len=1000, top_k=4,
                                           window=300, plants=2),
+    # 17 key chunks: the last pair of chunks has only its first inside the sequence
+    "bf16_gqa_B256_odd_chunks": _GQA.replace(n_q_heads=8, n_kv_heads=2, seq_len=64 * 16 + 30,
+                                             top_k=3, plants=4),
+    # blocks of 192 keys (not a multiple of 128): one workgroup per 64-key chunk
+    "bf16_d128_B192": _P32.replace(n_q_heads=4, n_kv_heads=2, seq_len=900, block=192, top_k=2,
+                                   window=100, plants=2),
 }
 
 
