@@ -354,10 +354,14 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
         const int rr = r0 + 8 * (j / 4) + 4 * h + j % 4;
         const int mode = rmode[rr];
         const int64_t t = rpos[rr];
-        const bool on = my_key < n && (mode == 0 || (mode == 1 && my_key <= t && my_key > t - W));
-        const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[j], scale2, -rl2[rr])) : 0.f;
+        // (computed for every element and selected: a conditional exponential
+        // becomes a branch per element)
+        const bool on = (my_key < n) & ((mode == 0) | ((mode == 1) & (my_key <= t) & (my_key > t - W)));
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[j], scale2, -rl2[rr]));
+        const float p = on ? e : 0.f;
         sacc[j] = p;
         pacc[j] = p * (pacc[j] - rd[rr]);
+        if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // four rows' reads in flight at a time
       }
     }
     if constexpr (!F32) {
@@ -854,7 +858,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       bool excl = false;
       if (valid)
         for (int i = 0; i < k; ++i) excl |= idx[row * k + i] == blk;
-      const int64_t tv = valid && !excl ? t : -(int64_t(1) << 40);
+      // positions fit in 32 bits; a row that takes no window keys here gets a
+      // position no key reaches
+      const int32_t tv = valid && !excl ? int32_t(t) : -(1 << 30);
       auto fa = [&](const uint8_t* base, int mt, int s) {
         return *reinterpret_cast<const Frag*>(base + (mt * A::NS + s) * A::FRAG + lane * 8 * A::ES);
       };
@@ -874,10 +880,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int64_t kj = key0 + 32 * mt + 8 * (j / 4) + 4 * h + j % 4;
-          const bool on = kj <= tv && kj > tv - W;
-          const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[mt][j], scale2, -l2)) : 0.f;
+          const int32_t kj = int32_t(key0) + 32 * mt + 8 * (j / 4) + 4 * h + j % 4;
+          // (computed for every element and selected: a conditional
+          // exponential becomes a branch per element)
+          const bool on = (kj <= tv) & (kj > tv - W);
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][j], scale2, -l2));
+          const float p = on ? e : 0.f;
           sacc[mt][j] = p * (pacc[mt][j] - dr);
+          if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bounded register use
         }
       const uint8_t* kt = L + A::KBYTES + A::KBYTES;
 #pragma unroll
