@@ -696,7 +696,7 @@ __global__ __launch_bounds__(kDkvWideThreads) void bwd_dkv_wide_kernel(
         const int rr = r0 + 8 * (j / 4) + 4 * h + j % 4;
         const int32_t lo = rlo[cur][rr], hi = rhi[cur][rr];
         const float e = __builtin_amdgcn_exp2f(fmaf(sacc[j], scale2, -rlse[cur][rr] * kLog2e));
-        const float p = (mk > lo) & (mk <= hi) ? e : 0.f;
+        const float p = ((mk > lo) & (mk <= hi)) ? e : 0.f;
         sacc[j] = p;
         pacc[j] = p * (pacc[j] - rd[cur][rr]);
         // four rows' reads in flight at a time: all sixteen at once would
