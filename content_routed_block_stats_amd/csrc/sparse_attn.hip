@@ -389,6 +389,12 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
 
 // ----------------------------------------------------------- window + merge --
 
+// Whether the window/merge pass keeps the partials' positions of its tile in
+// its second chunk buffer (free once the window part is done).
+__host__ __device__ constexpr bool window_pos_in_chunk(int k, int chunk_bytes) {
+  return int64_t(k) * kWinRows * 4 <= chunk_bytes;
+}
+
 template <bool F32, int D, typename PartT, typename OutT>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void window_merge_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
@@ -400,8 +406,12 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   using A = AT<F32, D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int32_t* sidx = reinterpret_cast<int32_t*>(lds + 2 * A::CHUNK);   // [k][kWinRows]
-  int32_t* spos = sidx + kWinRows * k;                                // [k][kWinRows]
-  float2* wml = reinterpret_cast<float2*>(spos + kWinRows * k);       // window (m2, l) per row
+  float2* wml = reinterpret_cast<float2*>(sidx + kWinRows * k);       // window (m2, l) per row
+  // the partials' positions, [k][kWinRows]: loaded once the window part is
+  // done, into the second chunk buffer when they fit there (keeping the LDS
+  // of a workgroup within half a CU's), else after wml
+  int32_t* spos = window_pos_in_chunk(k, A::CHUNK) ? reinterpret_cast<int32_t*>(lds + A::CHUNK)
+                                                   : reinterpret_cast<int32_t*>(wml + kWinRows);
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   // workgroups are dealt round-robin over the 8 XCDs; give each XCD a
   // contiguous run of tiles so that neighbouring tiles, whose windows share
@@ -431,15 +441,9 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   for (int w = tid; w < kWinRows * k; w += kAttnThreads) {
     const int rr = w / k, i = w % k;   // coalesced idx reads, transposed LDS writes
     const int64_t rh = rho0 + rr;
-    int32_t v = -1, e = 0;
-    if (rh < rows_total) {
-      const int64_t tt = rh / g, jj = rh % g;
-      const int64_t at = ((b * hq + kv * g + jj) * n + tt) * k + i;
-      v = idx[at];
-      if (v >= 0) e = pos[at];
-    }
+    int32_t v = -1;
+    if (rh < rows_total) v = idx[((b * hq + kv * g + rh % g) * n + rh / g) * k + i];
     sidx[i * kWinRows + rr] = v;
-    spos[i * kWinRows + rr] = e;
   }
   typename A::Frag bq[1][A::NS];
   {
@@ -466,34 +470,67 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       const int32_t blk = int32_t(key0 / B);
       bool excl = false;
       for (int i = 0; i < k; ++i) excl |= sidx[i * kWinRows + r] == blk;
-      const int64_t tv = valid ? t : -(int64_t(1) << 40);
+      // 32-bit positions and bitwise tests: no exec-mask blocks per element
+      const int32_t tv = valid && !excl ? int32_t(t) : -(1 << 30);
+      const int32_t kb = int32_t(key0) + 4 * h;
       attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
                               [&](int, int mt, int a, int bb) {
-                                const int64_t j = key0 + 32 * mt + 8 * a + 4 * h + bb;
-                                return !excl && j <= tv && j > tv - W;
+                                const int32_t j = kb + 32 * mt + 8 * a + bb;
+                                return (j <= tv) & (j > tv - W);
                               });
     }
     __syncthreads();
   }
   // ---- hand the window part over to the merge layout (LDS, reusing the
-  // chunk buffers; the loop above ended on a barrier).  Element e of a row is
-  // column pi(e) = 32mt + 8a + 4h + b for e = h D/2 + 16mt + 4a + b -- the
-  // order partials are stored in -- so a lane half's 64 values are one
-  // contiguous run; 16-byte units are XOR-swizzled by row.
+  // first chunk buffer; the loop above ended on a barrier), normalised by its
+  // sum and in the partials' precision.  Element e of a row is column
+  // pi(e) = 32mt + 8a + 4h + b for e = h D/2 + 16mt + 4a + b -- the order
+  // partials are stored in -- so a lane half's values are one contiguous
+  // run; 16-byte units are XOR-swizzled by row.
   {
-    constexpr int U = D / 4;                        // 16-byte units per float32 row
-    float* wo = reinterpret_cast<float*>(lds);
     const RowState<D>& ws = st[0];
-#pragma unroll
-    for (int mt = 0; mt < A::MTD; ++mt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int u = (h * (D / 2) + 16 * mt + 4 * q) / 4;
-        *reinterpret_cast<floatx4*>(wo + r * D + 4 * (u ^ (r % U))) =
-            floatx4{ws.o[mt][4 * q], ws.o[mt][4 * q + 1], ws.o[mt][4 * q + 2], ws.o[mt][4 * q + 3]};
-      }
     const float lw = ws.l + wave_shfl_xor(ws.l, 32);
+    const float inv = lw > 0.f ? 1.f / lw : 0.f;
+    if constexpr (sizeof(PartT) == 4) {
+      constexpr int U = D / 4;                      // 16-byte units per float32 row
+      float* wo = reinterpret_cast<float*>(lds);
+#pragma unroll
+      for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int u = (h * (D / 2) + 16 * mt + 4 * q) / 4;
+          *reinterpret_cast<floatx4*>(wo + r * D + 4 * (u ^ (r % U))) =
+              floatx4{ws.o[mt][4 * q] * inv, ws.o[mt][4 * q + 1] * inv, ws.o[mt][4 * q + 2] * inv,
+                      ws.o[mt][4 * q + 3] * inv};
+        }
+    } else {
+      constexpr int U = D / 8;                      // 16-byte units per float16 row
+#pragma unroll
+      for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int el = h * (D / 2) + 16 * mt + 4 * q, u = el / 8;
+          uint32_t w2[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            w2[i] = uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(ws.o[mt][4 * q + 2 * i] * inv))) |
+                    (uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(ws.o[mt][4 * q + 2 * i + 1] * inv)))
+                     << 16);
+          *reinterpret_cast<uint2*>(lds + r * D * 2 + (u ^ (r % U)) * 16 + (el % 8) * 2) =
+              uint2{w2[0], w2[1]};
+        }
+    }
     if (h == 0) wml[r] = float2{ws.m2, lw};
+  }
+  // this wave's rows' partial positions (only the wave's own rows are merged
+  // by it, so a wavefront-scope fence suffices)
+  for (int w = lane; w < 32 * k; w += 64) {
+    const int rr = 32 * wave + w / k, i = w % k;
+    const int64_t rh = rho0 + rr;
+    int32_t e = 0;
+    if (rh < rows_total && sidx[i * kWinRows + rr] >= 0)
+      e = pos[((b * hq + kv * g + rh % g) * n + rh / g) * k + i];
+    spos[i * kWinRows + rr] = e;
   }
   wave_lds_sync();
 
@@ -503,8 +540,6 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int EPU = 16 / int(sizeof(PartT));      // elements per unit
   constexpr int RPR = 64 / CH;
   constexpr int GRP = 16;                           // partials requested at once
-  const float* wo = reinterpret_cast<const float*>(lds);
-  constexpr int U = D / 4;
   for (int rd = 0; rd < 32 / RPR; ++rd) {
     const int rr = 32 * wave + rd * RPR + lane / CH, sub = lane % CH;
     const int64_t rh = rho0 + rr;
@@ -519,11 +554,24 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     float den = wl.y > 0.f ? wl.y * __builtin_amdgcn_exp2f(wl.x - M) : 0.f;   // = 1 or 0
     float acc[EPU];
     {
-      const float wws = wl.y > 0.f ? ldexpf(__builtin_amdgcn_exp2f(wl.x - M), ev) : 0.f;
+      // the stored window part is normalised: its weight is den itself
+      const float wws = ldexpf(den, ev);
+      if constexpr (sizeof(PartT) == 4) {
+        constexpr int U = D / 4;
 #pragma unroll
-      for (int e = 0; e < EPU; ++e) {
-        const int el = sub * EPU + e, u = el / 4;
-        acc[e] = wo[rr * D + 4 * (u ^ (rr % U)) + el % 4] * wws;
+        for (int e = 0; e < EPU; ++e) {
+          const int el = sub * EPU + e, u = el / 4;
+          acc[e] = reinterpret_cast<const float*>(lds)[rr * D + 4 * (u ^ (rr % U)) + el % 4] * wws;
+        }
+      } else {
+        // a lane's unit of the partial row is unit sub of the stored row
+        constexpr int U = D / 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + rr * D * 2 + (sub ^ (rr % U)) * 16);
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) {
+          const uint32_t w2 = v[e / 2];
+          acc[e] = static_cast<float>(__builtin_bit_cast(_Float16, u16((e & 1) ? (w2 >> 16) : (w2 & 0xFFFFu)))) * wws;
+        }
       }
     }
     for (int i0 = 0; i0 < k; i0 += GRP) {
@@ -712,8 +760,9 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto wk = window_merge_kernel<F32, D, PartT, OutT>;
-  const size_t wshm =
-      2 * size_t(A::CHUNK) + 2 * size_t(kWinRows) * std::max(s.k, 1) * 4 + size_t(kWinRows) * 8;
+  const size_t wshm = 2 * size_t(A::CHUNK) + size_t(kWinRows) * std::max(s.k, 1) * 4 +
+                      size_t(kWinRows) * 8 +
+                      (window_pos_in_chunk(s.k, A::CHUNK) ? 0 : size_t(kWinRows) * s.k * 4);
   if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(wk),
                                hipFuncAttributeMaxDynamicSharedMemorySize, int(wshm))) != hipSuccess)
     return e;
