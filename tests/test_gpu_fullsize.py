@@ -241,3 +241,84 @@ def test_decode_256k_hier_fullsize(keys):
             ok, _ = idx_ok(idx_h[b, h], dict(idx=sel, scores=r, r_k=rk, r_k1=rk1))
             assert ok, f"hierarchical selection mismatch b={b} h={h}"
         say(f"  sequence {b} kv head {kv}: {wl.group} rows ok")
+
+
+@pytest.mark.timeout(900)
+def test_gqa_prefill_128k_backward_fullsize():
+    """ssa_sparse_attn_bwd at the 128K GQA workload, called as the benchmark
+    calls it (bf16 O from the forward, the same dO seed), on the GPU's own
+    selections.  Checked against the oracle's per-row backward
+    (attend_backward over S(t)):
+      - dQ on sampled rows of every q-head;
+      - dK and dV of whole blocks (an early one, a late one and the last),
+        each the sum over every row that attends one of its keys: the rows
+        that selected the block and the window rows reaching it.
+    Tolerance: 2e-3 of the largest reference magnitude in each compared set,
+    as for the small backward cases."""
+    wl = CONFIGS["gqa_prefill_128k"]
+    say("case gqa_prefill_128k backward: generating on the GPU")
+    data = make_prefill(wl, seed=0, device=DEV)
+    Q, K, V = data["Q"], data["K"], data["V"]
+    mu, sigma = ssa.ssa_block_stats(K, wl.block)
+    idx = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta)
+    Oo, lse = ssa.ssa_sparse_attn_fwd(Q, K, V, idx, block_size=wl.block, window=wl.window,
+                                      scale=wl.scale)
+    dO = torch.randn(Q.shape, generator=torch.Generator(device=DEV).manual_seed(7), device=DEV,
+                     dtype=torch.float32).to(Q.dtype)
+    say("  backward")
+    dQ, dK, dV = ssa.ssa_sparse_attn_bwd(Q, K, V, idx, Oo, lse, dO, block_size=wl.block,
+                                         window=wl.window, scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()
+    idx_h = idx[0].cpu().numpy()
+    del idx, Oo, lse, mu, sigma
+    p = O.Params(wl.block, wl.top_k, wl.window, wl.beta, wl.scale)
+    n, B, W, g = wl.seq_len, wl.block, wl.window, wl.group
+    tol = 2e-3
+    kvs: dict[int, tuple] = {}
+
+    def kv_data(kv):
+        if kv not in kvs:
+            kvs.clear()
+            kvs[kv] = (O.as_f64(K[0, kv]), O.as_f64(V[0, kv]))
+        return kvs[kv]
+
+    # dQ on sampled rows
+    rng = np.random.default_rng(3)
+    rows = sorted({(int(h), int(t)) for h in range(wl.n_q_heads)
+                   for t in list(rng.integers(0, n, size=1)) + [int(rng.integers(n - 300, n))]})
+    got, ref = [], []
+    for (h, t) in sorted(rows, key=lambda r: r[0] // g):
+        Kh, Vh = kv_data(h // g)
+        S = O.key_set(t, idx_h[h, t], B, W)
+        dq, _, _ = O.attend_backward(O.as_f64(Q[0, h, t]), Kh, Vh, S, p.scale, O.as_f64(dO[0, h, t]))
+        got.append(dQ[0, h, t].double().cpu().numpy())
+        ref.append(dq)
+    got, ref = np.array(got), np.array(ref)
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    say(f"  dQ on {len(rows)} rows: relative error {err:.3g}")
+    assert err <= tol, f"dQ relative error {err:.3g}"
+
+    # dK, dV of whole blocks
+    for kv, c in ((1, 200), (6, 450), (7, n // B - 1)):
+        Kh, Vh = kv_data(kv)
+        lo, hi = c * B, min(n, (c + 1) * B)
+        heads = range(kv * g, (kv + 1) * g)
+        sel = {(h - kv * g, int(t)) for h in heads for t in np.nonzero((idx_h[h] == c).any(axis=1))[0]}
+        win = {(h - kv * g, t) for h in heads for t in range(lo, min(n, hi - 1 + W))}
+        R = sorted(sel | win)
+        say(f"  block {c} of KV head {kv}: {len(sel)} selecting rows, {len(R)} rows in all")
+        Qg, dOg = Q[0, kv * g:(kv + 1) * g].cpu(), dO[0, kv * g:(kv + 1) * g].cpu()
+        dKr = np.zeros((hi - lo, Kh.shape[1]))
+        dVr = np.zeros_like(dKr)
+        for (j, t) in R:
+            h = kv * g + j
+            S = O.key_set(t, idx_h[h, t], B, W)
+            _, dk, dv = O.attend_backward(O.as_f64(Qg[j, t]), Kh, Vh, S, p.scale, O.as_f64(dOg[j, t]))
+            m = (S >= lo) & (S < hi)
+            dKr[S[m] - lo] += dk[m]
+            dVr[S[m] - lo] += dv[m]
+        for name, g_, r_ in (("dK", dK[0, kv, lo:hi], dKr), ("dV", dV[0, kv, lo:hi], dVr)):
+            e = np.abs(g_.double().cpu().numpy() - r_).max() / np.abs(r_).max()
+            say(f"    {name} relative error {e:.3g}")
+            assert e <= tol, f"{name} of block {c}, KV head {kv}: relative error {e:.3g}"
