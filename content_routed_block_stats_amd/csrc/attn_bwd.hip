@@ -81,7 +81,8 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const float* __restrict__ lse, const float* __restrict__ Drow, const uint8_t* __restrict__ img_a,
     const uint8_t* __restrict__ img_b, const uint32_t* __restrict__ kmax, int64_t n_chunks,
     const int4* __restrict__ tasks, const int32_t* __restrict__ task_count,
-    const uint32_t* __restrict__ entries, float* __restrict__ dq_part, int64_t n, int g, int hq,
+    const uint32_t* __restrict__ entries, uint8_t* __restrict__ dq_part, float* __restrict__ dq_sc,
+    int64_t n, int g, int hq,
     int hkv, int B, int64_t nb, float scale2, float scale) {
   using A = AT<F32, D>;
   using Frag = typename A::Frag;
@@ -183,16 +184,44 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2)))
       __syncthreads();
     }
   }
-  if (!valid) return;
+  if (!valid) return;   // (both lane halves of a row share it)
   const float f = ldexpf(scale, F32 ? 0 : value_exponent(kmax[bkv]));
-  float* out = dq_part + (e0 + r) * D;
+  if constexpr (F32) {
+    float* out = reinterpret_cast<float*>(dq_part) + (e0 + r) * D;
 #pragma unroll
-  for (int mt = 0; mt < A::MTD; ++mt)
+    for (int mt = 0; mt < A::MTD; ++mt)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      *reinterpret_cast<floatx4*>(out + 32 * mt + 8 * a + 4 * h) =
-          floatx4{dq[mt][4 * a] * f, dq[mt][4 * a + 1] * f, dq[mt][4 * a + 2] * f,
-                  dq[mt][4 * a + 3] * f};
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<floatx4*>(out + 32 * mt + 8 * a + 4 * h) =
+            floatx4{dq[mt][4 * a] * f, dq[mt][4 * a + 1] * f, dq[mt][4 * a + 2] * f,
+                    dq[mt][4 * a + 3] * f};
+  } else {
+    // float16 scaled by a power of two per partial: the row's largest |value|
+    // lands in [2^14, 2^15) (relative rounding 2^-11 of that maximum)
+    float m = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(dq[mt][j]));
+    m = fmaxf(m, wave_shfl_xor(m, 32)) * f;
+    int e = 0;
+    if (m > 0.f && m < __builtin_inff()) (void)frexpf(m, &e);   // m < 2^e
+    const float sc = ldexpf(f, 15 - e);
+    u16* out = reinterpret_cast<u16*>(dq_part) + (e0 + r) * D;
+#pragma unroll
+    for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        uint32_t w2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          w2[i] = uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(dq[mt][4 * a + 2 * i] * sc))) |
+                  (uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(dq[mt][4 * a + 2 * i + 1] * sc)))
+                   << 16);
+        *reinterpret_cast<uint2*>(out + 32 * mt + 8 * a + 4 * h) = uint2{w2[0], w2[1]};
+      }
+    if (h == 0) dq_sc[e0 + r] = ldexpf(1.f, e - 15);
+  }
 }
 
 // --------------------------------------------------------------- dkv_chunk --
@@ -802,7 +831,8 @@ template <bool F32, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_window_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const typename AT<F32, D>::In* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Drow, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ pos, const float* __restrict__ dq_part,
+    const int32_t* __restrict__ pos, const uint8_t* __restrict__ dq_part,
+    const float* __restrict__ dq_sc,
     const uint8_t* __restrict__ img_a, const uint8_t* __restrict__ img_b,
     const uint32_t* __restrict__ kmax, int64_t n_chunks, float* __restrict__ dQ, int64_t n, int g,
     int hq, int hkv, int B, int k, int W, float scale2, float scale, int64_t n_tiles) {
@@ -917,17 +947,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int j = 0; j < 16; ++j) dq[mt][j] *= f;
   // the row's partials from its selected blocks
-  for (int i = 0; i < k; ++i) {
-    if (idx[row * k + i] < 0) continue;
-    const float* src = dq_part + int64_t(pos[row * k + i]) * D;
+  if constexpr (F32) {
+    for (int i = 0; i < k; ++i) {
+      if (idx[row * k + i] < 0) continue;
+      const float* src = reinterpret_cast<const float*>(dq_part) + int64_t(pos[row * k + i]) * D;
 #pragma unroll
-    for (int mt = 0; mt < A::MTD; ++mt)
+      for (int mt = 0; mt < A::MTD; ++mt)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const floatx4 v = *reinterpret_cast<const floatx4*>(src + 32 * mt + 8 * a + 4 * h);
+        for (int a = 0; a < 4; ++a) {
+          const floatx4 v = *reinterpret_cast<const floatx4*>(src + 32 * mt + 8 * a + 4 * h);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dq[mt][4 * a + e] += v[e];
+          for (int e = 0; e < 4; ++e) dq[mt][4 * a + e] += v[e];
+        }
+    }
+  } else {
+    // float16 partials with their scales; two requested before either is
+    // waited for (an absent slot reads partial 0 with weight 0)
+    const u16* base = reinterpret_cast<const u16*>(dq_part);
+    for (int i0 = 0; i0 < k; i0 += 2) {
+      int64_t at[2];
+      float w[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = min(i0 + u, k - 1);
+        const bool on = i0 + u < k && idx[row * k + i] >= 0;
+        at[u] = on ? int64_t(pos[row * k + i]) : 0;
+        w[u] = on ? dq_sc[at[u]] : 0.f;
       }
+      uint2 v[2][A::MTD][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            v[u][mt][a] = *reinterpret_cast<const uint2*>(base + at[u] * D + 32 * mt + 8 * a + 4 * h);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int mt = 0; mt < A::MTD; ++mt)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const uint32_t x[2] = {v[u][mt][a].x, v[u][mt][a].y};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t bits = (e & 1) ? (x[e / 2] >> 16) : (x[e / 2] & 0xFFFFu);
+              dq[mt][4 * a + e] = fmaf(static_cast<float>(__builtin_bit_cast(_Float16, u16(bits))), w[u],
+                                       dq[mt][4 * a + e]);
+            }
+          }
+    }
   }
   float* out = dQ + row * D;
 #pragma unroll
@@ -946,7 +1015,8 @@ struct BwdWs {
   uint32_t* qmax;
   uint32_t* domax;
   float* Drow;
-  float* dq_part;
+  uint8_t* dq_part;   // per (row, slot): D float32 (float32 inputs) or D float16 values
+  float* dq_sc;       // float16 partials: each one's scale
   int64_t n_chunks;
   size_t bytes;
 };
@@ -969,7 +1039,8 @@ BwdWs bwd_ws_layout(const Shape& s, void* base) {
   const size_t o_km = take(size_t(s.b) * s.hkv * 4), o_qm = take(size_t(s.b) * s.hq * 4);
   const size_t o_dm = take(size_t(s.b) * s.hq * 4);
   const size_t o_D = take(size_t(s.b) * s.hq * size_t(s.n) * 4);
-  const size_t o_part = take(use_disp ? size_t(dl.slots) * s.d * 4 : 0);
+  const size_t o_part = take(use_disp ? size_t(dl.slots) * s.d * (s.in_bf16 ? 2 : 4) : 0);
+  const size_t o_sc = take(use_disp && s.in_bf16 ? size_t(dl.slots) * 4 : 0);
   w.bytes = off;
   if (base != nullptr) {
     uint8_t* p = static_cast<uint8_t*>(base);
@@ -980,7 +1051,8 @@ BwdWs bwd_ws_layout(const Shape& s, void* base) {
     w.qmax = reinterpret_cast<uint32_t*>(p + o_qm);
     w.domax = reinterpret_cast<uint32_t*>(p + o_dm);
     w.Drow = reinterpret_cast<float*>(p + o_D);
-    w.dq_part = reinterpret_cast<float*>(p + o_part);
+    w.dq_part = p + o_part;
+    w.dq_sc = reinterpret_cast<float*>(p + o_sc);
   }
   return w;
 }
@@ -1030,7 +1102,7 @@ hipError_t launch_bwd_t(const Shape& s, const void* Qv, const void* Kv, const vo
     if ((e = launch_dispatch(s, idx, w.disp, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_task_kernel<F32, D>), dim3(unsigned(2 * w.disp.max_tasks)),
                        dim3(kDqThreads), 0, st, Q, dO, lse, w.Drow, w.img_a, w.img_b, w.kmax,
-                       w.n_chunks, w.disp.tasks, w.disp.task_count, w.disp.entries, w.dq_part, s.n,
+                       w.n_chunks, w.disp.tasks, w.disp.task_count, w.disp.entries, w.dq_part, w.dq_sc, s.n,
                        s.g, s.hq, s.hkv, s.B, s.nb, scale2, s.scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -1063,7 +1135,7 @@ hipError_t launch_bwd_t(const Shape& s, const void* Qv, const void* Kv, const vo
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t n_tiles = (s.n * s.g + kWinTile - 1) / kWinTile;
   hipLaunchKernelGGL((bwd_dq_window_kernel<F32, D>), dim3(unsigned(n_tiles * n_bkv)), dim3(256), 0,
-                     st, Q, dO, lse, w.Drow, idx, use_disp ? w.disp.pos : nullptr, w.dq_part,
+                     st, Q, dO, lse, w.Drow, idx, use_disp ? w.disp.pos : nullptr, w.dq_part, w.dq_sc,
                      w.img_a, w.img_b, w.kmax, w.n_chunks, dQ, s.n, s.g, s.hq, s.hkv, s.B,
                      use_disp ? s.k : 0, s.W, scale2, s.scale, n_tiles);
   return hipGetLastError();
