@@ -349,12 +349,17 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
     }
     VFrag pf[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt) {
+      float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = sacc[nt][sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)];
-        if constexpr (F32) pf[nt][e] = pv; else pf[nt][e] = static_cast<_Float16>(pv);
+      for (int e = 0; e < 8; ++e) pv[e] = sacc[nt][sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)];
+      if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[nt][e] = pv[e];
+      } else {
+        pf[nt] = to_f16x8(pv);
       }
+    }
 #pragma unroll
     for (int mt = 0; mt < A::MTD; ++mt)
 #pragma unroll

@@ -70,23 +70,21 @@ __device__ __forceinline__ void store_partials(uint8_t* stage, PartT* dst, const
   constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
   constexpr int HALF = CH / 2;                     // chunks per lane half
   constexpr int R = kStageBytes / ROWB;            // rows per round
-  auto chunk = [&](int j) {
-    u32x4 w;
+  // the lane's HALF 16-byte units, converted once (in pairs for float16)
+  u32x4 w[HALF];
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) {
     if constexpr (sizeof(PartT) == 4) {
       const int mt = j / 4, q = j % 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, o[mt][4 * q + i] * sc);
+      for (int i = 0; i < 4; ++i) w[j][i] = __builtin_bit_cast(uint32_t, o[mt][4 * q + i] * sc);
     } else {
       const int mt = j / 2, q = j % 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = o[mt][8 * q + 2 * i] * sc, b2 = o[mt][8 * q + 2 * i + 1] * sc;
-        w[i] = uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(a))) |
-               (uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(b2))) << 16);
-      }
+      for (int i = 0; i < 4; ++i)
+        w[j][i] = pack_f16x2(o[mt][8 * q + 2 * i] * sc, o[mt][8 * q + 2 * i + 1] * sc);
     }
-    return w;
-  };
+  }
 #pragma unroll
   for (int rd = 0; rd < 32 / R; ++rd) {
     wave_lds_sync();
@@ -95,7 +93,7 @@ __device__ __forceinline__ void store_partials(uint8_t* stage, PartT* dst, const
 #pragma unroll
       for (int j = 0; j < HALF; ++j) {
         const int c = h * HALF + j;
-        *reinterpret_cast<u32x4*>(stage + ri * ROWB + ((c ^ (ri & (CH - 1))) * 16)) = chunk(j);
+        *reinterpret_cast<u32x4*>(stage + ri * ROWB + ((c ^ (ri & (CH - 1))) * 16)) = w[j];
       }
     }
     wave_lds_sync();
@@ -295,15 +293,18 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
   const int seg_chunks = min(block_chunks, SEG_CHUNKS);
   const int segs = (block_chunks + seg_chunks - 1) / seg_chunks;
 
+  // (segment ids, (sequence, KV head) pairs and row ids all fit 32 bits:
+  // 32-bit divisions are a few instructions, 64-bit ones a long sequence)
   auto image_of = [&](const int4& tk, int seg) {
-    const int64_t bkv = tk.x / nb, c = tk.x % nb;
-    return img + (bkv * n_chunks + c * block_chunks + int64_t(seg) * seg_chunks) * A::CHUNK;
+    const uint32_t bkv = uint32_t(tk.x) / uint32_t(nb), c = uint32_t(tk.x) - bkv * uint32_t(nb);
+    return img + (int64_t(bkv) * n_chunks + int64_t(c) * block_chunks + int64_t(seg) * seg_chunks) * A::CHUNK;
   };
   // query row of an entry (row id << 5 | slot) of task tk
   auto row_of = [&](const int4& tk, uint32_t code) {
-    const int64_t bkv = tk.x / nb, b = bkv / hkv, kv = bkv % hkv;
-    const int64_t rho = code >> 5;
-    return (b * hq + kv * g + rho % g) * n + rho / g;
+    const uint32_t bkv = uint32_t(tk.x) / uint32_t(nb);
+    const uint32_t b = bkv / uint32_t(hkv), kv = bkv - b * uint32_t(hkv);
+    const uint32_t rho = code >> 5, t = rho / uint32_t(g), jg = rho - t * uint32_t(g);
+    return (int64_t(b) * hq + int64_t(kv) * g + jg) * n + t;
   };
 
   // Software pipeline over tasks.  At the top of task i the query rows of
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
     const uint32_t code_nn = entries[(has_nn ? t2 : ti) * kTaskRows + r];
     // (b) this task: every chunk of its block against 8 x 32 query rows
     const bool wave_active = 32 * wave < task.z;
-    const int ev = F32 ? 0 : value_exponent(vmax[task.x / nb]);
+    const int ev = F32 ? 0 : value_exponent(vmax[uint32_t(task.x) / uint32_t(nb)]);
     RowState<D> st[1];
     row_state_init(st[0]);
     for (int sg = 0; sg < segs; ++sg) {

@@ -74,6 +74,21 @@ __host__ __device__ __forceinline__ constexpr int frag_k(int s, int h, int e) {
 }
 
 // One MFMA step contracting a 16-wide chunk: bf16 inputs (one instruction)...
+// Two float32 values as a float16 pair (round to nearest even), one
+// conversion instruction for both: converting element by element into a
+// float16 vector costs a conversion and a merge per value.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+
+// Eight float32 values as a float16 MFMA fragment.
+__device__ __forceinline__ f16x8 to_f16x8(const float (&v)[8]) {
+  return __builtin_bit_cast(f16x8, u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]),
+                                         pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])});
+}
+
 __device__ __forceinline__ floatx16 mma16(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
