@@ -106,7 +106,8 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2)))
   int64_t row = 0;
   if (valid) {
     const uint32_t en = entries[e0 + r];
-    const int64_t rho = en >> 5, t = rho / g, jg = rho % g;
+    const RowTJ q = split_rho(en >> 5, g);
+    const int64_t t = q.t, jg = q.jg;
     row = (b * hq + kv * g + jg) * n + t;
   }
   Frag bq[A::NS], bdo[A::NS];
@@ -304,8 +305,9 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
     if (i < sel_cnt) {
       const uint32_t en = entries[sel_start + i];
       const int64_t rho = en >> 5;
-      r.pos = rho / g;
-      r.row = (b * hq + kv * g + rho % g) * n + r.pos;
+      const RowTJ q = split_rho(rho, g);
+      r.pos = q.t;
+      r.row = (b * hq + kv * g + q.jg) * n + r.pos;
       r.mode = 0;
     } else if (i < total) {
       const int64_t w = i - sel_cnt;
@@ -608,8 +610,9 @@ __global__ __launch_bounds__(kDkvWideThreads) void bwd_dkv_wide_kernel(
     Pend p;
     const bool is_sel = i < sel_cnt;
     const int64_t rho = en >> 5, w = i - sel_cnt;
-    const int64_t pos = is_sel ? rho / g : key0 + w / g;
-    const int64_t row = (b * hq + kv * g + (is_sel ? rho % g : w % g)) * n + pos;
+    const RowTJ q = split_rho(is_sel ? rho : w, g);
+    const int64_t pos = is_sel ? q.t : key0 + q.t;
+    const int64_t row = (b * hq + kv * g + q.jg) * n + pos;
     p.pos = int32_t(pos);
     p.row = i < total ? row : -1;
     const int64_t sr = i < total ? row : 0;
@@ -848,7 +851,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int64_t rho0 = tile * kWinTile, rows_total = n * g;
   const int64_t rho = rho0 + 32 * wave + ln;
   const bool valid = rho < rows_total;
-  const int64_t t = valid ? rho / g : 0, jg = valid ? rho % g : 0;
+  const RowTJ tj = split_rho(valid ? rho : 0, g);
+  const int64_t t = tj.t, jg = tj.jg;
   const int64_t row = (b * hq + kv * g + jg) * n + t;
   Frag bq[A::NS], bdo[A::NS];
 #pragma unroll

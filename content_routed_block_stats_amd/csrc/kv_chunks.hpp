@@ -22,6 +22,17 @@ constexpr int kKeyChunk = 64;              // keys per LDS chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// A KV head's query row id rho = t g + jg (below 2^31) split into the
+// position t and the group member jg by one 32-bit division (a 64-bit one is
+// a long instruction sequence).
+struct RowTJ {
+  int64_t t, jg;
+};
+__device__ __forceinline__ RowTJ split_rho(int64_t rho, int g) {
+  const uint32_t r = uint32_t(rho), t = r / uint32_t(g);
+  return RowTJ{int64_t(t), int64_t(r - t * uint32_t(g))};
+}
+
 template <bool F32, int D>
 struct AT {
   using In = typename std::conditional<F32, float, bf16_t>::type;

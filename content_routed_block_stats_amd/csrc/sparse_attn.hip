@@ -429,7 +429,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int r = 32 * wave + ln;
   const int64_t rho = rho0 + r;
   const bool valid = rho < rows_total;
-  const int64_t t = valid ? rho / g : 0, jg = valid ? rho % g : 0;
+  const RowTJ tj = split_rho(valid ? rho : 0, g);
+  const int64_t t = tj.t, jg = tj.jg;
   const int64_t orow = (b * hq + kv * g + jg) * n + t;
 
   const int64_t t_lo = rho0 / g, t_hi = min(n - 1, (rho0 + kWinRows - 1) / g);
@@ -443,7 +444,10 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     const int rr = w / k, i = w % k;   // coalesced idx reads, transposed LDS writes
     const int64_t rh = rho0 + rr;
     int32_t v = -1;
-    if (rh < rows_total) v = idx[((b * hq + kv * g + rh % g) * n + rh / g) * k + i];
+    if (rh < rows_total) {
+      const RowTJ q = split_rho(rh, g);
+      v = idx[((b * hq + kv * g + q.jg) * n + q.t) * k + i];
+    }
     sidx[i * kWinRows + rr] = v;
   }
   typename A::Frag bq[1][A::NS];
@@ -529,8 +533,10 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     const int rr = 32 * wave + w / k, i = w % k;
     const int64_t rh = rho0 + rr;
     int32_t e = 0;
-    if (rh < rows_total && sidx[i * kWinRows + rr] >= 0)
-      e = pos[((b * hq + kv * g + rh % g) * n + rh / g) * k + i];
+    if (rh < rows_total && sidx[i * kWinRows + rr] >= 0) {
+      const RowTJ q = split_rho(rh, g);
+      e = pos[((b * hq + kv * g + q.jg) * n + q.t) * k + i];
+    }
     spos[i * kWinRows + rr] = e;
   }
   wave_lds_sync();
@@ -545,7 +551,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     const int rr = 32 * wave + rd * RPR + lane / CH, sub = lane % CH;
     const int64_t rh = rho0 + rr;
     if (rh >= rows_total) continue;
-    const int64_t row = (b * hq + kv * g + rh % g) * n + rh / g;
+    const RowTJ q = split_rho(rh, g);
+    const int64_t row = (b * hq + kv * g + q.jg) * n + q.t;
     const float2 wl = wml[rr];
     // running (max, sum, weighted values) over the window part and then the
     // partials in groups of GRP; every load is unconditional -- absent slots
