@@ -71,6 +71,19 @@ __device__ __forceinline__ void set_vf(VF<F32>& f, int e, float v) {
   if constexpr (F32) f[e] = v; else f[e] = static_cast<_Float16>(v);
 }
 
+// A whole fragment from eight float32 values (float16: converted in pairs).
+template <bool F32>
+__device__ __forceinline__ VF<F32> make_vf(const float (&v)[8]) {
+  if constexpr (F32) {
+    VF<F32> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = v[e];
+    return f;
+  } else {
+    return to_f16x8(v);
+  }
+}
+
 // ----------------------------------------------------------------- dq_task --
 // Two workgroups (4 waves x 32 rows each) per task of up to 256 rows, two per
 // CU; chunk images of the task's block in LDS (image A's K part, then all of
@@ -167,10 +180,10 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2)))
       const uint8_t* kt = L + A::KBYTES + A::KBYTES;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
-        VF<F32> pf;
+        float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          set_vf<F32>(pf, e, sacc[sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)]);
+        for (int e = 0; e < 8; ++e) pv[e] = sacc[sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)];
+        const VF<F32> pf = make_vf<F32>(pv);
 #pragma unroll
         for (int mt = 0; mt < A::MTD; ++mt)
           dq[mt] = mma16(*reinterpret_cast<const typename A::VFrag*>(kt + (mt * 4 + sp) * A::FRAG +
@@ -216,9 +229,7 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2)))
         uint32_t w2[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          w2[i] = uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(dq[mt][4 * a + 2 * i] * sc))) |
-                  (uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(dq[mt][4 * a + 2 * i + 1] * sc)))
-                   << 16);
+          w2[i] = pack_f16x2(dq[mt][4 * a + 2 * i] * sc, dq[mt][4 * a + 2 * i + 1] * sc);
         *reinterpret_cast<uint2*>(out + 32 * mt + 8 * a + 4 * h) = uint2{w2[0], w2[1]};
       }
     if (h == 0) dq_sc[e0 + r] = ldexpf(1.f, e - 15);
@@ -423,10 +434,7 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
           const float q1 = __builtin_bit_cast(float, ((pq[j][1][i / 2] >> sh) & 0xFFFFu) << 16) * sq;
           const float d0 = __builtin_bit_cast(float, ((pd[j][0][i / 2] >> sh) & 0xFFFFu) << 16) * sdo;
           const float d1 = __builtin_bit_cast(float, ((pd[j][1][i / 2] >> sh) & 0xFFFFu) << 16) * sdo;
-          const uint32_t wq = uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(q0))) |
-                              (uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(q1))) << 16);
-          const uint32_t wd = uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(d0))) |
-                              (uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(d1))) << 16);
+          const uint32_t wq = pack_f16x2(q0, q1), wd = pack_f16x2(d0, d1);
           const int at = ((8 * pc + i) * TRS + 2 * rp) * 2;
           *reinterpret_cast<uint32_t*>(rq + at) = wq;
           *reinterpret_cast<uint32_t*>(rdo + at) = wd;
@@ -438,13 +446,14 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
       // dV^T += dO^T P and dK^T += Q^T dS: rows contracted in frag_k order
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
-        VF<F32> pf, sf;
+        float pv[8], sv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = 4 * (2 * sp + (e >> 2)) + (e & 3);
-          set_vf<F32>(pf, e, sacc[j]);
-          set_vf<F32>(sf, e, pacc[j]);
+          pv[e] = sacc[j];
+          sv[e] = pacc[j];
         }
+        const VF<F32> pf = make_vf<F32>(pv), sf = make_vf<F32>(sv);
 #pragma unroll
         for (int mt = 0; mt < A::MTD; ++mt) {
           VF<F32> qt, dt;
@@ -754,10 +763,7 @@ __global__ __launch_bounds__(kDkvWideThreads) void bwd_dkv_wide_kernel(
       const float q1 = __builtin_bit_cast(float, ((pq[1][i / 2] >> sh) & 0xFFFFu) << 16) * sq;
       const float d0 = __builtin_bit_cast(float, ((pd[0][i / 2] >> sh) & 0xFFFFu) << 16) * sdo;
       const float d1 = __builtin_bit_cast(float, ((pd[1][i / 2] >> sh) & 0xFFFFu) << 16) * sdo;
-      const uint32_t wq = uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(q0))) |
-                          (uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(q1))) << 16);
-      const uint32_t wd = uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(d0))) |
-                          (uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(d1))) << 16);
+      const uint32_t wq = pack_f16x2(q0, q1), wd = pack_f16x2(d0, d1);
       const int at = ((8 * pc + i) * TRS + 2 * rp) * 2;
       *reinterpret_cast<uint32_t*>(rq + at) = wq;
       *reinterpret_cast<uint32_t*>(rdo + at) = wd;
@@ -767,13 +773,14 @@ __global__ __launch_bounds__(kDkvWideThreads) void bwd_dkv_wide_kernel(
       // dV^T += dO^T P and dK^T += Q^T dS: rows contracted in frag_k order
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
-        f16x8 pf, sf;
+        float pv[8], sv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = 4 * (2 * sp + (e >> 2)) + (e & 3);
-          pf[e] = static_cast<_Float16>(sacc[j]);
-          sf[e] = static_cast<_Float16>(pacc[j]);
+          pv[e] = sacc[j];
+          sv[e] = pacc[j];
         }
+        const f16x8 pf = to_f16x8(pv), sf = to_f16x8(sv);
 #pragma unroll
         for (int mt = 0; mt < A::MTD; ++mt) {
           // rows r0 + frag_k(sp, h, e): 4 consecutive rows, then 4 more 8 rows on
@@ -926,10 +933,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       const uint8_t* kt = L + A::KBYTES + A::KBYTES;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
-        VF<F32> pf;
+        float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          set_vf<F32>(pf, e, sacc[sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)]);
+        for (int e = 0; e < 8; ++e) pv[e] = sacc[sp >> 1][4 * (2 * (sp & 1) + (e >> 2)) + (e & 3)];
+        const VF<F32> pf = make_vf<F32>(pv);
 #pragma unroll
         for (int mt = 0; mt < A::MTD; ++mt)
           dq[mt] = mma16(*reinterpret_cast<const typename A::VFrag*>(kt + (mt * 4 + sp) * A::FRAG +
