@@ -515,14 +515,9 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int el = h * (D / 2) + 16 * mt + 4 * q, u = el / 8;
-          uint32_t w2[2];
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            w2[i] = uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(ws.o[mt][4 * q + 2 * i] * inv))) |
-                    (uint32_t(__builtin_bit_cast(u16, static_cast<_Float16>(ws.o[mt][4 * q + 2 * i + 1] * inv)))
-                     << 16);
           *reinterpret_cast<uint2*>(lds + r * D * 2 + (u ^ (r % U)) * 16 + (el % 8) * 2) =
-              uint2{w2[0], w2[1]};
+              uint2{pack_f16x2(ws.o[mt][4 * q] * inv, ws.o[mt][4 * q + 1] * inv),
+                    pack_f16x2(ws.o[mt][4 * q + 2] * inv, ws.o[mt][4 * q + 3] * inv)};
         }
     }
     if (h == 0) wml[r] = float2{ws.m2, lw};
