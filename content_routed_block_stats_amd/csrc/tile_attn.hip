@@ -102,12 +102,14 @@ __global__ __launch_bounds__(kTileThreads) void tile_attn_kernel(
     // a window chunk counts keys in (t - W, t]
     const bool selected = i < nsel;
     if (wave_active && (selected || (key0 <= wave_t_hi && key0 + kKeyChunk - 1 > wave_t_lo - W))) {
-      const int64_t lo = selected ? -(int64_t(1) << 40) : tv - W;
-      const int64_t hi = selected ? (int64_t(1) << 40) : tv;
+      // 32-bit positions and bitwise tests: no exec-mask blocks per element
+      const int32_t lo = selected ? INT32_MIN : int32_t(max(tv - W, int64_t(INT32_MIN)));
+      const int32_t hi = selected ? INT32_MAX : int32_t(max(tv, int64_t(INT32_MIN)));
+      const int32_t kb = int32_t(key0) + 4 * h;
       attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
                               [&](int, int mt, int a, int bb) {
-                                const int64_t kj = key0 + 32 * mt + 8 * a + 4 * h + bb;
-                                return kj <= hi && kj > lo;
+                                const int32_t kj = kb + 32 * mt + 8 * a + bb;
+                                return (kj <= hi) & (kj > lo);
                               });
     }
     __syncthreads();
