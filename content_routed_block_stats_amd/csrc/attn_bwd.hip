@@ -517,14 +517,15 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2))
 // rg = wave / 4) owns two consecutive chunks, so every staged row serves 128
 // keys and a CU holds one workgroup.  The LDS this frees holds a second row
 // buffer: the next batch's rows are copied global -> LDS directly (no
-// registers) during the whole of the current batch, whose barriers wait for
-// LDS traffic only.  No ordinary load is waited for while such a copy is in
-// flight except at the end of a batch, where the copy has to be complete
-// anyway (the compiler counts the copies as stores, so any such wait drains
-// them): row information is loaded two batches ahead and stored at the end
-// of a batch, and whether a window row's selection holds the block is
-// decided once, in the prologue, into a byte per window row.  Padded rows are copied whole: the padding
-// slot of a row repeats its last 16 bytes.
+// registers) during the whole of the current batch, whose two inner barriers
+// wait for LDS traffic only (the one that opens a batch waits for the copy).
+// No ordinary load is waited for while such a copy is in flight except at the
+// end of a batch, where the copy has to be complete anyway (the compiler
+// counts the copies as stores, so any such wait drains them): row information
+// is loaded two batches ahead and stored at the end of a batch, and whether a
+// window row's selection holds the block is decided once, in the prologue,
+// into a byte per window row.  Padded rows are copied whole: the padding slot
+// of a row repeats its last 16 bytes.
 
 // Workgroup barrier over LDS accesses only: global loads still in flight
 // (the global -> LDS row copies among them) are not waited for.
