@@ -143,12 +143,16 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
     li[i] = 0x7FFFFFFF;
   }
   for (int64_t c = lane; c < C; c += 64) {
-    float sc = scores[row * n_slots + c];
+    const float sn = scores[row * n_slots + c];
+    float sc = sn;
     int ci = int(c);
-    if (!(sc > ls[KMAX - 1])) continue;
+    if (!(sn > ls[KMAX - 1])) continue;
+    // sorted insert (score descending, block ascending; blocks arrive in
+    // ascending order): the new score against each slot, so entries it
+    // displaces move down one and never slip past an equal later entry
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
-      const bool gt = sc > ls[i];
+      const bool gt = sn > ls[i];
       const float ts = ls[i];
       const int tix = li[i];
       ls[i] = gt ? sc : ts;
@@ -157,7 +161,10 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
       ci = gt ? tix : ci;
     }
   }
-  // k rounds: the best head among the lanes wins and pops
+  // k rounds: the best head among the lanes wins and pops.  A score that is
+  // never inserted (NaN, or -inf) leaves the lists holding the sentinel
+  // 0x7FFFFFFF; a round that can only find the sentinel ends the selection,
+  // so every pick kept is a distinct routable block.
   int sel_mine[KMAX];
   int n_sel = 0;
   const int take = int(min<int64_t>(k, C));
@@ -173,6 +180,7 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
         bi = oi;
       }
     }
+    if (bi == 0x7FFFFFFF) break;   // wave-uniform: every lane saw the same winner
     if (li[0] == bi) {
 #pragma unroll
       for (int i = 0; i < KMAX - 1; ++i) {
@@ -182,19 +190,16 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float* __restric
       ls[KMAX - 1] = -__builtin_inff();
       li[KMAX - 1] = 0x7FFFFFFF;
     }
-    if (lane == 0) sel_mine[n_sel < KMAX ? n_sel : KMAX - 1] = bi;
+    if (lane == 0) sel_mine[n_sel] = bi;
     ++n_sel;
   }
   if (lane != 0) return;
-  // ascending output, -1 padded
+  // ascending output (the picks are distinct), -1 padded
   int32_t* out = idx_out + row * k;
-  for (int i = 0; i < k; ++i) {
-    if (i >= take) {
-      out[i] = -1;
-      continue;
-    }
+  for (int i = n_sel; i < k; ++i) out[i] = -1;
+  for (int i = 0; i < n_sel; ++i) {
     int rank = 0;
-    for (int j = 0; j < take; ++j) rank += sel_mine[j] < sel_mine[i] ? 1 : 0;
+    for (int j = 0; j < n_sel; ++j) rank += sel_mine[j] < sel_mine[i] ? 1 : 0;
     out[rank] = sel_mine[i];
   }
 }
@@ -229,8 +234,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     return;
   }
   if (!window) {
+    // a selection must be a complete block before the query; anything else
+    // (-1 padding) is an empty partial and nothing is read
     const int32_t c = idx[row * k + item];
-    if (c < 0) {
+    const int64_t C = min(int64_t(cap / B), (L + 1) / B);
+    if (c < 0 || c >= C) {
       if (tid == 0) {
         dst[0] = -__builtin_inff();
         dst[1] = 0.f;
@@ -324,21 +332,23 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
                                                           float* __restrict__ lse, int k) {
   const int64_t row = blockIdx.x;
   const float* P = part + row * (k + 1) * (D + 2);
+  // an empty partial has l = 0 and is skipped; a NaN partial (non-finite
+  // inputs) is kept, so NaN reaches o and lse
   float M = -__builtin_inff();
   for (int i = 0; i <= k; ++i) {
     const float* pi = P + i * (D + 2);
-    if (pi[1] > 0.f) M = fmaxf(M, pi[0]);
+    if (pi[1] != 0.f) M = fmaxf(M, pi[0]);
   }
   float den = 0.f;
   for (int i = 0; i <= k; ++i) {
     const float* pi = P + i * (D + 2);
-    if (pi[1] > 0.f) den += pi[1] * __builtin_amdgcn_exp2f(pi[0] - M);
+    if (pi[1] != 0.f) den += pi[1] * __builtin_amdgcn_exp2f(pi[0] - M);
   }
   for (int c = threadIdx.x; c < D; c += 64) {
     float acc = 0.f;
     for (int i = 0; i <= k; ++i) {
       const float* pi = P + i * (D + 2);
-      if (pi[1] > 0.f) acc = fmaf(__builtin_amdgcn_exp2f(pi[0] - M), pi[2 + c], acc);
+      if (pi[1] != 0.f) acc = fmaf(__builtin_amdgcn_exp2f(pi[0] - M), pi[2 + c], acc);
     }
     store_from_f32(o, row * D + c, acc / den);
   }

@@ -305,7 +305,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[st2][nt][j] = 0.f;
   float pt[2] = {0.f, 0.f};
-  float sc_ins = -__builtin_inff();
+  float sc_new = -__builtin_inff();   // the score being inserted
+  float sc_ins = -__builtin_inff();   // the entry carried down the list
   int ci_ins = -1;
 
   // fragment k (= chunk-in-pair * PARTS + part) of chunk pair gp of tile mt
@@ -340,13 +341,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float p0 = pt[0] + wave_shfl_xor(pt[0], 32);
     const float p1 = pt[1] + wave_shfl_xor(pt[1], 32);
     pt[0] = pt[1] = 0.f;
-    sc_ins = (cb >= 0 && cb < my_C) ? (h ? p1 : p0) * blk_scale : -__builtin_inff();
+    sc_new = (cb >= 0 && cb < my_C) ? (h ? p1 : p0) * blk_scale : -__builtin_inff();
+    sc_ins = sc_new;
     ci_ins = int(cb);
   };
-  // one step of the running top-(k+1) insertion; strict > keeps the earlier
-  // (lower) block on ties
+  // one step of the running top-(k+1) insertion.  The list is sorted by
+  // (score descending, block ascending) and blocks arrive in ascending order,
+  // so the new block goes after every entry with a score >= its own, and
+  // every entry from that slot on moves down one: the test is the NEW score
+  // against the slot (true from the insertion slot on, the list being
+  // sorted), never the carried entry's -- a displaced entry compared with an
+  // equal later one would otherwise slip past it.  NaN is never inserted.
   auto insert_step = [&](int i) {
-    const bool gt = sc_ins > ls[i];
+    const bool gt = sc_new > ls[i];
     const float ts = ls[i];
     const int ti = li[i];
     ls[i] = gt ? sc_ins : ts;

@@ -553,8 +553,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     // partials in groups of GRP; every load is unconditional -- absent slots
     // read the null partial (zeros, lse = -inf) -- so a group's loads all
     // go out before any of them is waited for
-    float M = wl.y > 0.f ? wl.x + __log2f(wl.y) : -__builtin_inff();
-    float den = wl.y > 0.f ? wl.y * __builtin_amdgcn_exp2f(wl.x - M) : 0.f;   // = 1 or 0
+    // an empty window part (every window key inside a selected block) has
+    // l = 0; a NaN sum (non-finite inputs) is kept, so NaN reaches O and LSE
+    const bool wempty = wl.y == 0.f;
+    float M = wempty ? -__builtin_inff() : wl.x + __log2f(wl.y);
+    float den = wempty ? 0.f : wl.y * __builtin_amdgcn_exp2f(wl.x - M);   // = 1 or 0
     float acc[EPU];
     {
       // the stored window part is normalised: its weight is den itself

@@ -191,12 +191,17 @@ __global__ __launch_bounds__(kTempThreads) void tempered_route_kernel(
         const float lt = l[nt] + wave_shfl_xor(l[nt], 32);
         T[nt] = ((m2[nt] + __builtin_amdgcn_logf(lt)) * kLn2 - log_b) * inv_beta;
       }
-      float sc = (cb < my_C) ? (h ? T[1] : T[0]) : -__builtin_inff();
+      const float sn = (cb < my_C) ? (h ? T[1] : T[0]) : -__builtin_inff();
+      float sc = sn;
       int ci = int(cb);
-      // one pass of the running top-(k+1); strict > keeps the lower block on ties
+      // one pass of the running top-(k+1), sorted by (score descending, block
+      // ascending) with blocks arriving in ascending order: the NEW score is
+      // tested against each slot, so the entries it displaces move down one
+      // and never slip past an equal later entry (strict >: the new block
+      // goes after equal scores)
 #pragma unroll
       for (int i = 0; i <= KMAX; ++i) {
-        const bool gt = sc > ls[i];
+        const bool gt = sn > ls[i];
         const float ts = ls[i];
         const int ti = li[i];
         ls[i] = gt ? sc : ts;
