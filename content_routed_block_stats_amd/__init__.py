@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     make_params,
     ssa_block_stats,
     ssa_decode_step,
+    ssa_decode_step_noalloc,
     ssa_group_stats,
     ssa_route_hier,
     ssa_route_tempered,

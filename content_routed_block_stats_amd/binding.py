@@ -75,13 +75,15 @@ def lib() -> ctypes.CDLL:
     L.ssa_sparse_attn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_decode_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
+    L.ssa_decode_step_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp]
     L.ssa_group_stats.argtypes = [P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp]
     L.ssa_route_hier.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
                                  _vp, ctypes.c_size_t, _vp]
     for name in ("ssa_block_stats", "ssa_workspace_size", "ssa_route_topk", "ssa_route_tempered",
                  "ssa_route_tiles", "ssa_tile_attn_fwd", "ssa_sparse_attn_fwd",
-                 "ssa_sparse_attn_bwd", "ssa_decode_step", "ssa_group_stats",
-                 "ssa_route_hier"):
+                 "ssa_sparse_attn_bwd", "ssa_decode_step", "ssa_decode_step_noalloc",
+                 "ssa_group_stats", "ssa_route_hier"):
         getattr(L, name).restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
@@ -351,6 +353,43 @@ def ssa_decode_step(q, k_new, v_new, K_cache, V_cache, cache_len, mu, sigma, *, 
                                  _ptr(V_cache), _ptr(cache_len), _ptr(mu), _ptr(sigma), _ptr(idx),
                                  _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
     return (o, lse, idx) if return_idx else (o, lse)
+
+
+def ssa_decode_step_noalloc(q, k_new, v_new, K_cache, V_cache, cache_len, mu, sigma, *,
+                            block_size: int, top_k: int, window: int, beta: float = 2.0,
+                            scale: float | None = None, out_dtype: torch.dtype | None = None,
+                            out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                            idx: torch.Tensor | None = None):
+    """ssa_decode_step without a workspace: the library's own scratch array is
+    used, so the C call allocates nothing.  Outputs (o, lse, idx) may be passed
+    in so the Python side allocates nothing either.  Returns (o, lse[, idx])."""
+    _dev_check(q, k_new, v_new, K_cache, V_cache, cache_len, mu, sigma, out, lse, idx)
+    b, hq, d = q.shape
+    hkv, cap = K_cache.shape[1], K_cache.shape[2]
+    if K_cache.shape != (b, hkv, cap, d) or V_cache.shape != K_cache.shape:
+        raise ValueError("caches do not match q")
+    if k_new.shape != (b, hkv, d) or v_new.shape != (b, hkv, d):
+        raise ValueError("k_new/v_new must be [b, Hkv, d]")
+    if cache_len.dtype != torch.int32 or cache_len.shape != (b,):
+        raise ValueError("cache_len must be int32 [b]")
+    if mu.shape != (b, hkv, cap // block_size, d) or sigma.shape != (*mu.shape, d):
+        raise ValueError("stats do not match the cache capacity")
+    out_dtype = out.dtype if out is not None else (out_dtype or q.dtype)
+    p = make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=cap,
+                    block_size=block_size, top_k=top_k, window=window, beta=beta, scale=scale,
+                    in_dtype=q.dtype, out_dtype=out_dtype)
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, hq), dtype=torch.float32, device=q.device)
+    if out.shape != (b, hq, d) or lse.shape != (b, hq) or lse.dtype != torch.float32:
+        raise ValueError("out must be [b, Hq, d], lse float32 [b, Hq]")
+    if idx is not None and (idx.shape != (b, hq, top_k) or idx.dtype != torch.int32):
+        raise ValueError("idx must be int32 [b, Hq, k]")
+    _check(lib().ssa_decode_step_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                         _ptr(K_cache), _ptr(V_cache), _ptr(cache_len), _ptr(mu),
+                                         _ptr(sigma), _ptr(idx), _ptr(out), _ptr(lse), _stream()))
+    return (out, lse, idx) if idx is not None else (out, lse)
 
 
 def ssa_group_stats(mu: torch.Tensor, sigma: torch.Tensor, *, block_size: int, group_blocks: int):

@@ -13,6 +13,7 @@
 // caches, merged per row at the end.  cache_len lives on the device, so steps
 // chain on a stream without a host round trip.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "ssa_common.hpp"
@@ -463,6 +464,38 @@ hipError_t launch_decode_topk(const float* scores, const int32_t* pos, int32_t* 
 }
 
 size_t decode_workspace_bytes(const Shape& s) { return dec_ws_layout(s, nullptr).bytes; }
+
+// ---- scratch of the allocation-free decode entry point --------------------
+//
+// The same kernels with their workspace in a file-scope device array.  Each
+// GPU holds its own copy for the life of the process; the host reads its
+// address once per device (hipGetSymbolAddress, with that device current)
+// and only ever passes that address: the array's name in host code is not a
+// device address.  Nothing in it must start at zero (every score, selection
+// and partial the kernels read is written earlier in the same step), and two
+// calls that overlap in time on one GPU share it, so they race.
+namespace {
+constexpr int kScratchMaxDevices = 64;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kDecodeScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_step(const Shape& s, const void* q, const void* k_new, const void* v_new,
                               void* K_cache, void* V_cache, int32_t* cache_len, float* mu,

@@ -357,6 +357,39 @@ ssa_status ssa_decode_step(const ssa_params* p, const void* q, const void* k_new
                   "ssa_decode_step");
 }
 
+ssa_status ssa_decode_step_noalloc(const ssa_params* p, const void* q, const void* k_new,
+                                   const void* v_new, void* K_cache, void* V_cache,
+                                   int32_t* cache_len, float* mu, float* sigma, int32_t* idx,
+                                   void* o, float* lse, void* stream) {
+  ssa::Shape s;
+  ssa_status st = check_params(p, &s);
+  if (st != SSA_OK) return st;
+  SSA_NONNULL(q);
+  SSA_NONNULL(k_new);
+  SSA_NONNULL(v_new);
+  SSA_NONNULL(K_cache);
+  SSA_NONNULL(V_cache);
+  SSA_NONNULL(cache_len);
+  SSA_NONNULL(o);
+  SSA_NONNULL(lse);
+  if (s.nb > 0) {
+    SSA_NONNULL(mu);
+    SSA_NONNULL(sigma);
+  }
+  const size_t need = ssa::decode_workspace_bytes(s);
+  if (need > ssa::kDecodeScratchBytes)
+    return fail(SSA_ERR_UNSUPPORTED,
+                "this decode step needs %zu bytes of scratch; the allocation-free entry point "
+                "holds %zu (use ssa_decode_step with a workspace)",
+                need, ssa::kDecodeScratchBytes);
+  void* ws = nullptr;
+  st = from_hip(ssa::decode_scratch(&ws), "ssa_decode_step_noalloc: scratch address");
+  if (st != SSA_OK) return st;
+  return from_hip(ssa::launch_decode_step(s, q, k_new, v_new, K_cache, V_cache, cache_len, mu,
+                                          sigma, idx, o, lse, ws, (hipStream_t)stream),
+                  "ssa_decode_step_noalloc");
+}
+
 const char* ssa_status_string(ssa_status s) {
   switch (s) {
     case SSA_OK: return "SSA_OK";

@@ -101,6 +101,10 @@ hipError_t launch_route_hier(const Shape& s, const void* q, const float* mu, con
 
 // decode step
 size_t decode_workspace_bytes(const Shape& s);
+// the allocation-free variant's scratch: a device array of this many bytes,
+// whose address on the current device decode_scratch() returns
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** out);
 // wave top-k of scores [rows, n_slots] over the blocks c < min(n_slots,
 // (pos[row / hq] + 1) / B), ascending, -1 padded (k <= 32)
 hipError_t launch_decode_topk(const float* scores, const int32_t* pos, int32_t* idx, int k,

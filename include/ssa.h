@@ -15,7 +15,9 @@
  *    row-major in the layout stated at each call, aligned to 16 bytes.  The
  *    library never allocates, frees or retains device memory; scratch space
  *    is the caller's workspace.  It keeps no global mutable state, so calls
- *    on different streams may run concurrently.
+ *    on different streams may run concurrently -- except
+ *    ssa_decode_step_noalloc, whose scratch is a device array inside the
+ *    library (see there).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns; results are ready when the stream is.
  *  - Validation is synchronous and on the host, before anything is enqueued:
@@ -293,6 +295,27 @@ ssa_status ssa_decode_step(const ssa_params* p, const void* q, const void* k_new
                            const void* v_new, void* K_cache, void* V_cache, int32_t* cache_len,
                            float* mu, float* sigma, int32_t* idx, void* o, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device scratch that ssa_decode_step_noalloc holds per GPU. */
+#define SSA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* The decode step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and kernels as ssa_decode_step, without the
+ * workspace: its scratch lives in a device array inside the library, one per
+ * GPU, held until the process ends (SSA_DECODE_NOALLOC_SCRATCH_BYTES, enough
+ * for e.g. 32 sequences x 32 q-heads x 512 blocks with k = 16 at d = 128).
+ * Calls whose ssa_workspace_size(p, SSA_OP_DECODE) exceeds it return
+ * SSA_ERR_UNSUPPORTED before anything is enqueued.  The call allocates and
+ * frees nothing; the first call on a device looks up the array's address
+ * there.  The stream must belong to the current device.  Every call on a GPU
+ * shares that GPU's array, so calls that overlap in time on one GPU (other
+ * streams or threads) race; calls in order on one stream do not.  No state
+ * carries over between calls. */
+ssa_status ssa_decode_step_noalloc(const ssa_params* p, const void* q, const void* k_new,
+                                   const void* v_new, void* K_cache, void* V_cache,
+                                   int32_t* cache_len, float* mu, float* sigma, int32_t* idx,
+                                   void* o, float* lse, void* stream);
 
 /* Static text for a status code. */
 const char* ssa_status_string(ssa_status s);

@@ -172,3 +172,23 @@ def test_hier_route_limits_and_pointers_on_host():
     # group stats: NULL outputs
     assert L.ssa_group_stats(ctypes.byref(p), 256, 256, 8, None, 256, 256, None) == \
         B.SSA_ERR_INVALID_ARGUMENT
+
+
+def test_decode_noalloc_checked_on_host():
+    """The allocation-free decode step refuses, before touching a device, a
+    size beyond its scratch and the same invalid arguments as ssa_decode_step."""
+    L = ssa.lib()
+    big = B.make_params(batch=64, n_q_heads=64, n_kv_heads=8, head_dim=128, seq_len=4096 * 64,
+                        block_size=64, top_k=8, window=64)
+    assert B.ssa_workspace_size(big, B.SSA_OP_DECODE) > 16 << 20
+    got = L.ssa_decode_step_noalloc(ctypes.byref(big), 256, 256, 256, 256, 256, 256, 256, 256,
+                                    None, 256, 256, None)
+    assert got == B.SSA_ERR_UNSUPPORTED, B.status_string(got)
+    assert "scratch" in L.ssa_last_error().decode()
+    p = _p()
+    got = L.ssa_decode_step_noalloc(ctypes.byref(p), 256, 256, 256, 256, 256, None, 256, 256,
+                                    None, 256, 256, None)
+    assert got == B.SSA_ERR_INVALID_ARGUMENT          # cache_len NULL
+    got = L.ssa_decode_step_noalloc(ctypes.byref(_p(block_size=48)), 256, 256, 256, 256, 256,
+                                    256, 256, 256, None, 256, 256, None)
+    assert got == B.SSA_ERR_INVALID_ARGUMENT
