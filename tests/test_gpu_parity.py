@@ -34,13 +34,17 @@ def _params(wl):
 
 
 def run_prefill(Q, K, V, wl, out_dtype=None):
+    """Statistics, routing and attention as a caller runs them (no k-th scores
+    requested: bfloat16 inputs take the certified single pass), plus a second
+    routing call that requests the k-th scores (the exact pass on every row)."""
     mu, sigma = ssa.ssa_block_stats(K, wl.block)
-    idx, kth = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta,
-                                  want_kth=True)
+    idx = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta)
+    idx_exact, kth = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k,
+                                        beta=wl.beta, want_kth=True)
     Oo, lse = ssa.ssa_sparse_attn_fwd(Q, K, V, idx, block_size=wl.block, window=wl.window,
                                       scale=wl.scale, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    return dict(mu=mu, sigma=sigma, idx=idx, kth=kth, O=Oo, lse=lse)
+    return dict(mu=mu, sigma=sigma, idx=idx, idx_exact=idx_exact, kth=kth, O=Oo, lse=lse)
 
 
 def compare_prefill(data, res, wl, rows=None, check_stats=True, O32=None, lse32=None):
@@ -60,6 +64,7 @@ def compare_prefill(data, res, wl, rows=None, check_stats=True, O32=None, lse32=
                 assert np.abs(mu_g[b, kv] - mu).max() <= STATS_REL * scale, "mu"
                 assert np.abs(sg_g[b, kv] - sigma).max() <= STATS_REL * scale, "sigma"
     idx = res["idx"].cpu().numpy()
+    idx_exact = res["idx_exact"].cpu().numpy() if res.get("idx_exact") is not None else None
     bf16_out = res["O"].dtype == torch.bfloat16
     Og = res["O"].float().cpu().numpy()
     lg = res["lse"].cpu().numpy()
@@ -75,6 +80,10 @@ def compare_prefill(data, res, wl, rows=None, check_stats=True, O32=None, lse32=
         ok, exact = idx_ok(idx[b, h, t], row)
         assert ok, f"selection mismatch at row {(b, h, t)}: gpu {idx[b, h, t].tolist()} " \
                    f"oracle {row['idx'].tolist()}"
+        if idx_exact is not None:   # the exact pass on every row (k-th scores requested)
+            ok2, _ = idx_ok(idx_exact[b, h, t], row)
+            assert ok2, f"exact-pass selection mismatch at row {(b, h, t)}: " \
+                        f"gpu {idx_exact[b, h, t].tolist()} oracle {row['idx'].tolist()}"
         n_exact += exact
         n_tie += (not exact)
         kv = h // g
@@ -272,8 +281,9 @@ def test_route_query_scale(qexp):
     mu, sigma = ssa.ssa_block_stats(K, wl.block)
     idx, kth = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta,
                                   want_kth=True)
+    idx1 = ssa.ssa_route_topk(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta)
     torch.cuda.synchronize()
-    idx_h, kth_h = idx.cpu().numpy(), kth.cpu().numpy()
+    idx_h, kth_h, idx1_h = idx.cpu().numpy(), kth.cpu().numpy(), idx1.cpu().numpy()
     n_exact = n_tie = 0
     for kv in range(wl.n_kv_heads):
         muo, sgo = O.block_stats(O.as_f64(data["K"][0, kv]), wl.block)
@@ -284,6 +294,8 @@ def test_route_query_scale(qexp):
                 sel, rk, rk1 = O.select_topk(r, wl.top_k)
                 ok, exact = idx_ok(idx_h[0, h, t], dict(idx=sel, scores=r, r_k=rk, r_k1=rk1))
                 assert ok, f"selection mismatch at {(h, t)}: {idx_h[0, h, t]} vs {sel}"
+                ok1, _ = idx_ok(idx1_h[0, h, t], dict(idx=sel, scores=r, r_k=rk, r_k1=rk1))
+                assert ok1, f"single-pass selection mismatch at {(h, t)}: {idx1_h[0, h, t]} vs {sel}"
                 n_exact += exact
                 n_tie += not exact
                 if C > wl.top_k:   # the k-th score, in the scaled inputs' own units
