@@ -425,6 +425,14 @@ def prefill_row(q, K, V, mu, sigma, p: Params, t: int, with_dense: bool = False)
     return out
 
 
+def kv_head(h: int, hq: int, hkv: int) -> int:
+    """The KV head query head h reads under grouped-query attention: the hq
+    query heads form hkv contiguous groups of hq/hkv, group j sharing KV head
+    j (the pages name GQA head counts but not the mapping; this is the usual
+    one, the one torch's SDPA uses with enable_gqa)."""
+    return h // (hq // hkv)
+
+
 class PrefillOracle:
     """Per-row oracle over a whole prefill input, caching per-head statistics.
 
@@ -449,7 +457,7 @@ class PrefillOracle:
         self._cache.pop((b, kv), None)
 
     def row(self, b: int, h: int, t: int, with_dense: bool = False) -> dict:
-        kv = h // (self.hq // self.hkv)
+        kv = kv_head(h, self.hq, self.hkv)
         Kh, Vh, mu, sigma = self.head(b, kv)
         return prefill_row(as_f64(self.Q[b, h, t]), Kh, Vh, mu, sigma, self.p, t, with_dense)
 
@@ -486,8 +494,9 @@ def planted_recall(oracle: PrefillOracle, plants: list[dict], beta: float | None
     by the second-cumulant score (score="cumulant") or by the exact tempered
     score (score="tempered", beta > 0).
 
-    PARITY UNPINNED: the write-up states only the qualitative result
-    (second-cumulant routing recovers targets that centroid routing misses).
+    The write-up states only the qualitative result (second-cumulant routing
+    recovers targets that centroid routing misses); the function is pinned by
+    a hand-worked case (two blocks whose scores cross as beta grows).
     """
     if not plants:
         return math.nan
@@ -495,7 +504,7 @@ def planted_recall(oracle: PrefillOracle, plants: list[dict], beta: float | None
                                              beta, oracle.p.scale)
     hits = 0
     for pl in plants:
-        kv = pl["h"] // (oracle.hq // oracle.hkv)
+        kv = kv_head(pl["h"], oracle.hq, oracle.hkv)
         Kh, Vh, mu, sigma = oracle.head(pl["b"], kv)
         t = pl["t"]
         C = routable_blocks(t, p.block, mu.shape[0])

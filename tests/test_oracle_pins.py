@@ -30,7 +30,8 @@ def _impl(**overrides):
         dropped_mass=OR.dropped_mass, recovery_weight=OR.recovery_weight,
         tempered_scores=OR.tempered_scores, tile_routable_blocks=OR.tile_routable_blocks,
         tile_scores=OR.tile_scores, attend_backward=OR.attend_backward,
-        group_summaries=OR.group_summaries, group_bound=OR.group_bound, route_hier=OR.route_hier)
+        group_summaries=OR.group_summaries, group_bound=OR.group_bound, route_hier=OR.route_hier,
+        kv_head=OR.kv_head)
     for k, v in overrides.items():
         setattr(ns, k, v)
 
@@ -74,6 +75,23 @@ def _impl(**overrides):
             out.update(O_full=Of, lse_full=lf, eps=eps, eps_direct=eps_d)
         return out
     ns.prefill_row = prefill_row
+
+    def planted_recall(Q, K, plants, p, score="cumulant"):
+        hq, hkv = Q.shape[1], K.shape[1]
+        hits = 0
+        for pl in plants:
+            Kh = OR.as_f64(K[pl["b"], ns.kv_head(pl["h"], hq, hkv)])
+            mu, sigma = ns.block_stats(Kh, p.block)
+            C = ns.routable_blocks(pl["t"], p.block, mu.shape[0])
+            q = OR.as_f64(Q[pl["b"], pl["h"], pl["t"]])
+            if score == "tempered":
+                r = ns.tempered_scores(q, Kh, p.block, C, p.beta)
+            else:
+                r = ns.route_scores(q, mu[:C], sigma[:C], p.beta)
+            idx, _, _ = ns.select_topk(r, p.top_k)
+            hits += int(pl["block"] in idx.tolist())
+        return hits / len(plants)
+    ns.planted_recall = planted_recall
     return ns
 
 
@@ -679,6 +697,53 @@ def check_route_hier_hand(ns):
     assert out["idx"].tolist() == [0, 2], out
 
 
+def check_planted_recall_hand(ns):
+    """Hand-worked planted recall, B = 2, d = 2, n = 4, four query heads on two
+    KV heads (heads 0, 1 read KV head 0; heads 2, 3 KV head 1), every query
+    row at t = 3 equal to q = (1, 0), k = 1.  KV head 0: block 0 keys (3, 0)
+    and (-3, 0) (mu = 0, Sigma = diag(9, 0)), block 1 keys (1, 0) twice
+    (mu = (1, 0), Sigma = 0); KV head 1 the same blocks swapped.  Cumulant
+    scores: the spread block 4.5 beta, the tight block 1, so beta = 2 picks the
+    spread block and beta in {0, 0.2} the tight one.  Tempered scores: the
+    spread block log(cosh 3 beta) / beta (2.653 at beta = 2, 0.443 at
+    beta = 0.1), the tight block 1.  Plants (head, block) (1, 0), (2, 1),
+    (0, 1): recall 2/3 where the spread block wins, 1/3 where the tight one
+    does; reading KV head h % 2 instead of h // 2 gives 0 at beta = 2."""
+    Q = np.zeros((1, 4, 4, 2))
+    Q[0, :, 3] = [1.0, 0.0]
+    K = np.zeros((1, 2, 4, 2))
+    K[0, 0] = [[3, 0], [-3, 0], [1, 0], [1, 0]]
+    K[0, 1] = [[1, 0], [1, 0], [3, 0], [-3, 0]]
+    plants = [dict(b=0, h=1, t=3, block=0), dict(b=0, h=2, t=3, block=1),
+              dict(b=0, h=0, t=3, block=1)]
+    for beta, score, want in ((2.0, "cumulant", 2 / 3), (0.0, "cumulant", 1 / 3),
+                              (0.2, "cumulant", 1 / 3), (2.0, "tempered", 2 / 3),
+                              (0.1, "tempered", 1 / 3)):
+        got = ns.planted_recall(Q, K, plants, O.Params(2, 1, 1, beta, 1.0), score)
+        assert abs(got - want) < 1e-15, (beta, score, got, want)
+
+
+def check_gqa_dense_sdpa(ns, seed=23):
+    """k >= nb and W >= B under GQA (8 query heads on 2 KV heads): every row's
+    output is dense causal attention as torch's SDPA computes it with
+    enable_gqa (CPU, float64), which pins the query-head -> KV-head map."""
+    rng = np.random.default_rng(seed)
+    hq, hkv, n, d, B = 8, 2, 20, 4, 4
+    Q = rng.normal(size=(1, hq, n, d))
+    K = rng.normal(size=(1, hkv, n, d))
+    V = rng.normal(size=(1, hkv, n, d))
+    p = O.Params(B, n // B + 1, B, 2.0, 0.5)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(Q), torch.tensor(K), torch.tensor(V), is_causal=True, scale=0.5,
+        enable_gqa=True).numpy()
+    for h in range(hq):
+        kv = ns.kv_head(h, hq, hkv)
+        mu, sigma = ns.block_stats(K[0, kv], B)
+        for t in range(n):
+            row = ns.prefill_row(Q[0, h, t], K[0, kv], V[0, kv], mu, sigma, p, t)
+            np.testing.assert_allclose(row["O"], ref[0, h, t], rtol=1e-10, atol=1e-12)
+
+
 CHECKS = [check_golden, check_stats_vs_library, check_scores_two_ways, check_centroid_limit,
           check_topk_brute, check_dense_reduction, check_window_only, check_gather_equals_mask,
           check_recovery_law, check_recovery_law_pipeline, check_dropped_mass,
@@ -686,7 +751,8 @@ CHECKS = [check_golden, check_stats_vs_library, check_scores_two_ways, check_cen
           check_tempered_limits, check_tile_scores_moments, check_tile_select_brute,
           check_tile_single_row, check_tile_dense_reduction, check_backward_finite_differences,
           check_backward_autograd, check_backward_dense, check_group_bound_admissible,
-          check_route_hier_exact, check_route_hier_hand]
+          check_route_hier_exact, check_route_hier_hand, check_planted_recall_hand,
+          check_gqa_dense_sdpa]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda f: f.__name__)
@@ -875,6 +941,10 @@ def _mut_hier_bound_unused(q, mu, sigma, gs, m, k, beta, C):
     return out
 
 
+def _mut_kv_head_modulo(h, hq, hkv):
+    return h % hkv
+
+
 MUTANTS = {
     "sample_covariance": dict(block_stats=_mut_sample_cov),
     "beta_not_halved": dict(route_scores=_mut_full_beta),
@@ -905,6 +975,7 @@ MUTANTS = {
     "group_bound_no_covariance_slack": dict(group_bound=_mut_bound_no_lam),
     "hier_prune_on_equal": dict(route_hier=_mut_hier_prune_on_equal),
     "hier_never_prunes": dict(route_hier=_mut_hier_bound_unused),
+    "gqa_heads_interleaved": dict(kv_head=_mut_kv_head_modulo),
 }
 
 
@@ -921,9 +992,10 @@ def test_mutant_is_caught(name):
 
 
 def test_planted_recall_report():
-    """Planted-outlier recall, beta = 2 vs beta = 0 (centroid). PARITY UNPINNED:
-    the write-up reports only that the variance term recovers targets the
-    centroid misses; this checks that direction on the tiny workload."""
+    """Planted-outlier recall on the tiny workload, beta = 2 vs beta = 0
+    (centroid): the write-up reports that the variance term recovers targets
+    the centroid misses; this checks that direction (the function itself is
+    pinned by the hand-worked case above)."""
     from synth_inputs import CONFIGS, make_prefill
     wl = CONFIGS["tiny_prefill_4k"]
     data = make_prefill(wl, seed=0)
@@ -967,3 +1039,23 @@ def test_oracle_compositions_match_pinned_copies():
     b_ = ns.head_backward(Qg, K, V, idx, p, dO)
     for x, y in zip(a_, b_):
         assert np.array_equal(x, y)
+    # whole-input compositions: PrefillOracle rows and planted recall (GQA)
+    rng3 = np.random.default_rng(24)
+    hq, hkv = 6, 2
+    Q4 = rng3.normal(size=(2, hq, n, d))
+    K4 = rng3.normal(size=(2, hkv, n, d))
+    V4 = rng3.normal(size=(2, hkv, n, d))
+    orc = O.PrefillOracle(Q4, K4, V4, p)
+    for b, h, t in ((0, 0, 9), (1, 5, 74), (0, 3, 40), (1, 2, 17)):
+        kv = ns.kv_head(h, hq, hkv)
+        mu4, sg4 = ns.block_stats(K4[b, kv], B)
+        a = orc.row(b, h, t)
+        r = ns.prefill_row(Q4[b, h, t], K4[b, kv], V4[b, kv], mu4, sg4, p, t)
+        assert a["idx"].tolist() == r["idx"].tolist() and np.array_equal(a["O"], r["O"])
+    plants = [dict(b=int(rng3.integers(2)), h=int(rng3.integers(hq)), t=int(rng3.integers(n)),
+                   block=int(rng3.integers(n // B))) for _ in range(40)]
+    for beta, score in ((2.0, "cumulant"), (0.0, "cumulant"), (1.5, "tempered")):
+        pb = O.Params(B, 3, 5, beta, 0.45)
+        got = O.planted_recall(orc, plants, beta=beta, score=score)
+        want = ns.planted_recall(Q4, K4, plants, pb, score)
+        assert got == want, (beta, score, got, want)
