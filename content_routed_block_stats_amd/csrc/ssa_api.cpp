@@ -34,6 +34,10 @@ ssa_status from_hip(hipError_t e, const char* what) {
 constexpr int64_t kMaxSeq = int64_t(1) << 30;
 constexpr int64_t kMaxRowsPerHead = int64_t(1) << 26;   // n * (Hq/Hkv), packed row ids
 constexpr int64_t kMaxBlocksAttn = 16384;               // LDS histogram of the dispatch
+// query rows b * Hq * n of one call: 2^32 rows of 64 bfloat16 values are already
+// 512 GiB, more than one GPU holds; the bound keeps every workspace size and
+// index product well inside 64 bits
+constexpr int64_t kMaxRowsTotal = int64_t(1) << 32;
 
 ssa_status check_params(const ssa_params* p, ssa::Shape* s) {
   if (p == nullptr) return fail(SSA_ERR_INVALID_ARGUMENT, "params is NULL");
@@ -61,6 +65,8 @@ ssa_status check_params(const ssa_params* p, ssa::Shape* s) {
   if (p->out_dtype != SSA_F32 && p->out_dtype != SSA_BF16)
     return fail(SSA_ERR_INVALID_ARGUMENT, "out_dtype %d unknown", p->out_dtype);
   const int g = p->n_q_heads / p->n_kv_heads;
+  if (int64_t(p->batch) * p->n_q_heads > kMaxRowsTotal / p->seq_len)
+    return fail(SSA_ERR_UNSUPPORTED, "batch * n_q_heads * seq_len above 2^32 query rows");
   if (p->seq_len * g > kMaxRowsPerHead)
     return fail(SSA_ERR_UNSUPPORTED, "seq_len * (n_q_heads/n_kv_heads) above 2^26");
   s->b = p->batch;

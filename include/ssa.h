@@ -64,7 +64,9 @@ typedef enum ssa_op {
 /* Shapes and method parameters.  Limits checked by every call:
  *   batch >= 1; n_kv_heads >= 1; n_q_heads a positive multiple of n_kv_heads;
  *   head_dim in {64, 128};
- *   seq_len >= 1 (prefill: n; decode: the cache capacity in tokens);
+ *   seq_len in [1, 2^30] (prefill: n; decode: the cache capacity in tokens);
+ *   seq_len * (n_q_heads / n_kv_heads) at most 2^26 and
+ *   batch * n_q_heads * seq_len at most 2^32 (SSA_ERR_UNSUPPORTED otherwise);
  *   block_size a multiple of 64 in [64, 1024];
  *   top_k in [0, 32];  window >= 1;
  *   beta finite; scale finite and > 0;

@@ -486,7 +486,7 @@ def recovery_weight(beta: float, delta: float, mu: float) -> float:
     return 1.0 / (1.0 + math.exp(-z))
 
 
-# -- study without a pin ----------------------------------------------------------
+# -- planted-outlier recall (a study) ------------------------------------------------
 
 def planted_recall(oracle: PrefillOracle, plants: list[dict], beta: float | None = None,
                    score: str = "cumulant") -> float:
