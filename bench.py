@@ -49,7 +49,8 @@ def route_flops(wl) -> float:
 
 
 def gather_bytes(wl) -> float:
-    """Algorithmic HBM bytes of ssa_sparse_attn_fwd with block-major dispatch.
+    """Design HBM bytes of ssa_sparse_attn_fwd with block-major dispatch (the
+    bytes this design reads and writes, its own intermediates included).
 
     Per selected (row, block): the query row (2d bytes, bf16) read by the
     block's task, the fp16 partial written and read back (2 * (2d + 8)), the
@@ -67,6 +68,15 @@ def gather_bytes(wl) -> float:
     per_row = 2 * d + 4 * k + 2 * d + 4
     kv = wl.batch * wl.n_kv_heads * 4 * n * d * 2
     return float(sel * per_sel + rows * per_row + kv)
+
+
+def compulsory_gather_bytes(wl) -> float:
+    """Bytes ssa_sparse_attn_fwd cannot avoid: Q, K and V read once, idx read
+    once, O and LSE written once."""
+    e = 2 if wl.dtype == "bf16" else 4
+    rows = wl.batch * wl.n_q_heads * wl.seq_len
+    return float(rows * wl.head_dim * e * 2 + rows * (4 * wl.top_k + 4)
+                 + wl.batch * wl.n_kv_heads * wl.seq_len * wl.head_dim * e * 2)
 
 
 def kernel_source_digest(*names: str) -> str:
@@ -105,47 +115,145 @@ def counted_mfma_busy(prefix: str, digest: str):
     return None
 
 
-def cpu_baseline(wl, data, seconds: float) -> dict:
-    """Time the CPU oracle on a bounded sample of the workload (one thread)."""
+# -- CPU oracle baseline and dropped mass (worker processes) -------------------
+
+_W: dict = {}
+
+
+def _cpu_worker_init(folder: str, params: tuple) -> None:
+    """Worker start-up: BLAS on one thread, the KV head's arrays memory-mapped
+    from the parent's files (shared page cache), the oracle imported."""
+    from threadpoolctl import threadpool_limits
+
     import numpy as np
-    import torch
+
+    import oracle as O
+
+    _W["limits"] = threadpool_limits(limits=1)
+    for name in ("K", "V", "mu", "sigma", "q", "t", "sel"):
+        _W[name] = np.load(os.path.join(folder, name + ".npy"), mmap_mode="r")
+    _W["p"] = O.Params(*params)
+    _W["O"] = O
+
+
+def _cpu_worker_ready(_: int) -> int:
+    return int(_W["t"].shape[0])
+
+
+def _cpu_worker_rows(span: tuple) -> tuple:
+    """Rows [i0, i1) of the sample: the oracle's full row (timed), then the
+    dropped mass of the GPU's own selection for the row (untimed)."""
+    import numpy as np
+
+    O, p = _W["O"], _W["p"]
+    K, V, mu, sigma = _W["K"], _W["V"], _W["mu"], _W["sigma"]
+    busy, eps = 0.0, []
+    for i in range(*span):
+        t = int(_W["t"][i])
+        q = np.asarray(_W["q"][i])
+        t0 = time.perf_counter()
+        O.prefill_row(q, K, V, mu, sigma, p, t)
+        busy += time.perf_counter() - t0
+        S = O.key_set(t, np.asarray(_W["sel"][i]), p.block, p.window)
+        eps.append(O.dropped_mass(q, K, S, t, p.scale)[0])
+    return busy, eps
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(wl, data, idx, seconds: float, max_workers: int = 16) -> tuple[dict, dict]:
+    """The CPU oracle on a bounded sample of the workload, in worker processes
+    on the host cores this process may use (at most max_workers), one BLAS
+    thread each; also the dropped mass of the GPU's selection on the sampled
+    rows.  Returns (cpu_baseline, dropped_mass)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import tempfile
+
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle as O
 
     p = O.Params(wl.block, wl.top_k, wl.window, wl.beta, wl.scale)
+    cores = max(1, min(max_workers, len(os.sched_getaffinity(0))))
     rng = np.random.default_rng(0)
-    kv = 0
-    g = wl.group
+    kv, g = 0, wl.group
     Kh = O.as_f64(data["K"][0, kv].cpu())
     Vh = O.as_f64(data["V"][0, kv].cpu())
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         mu, sigma = O.block_stats(Kh, wl.block)
         t_stats = time.perf_counter() - t0
-        rows = 0
-        t_rows = 0.0
-        while t_rows < seconds and rows < 4096:
+        # one-thread rate on a few rows sizes the sample
+        t1 = time.perf_counter()
+        probe = 0
+        while time.perf_counter() - t1 < 1.0 and probe < 64:
             t = int(rng.integers(0, wl.seq_len))
-            h = kv * g + int(rng.integers(0, g))
-            q = O.as_f64(data["Q"][0, h, t].cpu())
-            t1 = time.perf_counter()
-            O.prefill_row(q, Kh, Vh, mu, sigma, p, t)
-            t_rows += time.perf_counter() - t1
-            rows += 1
-    per_row = t_rows / rows
-    total = wl.batch * wl.n_kv_heads * t_stats + wl.batch * wl.n_q_heads * wl.seq_len * per_row
-    return {
+            O.prefill_row(O.as_f64(data["Q"][0, kv * g, t].cpu()), Kh, Vh, mu, sigma, p, t)
+            probe += 1
+        per_row_1 = (time.perf_counter() - t1) / probe
+    rows = int(min(32768, max(cores * 8, cores * seconds / per_row_1)))
+    rows = (rows + cores - 1) // cores * cores
+    ts = rng.integers(0, wl.seq_len, size=rows)
+    hs = kv * g + rng.integers(0, g, size=rows)
+    import torch
+
+    ti = torch.as_tensor(ts, device=data["Q"].device)
+    hi = torch.as_tensor(hs, device=data["Q"].device)
+    qs = data["Q"][0][hi, ti].double().cpu().numpy()
+    sel = idx[0][hi, ti].cpu().numpy()
+    with tempfile.TemporaryDirectory(prefix="ssa_bench_") as folder:
+        for name, arr in (("K", Kh), ("V", Vh), ("mu", mu), ("sigma", sigma), ("q", qs),
+                          ("t", ts), ("sel", sel)):
+            np.save(os.path.join(folder, name + ".npy"), np.ascontiguousarray(arr))
+        params = (p.block, p.top_k, p.window, p.beta, p.scale)
+        # fresh interpreters (spawn): the workers never touch the GPU; a worker
+        # that fails breaks the pool (an exception here), it is not restarted
+        with cf.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn"),
+                                    initializer=_cpu_worker_init,
+                                    initargs=(folder, params)) as pool:
+            list(pool.map(_cpu_worker_ready, range(cores)))
+            per = rows // cores
+            spans = [(i * per, (i + 1) * per) for i in range(cores)]
+            t0 = time.perf_counter()
+            out = list(pool.map(_cpu_worker_rows, spans))
+            wall = time.perf_counter() - t0
+    busy = sum(o[0] for o in out)
+    eps = np.array([e for o in out for e in o[1]])
+    rate_rows = rows / wall                      # rows per second, all workers
+    n_rows = wl.batch * wl.n_q_heads * wl.seq_len
+    heads = wl.batch * wl.n_kv_heads
+    total = math.ceil(heads / cores) * t_stats + n_rows / rate_rows
+    total_1 = heads * t_stats + n_rows * (busy / rows)
+    base = {
         "value": wl.batch * wl.seq_len / total,
         "unit": "query-tokens/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"block statistics of 1 of {wl.batch * wl.n_kv_heads} KV heads "
-                   f"({t_stats:.2f} s) + {rows} query rows at uniform positions "
-                   f"({t_rows:.2f} s, {per_row * 1e3:.2f} ms/row), NumPy float64 on one "
-                   f"thread of {platform.processor() or platform.machine()}; full-job time "
-                   f"extrapolated to {total:.0f} s"),
+        "sample": (f"block statistics of 1 of {heads} KV heads ({t_stats:.2f} s, one thread) + "
+                   f"{rows} query rows of KV head 0 at uniform positions, {cores} worker "
+                   f"processes x 1 BLAS thread ({wall:.1f} s wall, {busy / rows * 1e3:.2f} ms "
+                   f"per row per worker), NumPy float64; full-job time extrapolated to "
+                   f"{total:.0f} s (heads' statistics in parallel rounds of {cores})"),
+        "cpu_model": _cpu_model(),
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+        "value_one_thread": wl.batch * wl.seq_len / total_1,
     }
+    dm = {"what": "dropped softmax mass 1 - exp(LSE_S - LSE_full) of the GPU's own selection "
+                  "(ssa_route_topk), oracle float64, on the sampled rows",
+          "rows": int(eps.size), "mean": float(eps.mean()), "p50": float(np.percentile(eps, 50)),
+          "p99": float(np.percentile(eps, 99)), "max": float(eps.max())}
+    return base, dm
 
 
 def bench_decode(steps: int, warmup: int) -> dict:
@@ -324,6 +432,44 @@ def recall_sweep(wl, seed: int, betas: list[float]) -> dict:
             "rows": rows}
 
 
+def onbox_peaks() -> dict:
+    """The card's own ceilings: the dense bf16 MFMA loop and a streaming read
+    of 4 GiB (larger than every cache), medians of 5 timed launches each."""
+    import statistics
+
+    import torch
+
+    import content_routed_block_stats_amd as ssa
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return statistics.median(out)
+
+    wgs, iters = 2048, 5000
+    flops = ssa.ssa_probe_mfma_bf16(wgs, 1)[1] * iters
+    ms_m = timed(lambda: ssa.ssa_probe_mfma_bf16(wgs, iters))
+    buf = torch.ones(1 << 30, dtype=torch.int32, device="cuda")     # 4 GiB
+    rwgs = 4096
+    out = torch.empty(rwgs * 256, dtype=torch.int32, device="cuda")
+    ms_r = timed(lambda: ssa.ssa_probe_hbm_read(buf, rwgs, out))
+    nbytes = buf.numel() * 4
+    del buf, out
+    return {"mfma_bf16_tflops": round(flops / (ms_m * 1e-3) / 1e12, 1),
+            "hbm_read_gbs": round(nbytes / (ms_r * 1e-3) / 1e9, 1),
+            "how": (f"ssa_probe_mfma_bf16: {wgs} workgroups x 4 waves x {iters} x 16 "
+                    "v_mfma_f32_32x32x16_bf16 on 4 chains; ssa_probe_hbm_read: 4 GiB, "
+                    f"{rwgs} workgroups x 256 threads x 16 B loads; medians of 5 launches")}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +482,10 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--recall-sweep", action="store_true",
                     help="only print the planted-recall-vs-beta study for --workload")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the on-card bf16 MFMA and HBM read ceilings")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not overwrite a 512 MB buffer (flushing the MALL) before each step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 2 GiB device->device (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -356,6 +506,12 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n}), flush=True)
         return 0
+
+    if args.peaks:
+        print(json.dumps(onbox_peaks()), flush=True)
+        return 0
+
+    import statistics
 
     import content_routed_block_stats_amd as ssa
     from synth_inputs import CONFIGS, make_prefill
@@ -402,7 +558,18 @@ def main() -> int:
         if ev:
             ev[3].record()
 
+    # the MALL (256 MB) is flushed before each step by overwriting 512 MB,
+    # outside the step's events
+    flush_buf = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+
+    print("[bench] on-card peaks", file=sys.stderr, flush=True)
+    peaks = onbox_peaks()
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -411,17 +578,25 @@ def main() -> int:
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
+        flush()
         step(evs[i])
     stop.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    st = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
+    ms_wall = start.elapsed_time(stop) / args.steps
+    # medians over the timed steps: the whole step and each stage
+    ms = statistics.median(e[0].elapsed_time(e[3]) for e in evs)
+    ms_mean = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+    st = [statistics.median(e[j].elapsed_time(e[j + 1]) for e in evs) for j in range(3)]
     t_stats, t_route, t_attn = st
+    idx_step = idx.clone()     # later stages reuse idx; the dropped mass needs the step's
 
     rf = route_flops(wl)
     achieved = rf / (t_route * 1e-3) / 1e12
     gb = gather_bytes(wl)
     gbs = gb / (t_attn * 1e-3) / 1e9
+    cb = compulsory_gather_bytes(wl)
+    pairs = attn_pairs(wl, idx)
+    logical = pairs * 2 * wl.head_dim * (2 if wl.dtype == "bf16" else 4)
     route_digest = kernel_source_digest("route_topk.hip", "ssa_common.hpp")
     attn_digest = kernel_source_digest("sparse_attn.hip", "kv_chunks.hpp", "ssa_common.hpp")
     tokens = b * n
@@ -433,6 +608,11 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_mean": round(ms_mean, 4),
+        "ms_per_step_wall_incl_flush": round(ms_wall, 4),
+        "timing": ("medians over the timed steps of HIP events on the launch stream; "
+                   + ("a 512 MB buffer overwritten before each step (MALL flush), outside the "
+                      "events" if flush_buf is not None else "no cache flush")),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -446,14 +626,27 @@ def main() -> int:
         "roofline": {"kernel": "route_topk", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "peak_onbox": peaks["mfma_bf16_tflops"],
+                     "frac_onbox": round(achieved / peaks["mfma_bf16_tflops"], 4),
                      "traffic": counted_traffic("route_topk", route_digest),
-                     "mfma_busy_counted": counted_mfma_busy("route_topk_kernel", route_digest),
+                     "mfma_busy_counted": counted_mfma_busy("route_fast_kernel", route_digest),
                      "algorithmic_flops_per_launch": rf},
         "roofline_gather": {"kernel": "sparse_attn_fwd", "bound": "hbm", "achieved": round(gbs, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "peak_onbox": peaks["hbm_read_gbs"],
+                            "frac_onbox": round(gbs / peaks["hbm_read_gbs"], 4),
                             "traffic": counted_traffic("sparse_attn_fwd", attn_digest),
-                            "algorithmic_bytes_per_launch": gb},
+                            "bytes_basis": "design bytes (this design's reads and writes, "
+                                           "fp16 partials included)",
+                            "design_bytes_per_launch": gb,
+                            "compulsory_bytes_per_launch": cb,
+                            "compulsory_gbs": round(cb / (t_attn * 1e-3) / 1e9, 1),
+                            "effective_gather_gbs": round(logical / (t_attn * 1e-3) / 1e9, 1),
+                            "effective_gather_note": ("K and V bytes of every (row, key of S(t)) "
+                                                      "pair as a per-row gather would read them, "
+                                                      "over the stage time")},
+        "onbox_peaks": peaks,
     }
     # the query-tile-shared variant: one selection per tile of B positions
     tiles = (n + wl.block - 1) // wl.block
@@ -529,7 +722,6 @@ def main() -> int:
     tb1.record()
     torch.cuda.synchronize()
     t_bwd = tb0.elapsed_time(tb1) / breps
-    pairs = attn_pairs(wl, idx)
     bwd_fl = 14.0 * wl.head_dim * pairs
     res["backward"] = {"what": "dQ, dK, dV through the attention over the step's selections",
                        "ms": round(t_bwd, 3), "ms_vs_forward_attention": round(t_bwd / t_attn, 2),
@@ -564,7 +756,8 @@ def main() -> int:
         res["decode"] = bench_decode(steps=max(5, args.steps), warmup=2)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds)
+        res["cpu_baseline"], res["dropped_mass"] = cpu_baseline(wl, data, idx_step,
+                                                                args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     ssa_decode_step,
     ssa_decode_step_noalloc,
     ssa_group_stats,
+    ssa_probe_hbm_read,
+    ssa_probe_mfma_bf16,
     ssa_route_hier,
     ssa_route_tempered,
     ssa_route_tiles,

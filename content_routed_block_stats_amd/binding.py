@@ -80,10 +80,14 @@ def lib() -> ctypes.CDLL:
     L.ssa_group_stats.argtypes = [P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp]
     L.ssa_route_hier.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
                                  _vp, ctypes.c_size_t, _vp]
+    L.ssa_probe_mfma_bf16.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_double), _vp]
+    L.ssa_probe_hbm_read.argtypes = [_vp, ctypes.c_size_t, _vp, ctypes.c_int32, _vp]
     for name in ("ssa_block_stats", "ssa_workspace_size", "ssa_route_topk", "ssa_route_tempered",
                  "ssa_route_tiles", "ssa_tile_attn_fwd", "ssa_sparse_attn_fwd",
                  "ssa_sparse_attn_bwd", "ssa_decode_step", "ssa_decode_step_noalloc",
-                 "ssa_group_stats", "ssa_route_hier"):
+                 "ssa_group_stats", "ssa_route_hier", "ssa_probe_mfma_bf16",
+                 "ssa_probe_hbm_read"):
         getattr(L, name).restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
@@ -445,3 +449,24 @@ def ssa_route_hier(q: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, gmu: 
                                 _ptr(gsigma), _ptr(grl), group_blocks, _ptr(pos), _ptr(idx),
                                 _ptr(ev), _ptr(ws), ws.numel(), _stream()))
     return (idx, ev) if want_evaluated else idx
+
+
+# -- peak probes (include/ssa_probes.h) ----------------------------------------
+
+def ssa_probe_mfma_bf16(workgroups: int, iters: int, device="cuda"):
+    """Launch the dense bf16 MFMA loop on the current stream -> (out, flops)."""
+    out = torch.empty((workgroups,), dtype=torch.float32, device=device)
+    fl = ctypes.c_double(0.0)
+    _check(lib().ssa_probe_mfma_bf16(_ptr(out), workgroups, iters, ctypes.byref(fl), _stream()))
+    return out, fl.value
+
+
+def ssa_probe_hbm_read(buf: torch.Tensor, workgroups: int, out: torch.Tensor | None = None):
+    """Launch the streaming read of buf (contiguous, on the GPU) on the current
+    stream -> out (uint32 as int32, [workgroups * 256])."""
+    _dev_check(buf)
+    if out is None:
+        out = torch.empty((workgroups * 256,), dtype=torch.int32, device=buf.device)
+    _check(lib().ssa_probe_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                    workgroups, _stream()))
+    return out

@@ -1,6 +1,8 @@
 """The C ABI on the host (no GPU): the library loads, exports every function
-include/ssa.h declares, and rejects invalid arguments before touching a device."""
+the headers under include/ declare, and rejects invalid arguments before
+touching a device."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,21 +12,24 @@ import content_routed_block_stats_amd as ssa
 from content_routed_block_stats_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ssa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(ssa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     lib = ssa.lib()
     names = _declared_functions()
-    assert {"ssa_block_stats", "ssa_route_topk", "ssa_sparse_attn_fwd", "ssa_decode_step"} <= set(names)
+    assert {"ssa_block_stats", "ssa_route_topk", "ssa_sparse_attn_fwd", "ssa_decode_step",
+            "ssa_probe_mfma_bf16", "ssa_probe_hbm_read"} <= set(names)
     for name in names:
-        assert hasattr(lib, name), f"{name} declared in ssa.h but not exported"
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
     assert lib.ssa_version() >= 100
 
 
@@ -192,3 +197,20 @@ def test_decode_noalloc_checked_on_host():
     got = L.ssa_decode_step_noalloc(ctypes.byref(_p(block_size=48)), 256, 256, 256, 256, 256,
                                     256, 256, 256, None, 256, 256, None)
     assert got == B.SSA_ERR_INVALID_ARGUMENT
+
+
+def test_peak_probes_check_arguments_on_host():
+    lib = ssa.lib()
+    fl = ctypes.c_double(0.0)
+    dummy = ctypes.c_void_p(4096)   # never dereferenced: every call below is rejected first
+    assert lib.ssa_probe_mfma_bf16(None, 8, 8, ctypes.byref(fl), None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_mfma_bf16(dummy, 0, 8, ctypes.byref(fl), None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_mfma_bf16(dummy, 8, 0, ctypes.byref(fl), None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_mfma_bf16(dummy, 8, 8, None, None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_hbm_read(None, 1024, dummy, 8, None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_hbm_read(dummy, 1000, dummy, 8, None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_hbm_read(dummy, 0, dummy, 8, None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_hbm_read(dummy, 1024, None, 8, None) == B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_hbm_read(ctypes.c_void_p(4100), 1024, dummy, 8, None) == \
+        B.SSA_ERR_INVALID_ARGUMENT
+    assert lib.ssa_probe_hbm_read(dummy, 1024, dummy, 0, None) == B.SSA_ERR_INVALID_ARGUMENT
