@@ -9,6 +9,8 @@ properties that hold at any size on every row.
 from __future__ import annotations
 
 import math
+import json
+import os
 import sys
 
 import numpy as np
@@ -75,6 +77,7 @@ def compare_prefill(data, res, wl, rows=None, check_stats=True, O32=None, lse32=
     o_tol = O_TOL[wl.dtype]
     n_exact = n_tie = 0
     worst_o = worst_l = worst_o32 = 0.0
+    eps = []
     for (b, h, t) in rows:
         row = orc.row(b, h, t)
         ok, exact = idx_ok(idx[b, h, t], row)
@@ -92,6 +95,9 @@ def compare_prefill(data, res, wl, rows=None, check_stats=True, O32=None, lse32=
         eo, el = attn_errors(Og[b, h, t], lg[b, h, t], qrow, Kh, Vh, idx[b, h, t], t, p,
                              bf16_out=bf16_out)
         worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        # dropped softmax mass of the GPU's selection (reported, not checked)
+        eps.append(O.dropped_mass(qrow, Kh, O.key_set(t, idx[b, h, t], p.block, p.window), t,
+                                  p.scale)[0])
         assert eo <= o_tol, f"O error {eo:.3g} at row {(b, h, t)}"
         assert el <= LSE_TOL, f"LSE error {el:.3g} at row {(b, h, t)}"
         if O32 is not None:       # the same inputs with a float32 output tensor
@@ -100,6 +106,16 @@ def compare_prefill(data, res, wl, rows=None, check_stats=True, O32=None, lse32=
             assert e32 <= o_tol, f"float32-output O error {e32:.3g} at row {(b, h, t)}"
     say(f"  rows {len(rows)}: exact selections {n_exact}, allowed near-ties {n_tie}, "
         f"max|dO| {worst_o:.3g} (f32 out {worst_o32:.3g}), max|dLSE| {worst_l:.3g}")
+    e = np.asarray(eps)
+    rec = {"case": wl.name, "rows": len(rows), "exact": n_exact, "near_ties": n_tie,
+           "dropped_mass": {"rows": int(e.size), "mean": float(e.mean()),
+                            "p50": float(np.percentile(e, 50)), "p99": float(np.percentile(e, 99)),
+                            "max": float(e.max())}}
+    say("  report:", json.dumps(rec))
+    path = os.environ.get("SSA_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
     return n_exact, n_tie
 
 
