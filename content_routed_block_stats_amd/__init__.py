@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     ssa_probe_hbm_read,
     ssa_probe_mfma_bf16,
     ssa_route_hier,
+    ssa_route_hier_prefill,
+    ssa_route_hier_prefill_workspace_size,
     ssa_route_tempered,
     ssa_route_tiles,
     ssa_route_topk,

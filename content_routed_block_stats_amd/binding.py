@@ -80,13 +80,18 @@ def lib() -> ctypes.CDLL:
     L.ssa_group_stats.argtypes = [P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp]
     L.ssa_route_hier.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
                                  _vp, ctypes.c_size_t, _vp]
+    L.ssa_route_hier_prefill_workspace_size.argtypes = [P, ctypes.c_int32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+    L.ssa_route_hier_prefill.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp,
+                                         _vp, _vp, ctypes.c_size_t, _vp]
     L.ssa_probe_mfma_bf16.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_double), _vp]
     L.ssa_probe_hbm_read.argtypes = [_vp, ctypes.c_size_t, _vp, ctypes.c_int32, _vp]
     for name in ("ssa_block_stats", "ssa_workspace_size", "ssa_route_topk", "ssa_route_tempered",
                  "ssa_route_tiles", "ssa_tile_attn_fwd", "ssa_sparse_attn_fwd",
                  "ssa_sparse_attn_bwd", "ssa_decode_step", "ssa_decode_step_noalloc",
-                 "ssa_group_stats", "ssa_route_hier", "ssa_probe_mfma_bf16",
+                 "ssa_group_stats", "ssa_route_hier", "ssa_route_hier_prefill_workspace_size",
+                 "ssa_route_hier_prefill", "ssa_probe_mfma_bf16",
                  "ssa_probe_hbm_read"):
         getattr(L, name).restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
@@ -448,6 +453,54 @@ def ssa_route_hier(q: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, gmu: 
     _check(lib().ssa_route_hier(ctypes.byref(p), _ptr(q), _ptr(mu), _ptr(sigma), _ptr(gmu),
                                 _ptr(gsigma), _ptr(grl), group_blocks, _ptr(pos), _ptr(idx),
                                 _ptr(ev), _ptr(ws), ws.numel(), _stream()))
+    return (idx, ev) if want_evaluated else idx
+
+
+def ssa_route_hier_prefill_workspace_size(p: SSAParams, group_blocks: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ssa_route_hier_prefill_workspace_size(ctypes.byref(p), group_blocks,
+                                                       ctypes.byref(n)))
+    return n.value
+
+
+def route_tile_count(seq_len: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """512-row tiles per (sequence, KV head) of ssa_route_hier_prefill's rows."""
+    return -(-seq_len * (n_q_heads // n_kv_heads) // 512)
+
+
+def ssa_route_hier_prefill(Q: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor,
+                           gmu: torch.Tensor, gsigma: torch.Tensor, grl: torch.Tensor, *,
+                           block_size: int, group_blocks: int, top_k: int, beta: float = 2.0,
+                           want_evaluated: bool = False, idx: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None):
+    """Exact top-k of prefill rows Q [b, Hq, n, d] (bfloat16) by branch and
+    bound over groups -> idx [b, Hq, n, k] int32 (, evaluated [b, Hkv, tiles]
+    int32: blocks scored per 512-row tile).  gmu/gsigma/grl come from
+    ssa_group_stats of mu/sigma with the same group_blocks."""
+    _dev_check(Q, mu, sigma, gmu, gsigma, grl)
+    b, hq, n, d = Q.shape
+    hkv, nb = mu.shape[1], mu.shape[2]
+    if mu.shape != (b, hkv, nb, d) or sigma.shape != (*mu.shape, d):
+        raise ValueError("mu/sigma do not match Q")
+    if nb != n // block_size:
+        raise ValueError("mu/sigma must hold n // block_size blocks")
+    if group_blocks < 1:
+        raise ValueError("group_blocks must be positive")
+    G = -(-nb // group_blocks)
+    if gmu.shape != (b, hkv, G, d) or gsigma.shape != (b, hkv, G, d, d) or grl.shape != (b, hkv, G, 2):
+        raise ValueError("group summaries do not match mu")
+    p = make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=n,
+                    block_size=block_size, top_k=top_k, beta=beta, in_dtype=Q.dtype)
+    if idx is None:
+        idx = torch.empty((b, hq, n, top_k), dtype=torch.int32, device=Q.device)
+    ev = (torch.empty((b, hkv, route_tile_count(n, hq, hkv)), dtype=torch.int32, device=Q.device)
+          if want_evaluated else None)
+    need = ssa_route_hier_prefill_workspace_size(p, group_blocks)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    _check(lib().ssa_route_hier_prefill(ctypes.byref(p), _ptr(Q), _ptr(mu), _ptr(sigma), _ptr(gmu),
+                                        _ptr(gsigma), _ptr(grl), group_blocks, _ptr(idx), _ptr(ev),
+                                        _ptr(workspace), workspace.numel(), _stream()))
     return (idx, ev) if want_evaluated else idx
 
 

@@ -248,6 +248,10 @@ RouteWs route_ws_layout(const Shape& s, void* base) {
 // ||sym(lo)||_2 = ||A||_2 / 2 <= sqrt(||A^2||_F) / 2; A^2 runs on the float16
 // MFMA (products exact, float32 sums: ||A^2 - computed||_F <= d 2^-24 ||A||_F^2);
 // the low part's own rounding E = (T'_c - hi_c) - lo adds at most ||E||_F.
+//
+// D comes from shift_sigma (shift_nb blocks per KV head): the blocks' own
+// Sigma for block images, the blocks' Sigma too for images of group summaries,
+// so that group bounds and block scores leave out the same q^T diag(D) q.
 template <bool F32, int D>
 __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ mu,
                                                           const float* __restrict__ sigma,
@@ -255,7 +259,9 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
                                                           uint32_t* __restrict__ bounds,
                                                           float* __restrict__ dbar,
                                                           uint8_t* __restrict__ prep, int64_t nb,
-                                                          float beta) {
+                                                          float beta,
+                                                          const float* __restrict__ shift_sigma,
+                                                          int64_t shift_nb) {
   using Lay = RouteLayout<D>;
   constexpr int AS = D + 8;   // row stride of A (halves), against LDS bank conflicts
   __shared__ float red[4][4];
@@ -272,8 +278,8 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
   if constexpr (!F32) {
     // D: mean of the first blocks' (beta/2) diagonals (any vector common to
     // the KV head's blocks leaves the ranking unchanged; this one keeps T' small)
-    const int64_t m = nb < kShiftBlocks ? nb : kShiftBlocks;
-    const float* S0 = sigma + bkv * nb * int64_t(D) * D;
+    const int64_t m = shift_nb < kShiftBlocks ? shift_nb : kShiftBlocks;
+    const float* S0 = shift_sigma + bkv * shift_nb * int64_t(D) * D;
     for (int j = tid; j < D; j += blockDim.x) {
       float acc = 0.f;
       for (int64_t c = 0; c < m; ++c) acc += half_beta * S0[(c * D + j) * D + j];
@@ -1232,6 +1238,90 @@ __global__ __launch_bounds__(kRecCap) void route_scatter_kernel(
 
 constexpr int kRescoreThreads = 256;
 
+// The exact (hi + lo) score of a lane's row against the block image at L (in
+// LDS), with the exact pass's arithmetic operation for operation: per output
+// tile from the widest down, an MFMA chain from mu over the chunks in order
+// (hi then lo of each), then the row-dot of the tile; the lane halves summed;
+// times the image's scale.  Lane (ln, h) returns row ln of query tile h.
+//
+// With lin != nullptr it also returns, in the same units, the mean term
+// <q, mu> alone (the row-dot of q with the image's mu).
+template <int D>
+__device__ __forceinline__ float hilo_score(const uint8_t* L, const f16x8 (&bq)[2][D / 16],
+                                            int lane, float* lin = nullptr) {
+  using Lay = RouteLayout<D>;
+  constexpr int MT = Lay::MT;
+  const int h = lane / 32;
+  // fragment (mt, chunk s2, part) of the image
+  auto frag = [&](int mt, int s2, int part) {
+    return *reinterpret_cast<const f16x8*>(L + Lay::frag(mt, s2) * kFragBytes + part * 1024 +
+                                           lane * 16);
+  };
+  float pt[2] = {0.f, 0.f}, pl[2] = {0.f, 0.f};
+  // chunks move one ahead of their MFMAs (hi and lo of the next chunk are
+  // read before this chunk's four MFMAs); the scheduling barriers keep the
+  // compiler from reading the whole image ahead, which needs more registers
+  // than a wave has
+  f16x8 cur[2] = {frag(MT - 1, 0, 0), frag(MT - 1, 0, 1)};
+#pragma unroll
+  for (int mt = MT - 1; mt >= 0; --mt) {
+    floatx16 acc[2];
+    {
+      const floatx4* p = reinterpret_cast<const floatx4*>(L + Lay::MU_OFF + mt * 64) + h * (MT * 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 v = p[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[0][4 * q + e] = v[e];
+      }
+      acc[1] = acc[0];
+    }
+    if (lin != nullptr) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int a = j / 4, bb = j % 4;
+          pl[nt] = fmaf(acc[nt][j], static_cast<float>(bq[nt][2 * mt + (a >> 1)][4 * (a & 1) + bb]), pl[nt]);
+        }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 <= 2 * mt + 1; ++s2) {
+      f16x8 nxt[2] = {cur[0], cur[1]};
+      if (s2 < 2 * mt + 1) {
+        nxt[0] = frag(mt, s2 + 1, 0);
+        nxt[1] = frag(mt, s2 + 1, 1);
+      } else if (mt > 0) {
+        nxt[0] = frag(mt - 1, 0, 0);
+        nxt[1] = frag(mt - 1, 0, 1);
+      }
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[nt] = mma16(cur[part], bq[nt][s2], acc[nt]);
+      cur[0] = nxt[0];
+      cur[1] = nxt[1];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int a = j / 4, bb = j % 4;
+        pt[nt] = fmaf(acc[nt][j], static_cast<float>(bq[nt][2 * mt + (a >> 1)][4 * (a & 1) + bb]), pt[nt]);
+      }
+  }
+  const float scale = *reinterpret_cast<const float*>(L + Lay::SCALE_OFF);
+  if (lin != nullptr) {
+    const float l0 = pl[0] + wave_shfl_xor(pl[0], 32);
+    const float l1 = pl[1] + wave_shfl_xor(pl[1], 32);
+    *lin = (h ? l1 : l0) * scale;
+  }
+  const float s0 = pt[0] + wave_shfl_xor(pt[0], 32);
+  const float s1 = pt[1] + wave_shfl_xor(pt[1], 32);
+  return (h ? s1 : s0) * scale;
+}
+
 // Workgroup (c, KV head): the exact (hi + lo) score of block c for every pair
 // in c's list, then for every full row that can route to c, 64 rows per wave
 // at a time (two 32-row MFMA tiles).  The arithmetic is the exact pass's,
@@ -1250,7 +1340,7 @@ __global__ __launch_bounds__(kRescoreThreads) void route_rescore_kernel(
     int64_t n_tiles, int L) {
   using Lay = RouteLayout<D>;
   using QT = f16x8;
-  constexpr int MT = Lay::MT, NS = Lay::NS, BYTES = Lay::BLOCK_BYTES;
+  constexpr int NS = Lay::NS, BYTES = Lay::BLOCK_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[Lay::LDS_BYTES];
   const int64_t c = blockIdx.x, bkv = blockIdx.y;
   const int32_t cnt = pcnt[bkv * nb + c];
@@ -1268,47 +1358,11 @@ __global__ __launch_bounds__(kRescoreThreads) void route_rescore_kernel(
     __syncthreads();
   }
   const float qsc = ldexpf(1.f, -query_exponent(qmax[bkv]));
-  const float scale_c = *reinterpret_cast<const float*>(lds + Lay::SCALE_OFF);
   // the score of the lane's row (tile h, row ln) for block c
   auto score = [&](const int64_t (&rho_of)[2], const bool (&valid)[2]) {
     QT bq[2][NS];
     load_q_tiles<false, D>(bq, Q, rho_of, valid, b, kv, g, hq, n, h, qsc);
-    float pt[2] = {0.f, 0.f};
-#pragma unroll
-    for (int mt = MT - 1; mt >= 0; --mt) {
-      floatx16 acc[2];
-      {
-        const floatx4* p =
-            reinterpret_cast<const floatx4*>(lds + Lay::MU_OFF + mt * 64) + h * (MT * 4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const floatx4 v = p[q];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[0][4 * q + e] = v[e];
-        }
-        acc[1] = acc[0];
-      }
-#pragma unroll
-      for (int s2 = 0; s2 <= 2 * mt + 1; ++s2)
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const QT a = *reinterpret_cast<const QT*>(lds + Lay::frag(mt, s2) * kFragBytes +
-                                                    part * 1024 + lane * 16);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[nt] = mma16(a, bq[nt][s2], acc[nt]);
-        }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int a = j / 4, bb = j % 4;
-          pt[nt] = fmaf(acc[nt][j], static_cast<float>(bq[nt][2 * mt + (a >> 1)][4 * (a & 1) + bb]),
-                        pt[nt]);
-        }
-    }
-    const float s0 = pt[0] + wave_shfl_xor(pt[0], 32);
-    const float s1 = pt[1] + wave_shfl_xor(pt[1], 32);
-    return (h ? s1 : s0) * scale_c;
+    return hilo_score<D>(lds, bq, lane);
   };
   const int64_t rec0 = bkv * n_tiles * kRecCap;
   const uint32_t* ent = pent + rec0 * L + poff[bkv * nb + c];
@@ -1432,7 +1486,8 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
   }
   if (s.nb > 0) {
     hipLaunchKernelGGL((route_prep_kernel<F32, D>), dim3(unsigned(s.nb), unsigned(n_bkv)),
-                       dim3(256), 0, st, mu, sigma, w.qmax, w.bounds, w.dbar, w.img, s.nb, s.beta);
+                       dim3(256), 0, st, mu, sigma, w.qmax, w.bounds, w.dbar, w.img, s.nb, s.beta,
+                       sigma, s.nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1497,6 +1552,484 @@ hipError_t launch_route_d(const Shape& s, const void* Q, const float* mu, const 
   return launch_route_t<F32, D, 32>(s, Q, mu, sigma, idx, kth, ws, st);
 }
 
+// ------------------------------------------ hierarchical routing (prefill) --
+//
+// The flat top-k by branch and bound over groups of m consecutive blocks,
+// for prefill query rows.  A group's summary (ssa_group_stats: mean centroid
+// mu_G, radius R_G, mean covariance S_G, slack lam_G) bounds every member's
+// score for beta >= 0:
+//   UB_G(q) = r_G(q) + ||q|| R_G + (beta/2) lam_G ||q||^2,
+// r_G the routing score of (mu_G, S_G).  r_G is computed like a block score:
+// the summaries are prepared into the same images (with the blocks' diagonal
+// shift, so bounds and scores leave out the same q^T diag(D) q) and scored
+// with the exact pass's hi + lo arithmetic; the bound carries a relative
+// margin (kHierPrefillMargin of its terms' magnitudes) over float32 rounding.
+//
+// Blocks are scored for a tile of rows at a time (one image in LDS serves
+// 512 rows), so a tile pays for the union of what its rows need.  Rows are
+// therefore regrouped first: within each chunk of kHierChunk consecutive
+// 512-row tiles (nearby positions, so similar routable ranges), by the group
+// of their largest bound, so that a tile's rows tend to need the same few
+// groups.
+//
+//  * bound: per 512-row tile of a KV head's rows (in row order), UB_G of
+//    every row for every group with a routable block in the tile (row-major
+//    in the workspace), each row's best group, and per group the number of
+//    the tile's rows it is best for.
+//  * scan + order: rows listed chunk by chunk, by best group within a chunk
+//    (ties keep row order); tiles of 512 consecutive list entries.
+//  * visit: per listed tile, the groups in decreasing order of the tile's
+//    largest bound; a group is scored -- each of its blocks against all the
+//    tile's rows, merged into each row's running top-k -- unless, for every
+//    row, its bound is strictly below the row's running k-th score.  Skipped
+//    blocks score below each row's k-th (ties included), so every row gets
+//    exactly the flat selection, with the exact pass's scores.
+
+constexpr float kHierPrefillMargin = 1e-4f;
+constexpr int kHierSortMax = 4096;   // groups per (sequence, KV head) the visit orders
+constexpr int kHierChunk = 16;       // row tiles whose rows are regrouped together
+
+__host__ __device__ inline int64_t hier_chunks(int64_t n_tiles) {
+  return (n_tiles + kHierChunk - 1) / kHierChunk;
+}
+
+int64_t hier_groups(const Shape& s, int m) { return (s.nb + m - 1) / m; }
+
+struct HierWs {
+  uint8_t* img;      // block images [b*hkv][nb]
+  uint8_t* gimg;     // group images [b*hkv][G]
+  uint32_t* qmax;    // [b*hkv], then bounds [b*hkv][4] (unused here)
+  uint32_t* gbounds; // [b*hkv][4] (unused here)
+  float* dbar;       // [b*hkv][d]
+  float* gdbar;      // [b*hkv][d]
+  float* ub;         // [b*hkv][rows][G]: bounds, row-major
+  int32_t* best;     // [b*hkv][rows]: each row's best group
+  int32_t* gcnt;     // [b*hkv][chunk][G][kHierChunk]: rows of each tile whose best group is g
+  int32_t* goff;     // same: exclusive prefix in (chunk, g, tile) order
+  int32_t* gtot;     // [b*hkv]
+  int32_t* list;     // [b*hkv][rows]: rows by best group
+  size_t bytes;
+};
+
+HierWs hier_ws_layout(const Shape& s, int m, void* base) {
+  HierWs w{};
+  const size_t per = s.d == 64 ? RouteLayout<64>::BLOCK_BYTES : RouteLayout<128>::BLOCK_BYTES;
+  const size_t n_bkv = size_t(s.b) * s.hkv, nt = size_t(route_tiles(s));
+  const size_t rows = size_t(s.n) * size_t(s.g);
+  const size_t G = size_t(hier_groups(s, m));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t o_img = take(n_bkv * size_t(s.nb) * per + 1024);
+  const size_t o_gimg = take(n_bkv * G * per + 1024);
+  const size_t o_q = take(n_bkv * 4 * 5);
+  const size_t o_gb = take(n_bkv * 4 * 4);
+  const size_t o_db = take(n_bkv * size_t(s.d) * 4);
+  const size_t o_gdb = take(n_bkv * size_t(s.d) * 4);
+  const size_t o_ub = take(n_bkv * rows * G * 4);
+  const size_t o_best = take(n_bkv * rows * 4);
+  const size_t nc = size_t(hier_chunks(int64_t(nt))) * kHierChunk;
+  const size_t o_gc = take(n_bkv * G * nc * 4);
+  const size_t o_go = take(n_bkv * G * nc * 4);
+  const size_t o_gt = take(n_bkv * 4);
+  const size_t o_li = take(n_bkv * rows * 4);
+  w.bytes = off;
+  if (base != nullptr) {
+    uint8_t* p = static_cast<uint8_t*>(base);
+    w.img = p + o_img;
+    w.gimg = p + o_gimg;
+    w.qmax = reinterpret_cast<uint32_t*>(p + o_q);
+    w.gbounds = reinterpret_cast<uint32_t*>(p + o_gb);
+    w.dbar = reinterpret_cast<float*>(p + o_db);
+    w.gdbar = reinterpret_cast<float*>(p + o_gdb);
+    w.ub = reinterpret_cast<float*>(p + o_ub);
+    w.best = reinterpret_cast<int32_t*>(p + o_best);
+    w.gcnt = reinterpret_cast<int32_t*>(p + o_gc);
+    w.goff = reinterpret_cast<int32_t*>(p + o_go);
+    w.gtot = reinterpret_cast<int32_t*>(p + o_gt);
+    w.list = reinterpret_cast<int32_t*>(p + o_li);
+  }
+  return w;
+}
+
+// ||q'||^2 of the lane's row (tile h, row ln), float16 values, float32 sum.
+template <int D>
+__device__ __forceinline__ float row_norm2(const f16x8 (&bq)[2][D / 16], int h) {
+  float nq[2] = {0.f, 0.f};
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = static_cast<float>(bq[nt][s2][e]);
+        nq[nt] = fmaf(x, x, nq[nt]);
+      }
+  const float a = nq[0] + wave_shfl_xor(nq[0], 32);
+  const float b = nq[1] + wave_shfl_xor(nq[1], 32);
+  return h ? b : a;
+}
+
+// Direct global->LDS copy of one image (all waves of the workgroup), written
+// in asm with m0 saved and restored around each copy, as in the single pass:
+// the compiler then does not make every later LDS read wait for the copy
+// (it cannot tell the buffers apart), so a copy into one buffer overlaps the
+// work on the other.  The caller waits (s_waitcnt vmcnt(0)) and barriers
+// before reading the copied buffer.
+template <int D>
+__device__ __forceinline__ void stage_image(const uint8_t* src, uint8_t* dst, int wave, int lane,
+                                            int waves) {
+  using Lay = RouteLayout<D>;
+  const uint32_t base =
+      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(dst)));
+  for (int r = wave; r < Lay::DMA_ROWS; r += waves) {
+    const uint8_t* g = src + r * 1024 + lane * 16;
+    const uint32_t l = __builtin_amdgcn_readfirstlane(base + uint32_t(r * 1024));
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "v"(g), "s"(l)
+        : "memory");
+  }
+}
+
+// Workgroup (tile, KV head), rows in row order: UB_G for the tile's rows and
+// every group with a block routable in the tile (-inf where none is routable
+// for the row), each row's best group (the lowest of its largest bounds; 0
+// when it has none), and the tile's count of rows per best group.
+template <int D>
+__global__ __launch_bounds__(kRouteThreads) void hier_ub_kernel(
+    const bf16_t* __restrict__ Q, const uint8_t* __restrict__ gimg, const float* __restrict__ grl, const uint32_t* __restrict__ qmax, float* __restrict__ ub,
+    int32_t* __restrict__ best, int32_t* __restrict__ gcnt, int64_t n, int g, int hq, int hkv,
+    int B, int64_t nb, int m, int64_t G, int64_t n_tiles, int64_t n_bkv, float beta) {
+  using Lay = RouteLayout<D>;
+  constexpr int NS = D / 16, BYTES = Lay::BLOCK_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Lay::LDS_BYTES];
+  __shared__ int32_t hist[kHierSortMax];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int64_t wid = blockIdx.x;
+  const int64_t bkv = wid % n_bkv;
+  const int64_t tile = n_tiles - 1 - wid / n_bkv;
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  const int64_t rows_total = n * g;
+  const int64_t rho0 = tile * kRouteRows;
+  f16x8 bq[2][NS];
+  const int eq = query_exponent(qmax[bkv]);
+  const float qsc = ldexpf(1.f, -eq);
+  {
+    const int64_t p0 = rho0 + 64 * wave + ln, p1 = p0 + 32;
+    const bool valid[2] = {p0 < rows_total, p1 < rows_total};
+    const int64_t rho_of[2] = {p0, p1};
+    load_q_tiles<false, D>(bq, Q, rho_of, valid, b, kv, g, hq, n, h, qsc);
+  }
+  const int r = 64 * wave + 32 * h + ln;
+  const int64_t my_rho = rho0 + r;
+  const bool my_valid = my_rho < rows_total;
+  const int64_t my_t = my_valid ? split_rho(my_rho, g).t : 0;
+  const int64_t my_C = my_valid ? min(nb, (my_t + 1) / B) : 0;
+  const int64_t t_max = min(n - 1, (rho0 + kRouteRows - 1) / g);
+  const int64_t C_wg = min(nb, (t_max + 1) / B);
+  const int64_t G_wg = (C_wg + m - 1) / m;
+  for (int64_t i = tid; i < G; i += kRouteThreads) hist[i] = 0;
+  const float nq2 = row_norm2<D>(bq, h);
+  const float qn = sqrtf(nq2);
+  float* my_ub = ub + (bkv * rows_total + (my_valid ? my_rho : 0)) * G;
+  float best_u = -__builtin_inff();
+  int best_g = 0;
+  const uint8_t* src = gimg + bkv * G * int64_t(BYTES);
+  if (G_wg > 0) stage_image<D>(src, lds, wave, lane, kRouteThreads / 64);
+  for (int64_t gi = 0; gi < G_wg; ++gi) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // image gi is in LDS; every wave is done with gi - 1's buffer
+    if (gi + 1 < G_wg)
+      stage_image<D>(src + (gi + 1) * BYTES, lds + ((gi + 1) & 1) * Lay::LDS_BYTES, wave, lane,
+                     kRouteThreads / 64);
+    // (an empty register constraint keeps the compiler from hoisting float32
+    // copies of the loop-invariant q fragments, which would not fit)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) asm volatile("" : "+v"(bq[nt][s2]));
+    float lin;   // the mean term <q, mu_G>, in the same (score) units
+    const float su = hilo_score<D>(lds + (gi & 1) * Lay::LDS_BYTES, bq, lane, &lin);
+    const float R = grl[(bkv * G + gi) * 2], lam = grl[(bkv * G + gi) * 2 + 1];
+    const float rad = qn * R * qsc, slack = 0.5f * beta * lam * nq2;
+    const float mag = fabsf(lin) + fabsf(su - lin) + rad + slack;
+    float u = su + rad + slack + kHierPrefillMargin * mag;
+    if (u != u) u = __builtin_inff();                   // non-finite inputs: never pruned
+    if (!my_valid || gi * m >= my_C) u = -__builtin_inff();
+    if (my_valid) my_ub[gi] = u;
+    if (u > best_u) {
+      best_u = u;
+      best_g = int(gi);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();   // hist cleared
+  if (my_valid) {
+    best[bkv * rows_total + my_rho] = best_g;
+    atomicAdd(&hist[best_g], 1);
+  }
+  __syncthreads();
+  const int64_t chunk = tile / kHierChunk, tc = tile % kHierChunk;
+  const int64_t n_chunks = hier_chunks(n_tiles);
+  for (int64_t i = tid; i < G; i += kRouteThreads)
+    gcnt[((bkv * n_chunks + chunk) * G + i) * kHierChunk + tc] = hist[i];
+}
+
+// Workgroup (tile, KV head): each row's place in the KV head's list of rows
+// by chunk and best group -- the offset of (its chunk, its group, its tile)
+// plus the rows of the tile before it with the same group.
+__global__ __launch_bounds__(kRouteThreads) void hier_order_kernel(
+    const int32_t* __restrict__ best, const int32_t* __restrict__ goff, int32_t* __restrict__ list,
+    int64_t rows_total, int64_t G, int64_t n_tiles) {
+  __shared__ int32_t tb[kRouteRows];
+  const int tid = threadIdx.x;
+  const int64_t bkv = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
+  const int64_t rho = tile * kRouteRows + tid;
+  const bool valid = rho < rows_total;
+  const int32_t bg = valid ? best[bkv * rows_total + rho] : -1;
+  tb[tid] = bg;
+  __syncthreads();
+  if (!valid) return;
+  int rank = 0;
+  for (int j = 0; j < tid; ++j) rank += tb[j] == bg ? 1 : 0;
+  const int64_t n_chunks = hier_chunks(n_tiles);
+  const int64_t gi = ((bkv * n_chunks + tile / kHierChunk) * G + bg) * kHierChunk + tile % kHierChunk;
+  list[bkv * rows_total + goff[gi] + rank] = int32_t(rho);
+}
+
+// Workgroup (listed tile, KV head): the visit.  Rows keep their top-k
+// sorted by (score descending, block ascending); blocks arrive in any order,
+// so the insert compares (score, block) pairs, a total order.
+template <int D, int KMAX>
+__global__ __launch_bounds__(kRouteThreads) void hier_visit_kernel(
+    const bf16_t* __restrict__ Q, const uint8_t* __restrict__ img,
+    const uint32_t* __restrict__ qmax, const float* __restrict__ ub,
+    const int32_t* __restrict__ list, int32_t* __restrict__ idx, int32_t* __restrict__ evaluated,
+    int64_t n, int g, int hq, int hkv, int B, int64_t nb, int m, int64_t G, int k,
+    int64_t n_tiles, int64_t n_bkv) {
+  using Lay = RouteLayout<D>;
+  constexpr int NS = D / 16, BYTES = Lay::BLOCK_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Lay::LDS_BYTES];
+  __shared__ uint64_t order[kHierSortMax];
+  __shared__ uint32_t gmax[kHierSortMax];
+  __shared__ int32_t cmax[kRouteThreads / 64];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int64_t wid = blockIdx.x;
+  const int64_t bkv = wid % n_bkv;
+  const int64_t tile = wid / n_bkv;
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  const int64_t rows_total = n * g;
+  const int64_t p0_tile = tile * kRouteRows;
+  const int32_t* lst = list + bkv * rows_total;
+  f16x8 bq[2][NS];
+  {
+    const float qsc = ldexpf(1.f, -query_exponent(qmax[bkv]));
+    const int64_t p0 = p0_tile + 64 * wave + ln, p1 = p0 + 32;
+    const bool valid[2] = {p0 < rows_total, p1 < rows_total};
+    const int64_t rho_of[2] = {valid[0] ? int64_t(lst[p0]) : 0, valid[1] ? int64_t(lst[p1]) : 0};
+    load_q_tiles<false, D>(bq, Q, rho_of, valid, b, kv, g, hq, n, h, qsc);
+  }
+  const int64_t my_p = p0_tile + 64 * wave + 32 * h + ln;
+  const bool my_valid = my_p < rows_total;
+  const int64_t my_rho = my_valid ? int64_t(lst[my_p]) : 0;
+  const int64_t my_t = my_valid ? split_rho(my_rho, g).t : 0;
+  const int64_t my_C = my_valid ? min(nb, (my_t + 1) / B) : 0;
+  const float* my_ub = ub + (bkv * rows_total + my_rho) * G;
+  // the tile's routable blocks (largest over its rows) and groups
+  {
+    int c = int(my_C);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c = max(c, __shfl_xor(c, o, 64));
+    if (lane == 0) cmax[wave] = c;
+  }
+  for (int i = tid; i < kHierSortMax; i += kRouteThreads) gmax[i] = 0u;
+  __syncthreads();
+  int64_t C_wg = 0;
+#pragma unroll
+  for (int w = 0; w < kRouteThreads / 64; ++w) C_wg = max(C_wg, int64_t(cmax[w]));
+  const int G_wg = int((C_wg + m - 1) / m);
+  // the tile's largest bound per group (order-preserving bits, LDS max)
+  // (a row's bounds exist for the groups with a block routable for it; the
+  // tile's other groups have nothing for the row)
+  auto bound = [&](int gi) {
+    return (my_valid && int64_t(gi) * m < my_C) ? my_ub[gi] : -__builtin_inff();
+  };
+  for (int gi = 0; gi < G_wg; ++gi) {
+    const float u = bound(gi);
+    const uint32_t bits = __float_as_uint(u);
+    uint32_t o = bits ^ (uint32_t(int32_t(bits) >> 31) | 0x80000000u);
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) o = max(o, uint32_t(__shfl_xor(int(o), sh, 64)));
+    if (lane == 0) atomicMax(&gmax[gi], o);
+  }
+  __syncthreads();
+  // groups in decreasing order of that bound (lower group first among equal
+  // bounds): a descending bitonic sort of (bound bits, ~group)
+  int P = 1;
+  while (P < G_wg) P <<= 1;
+  for (int i = tid; i < P; i += kRouteThreads)
+    order[i] = i < G_wg ? (uint64_t(gmax[i]) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(i)) : 0;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1)
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P; i += kRouteThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t a = order[i], c = order[j];
+          if (desc ? a < c : a > c) {
+            order[i] = c;
+            order[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+  float ls[KMAX];
+  int li[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    ls[i] = -__builtin_inff();
+    li[i] = 0x7FFFFFFF;
+  }
+  auto kth = [&]() {   // the running k-th score (+inf for k = 0: nothing is needed)
+    float t = k == 0 ? __builtin_inff() : -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (i == k - 1) t = ls[i];
+    return t;
+  };
+  int scored = 0;
+  const uint8_t* src = img + bkv * nb * int64_t(BYTES);
+  for (int j = 0; j < G_wg; ++j) {
+    const int gi = int(0xFFFFFFFFu - uint32_t(order[j] & 0xFFFFFFFFu));
+    const float u = bound(gi);
+    const bool need = __syncthreads_or(my_valid && !(u < kth()));
+    if (!need) continue;
+    const int64_t c0 = int64_t(gi) * m, c1 = min(C_wg, c0 + m);
+    stage_image<D>(src + c0 * BYTES, lds, wave, lane, kRouteThreads / 64);
+    for (int64_t c = c0; c < c1; ++c) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();   // image c is in LDS; every wave is done with c - 1's buffer
+      if (c + 1 < c1)
+        stage_image<D>(src + (c + 1) * BYTES, lds + ((c + 1 - c0) & 1) * Lay::LDS_BYTES, wave,
+                       lane, kRouteThreads / 64);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)   // (q stays in float16 registers; see hier_ub_kernel)
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) asm volatile("" : "+v"(bq[nt][s2]));
+      float sc = hilo_score<D>(lds + ((c - c0) & 1) * Lay::LDS_BYTES, bq, lane);
+      if (c >= my_C || !(sc > -__builtin_inff())) continue;   // not routable, -inf or NaN
+      int ci = int(c);
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        const bool gt = sc > ls[i] || (sc == ls[i] && ci < li[i]);
+        const float ts = ls[i];
+        const int ti = li[i];
+        ls[i] = gt ? sc : ts;
+        li[i] = gt ? ci : ti;
+        sc = gt ? ts : sc;
+        ci = gt ? ti : ci;
+      }
+    }
+    scored += int(c1 - c0);
+    __syncthreads();   // the last image's buffer is free before the next group stages
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (evaluated != nullptr && tid == 0) evaluated[bkv * n_tiles + tile] = scored;
+  if (!my_valid || k == 0) return;
+  const RowTJ rt = split_rho(my_rho, g);
+  int32_t* out = idx + ((b * hq + kv * g + rt.jg) * n + rt.t) * k;
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    if (i < k) {
+      const int ci = li[i] == 0x7FFFFFFF ? -1 : li[i];
+      const unsigned key_i = unsigned(ci);
+      int rank = 0;
+#pragma unroll
+      for (int j2 = 0; j2 < KMAX; ++j2)
+        if (j2 < k) {
+          const unsigned key_j = unsigned(li[j2] == 0x7FFFFFFF ? -1 : li[j2]);
+          rank += (key_j < key_i || (key_j == key_i && j2 < i)) ? 1 : 0;
+        }
+      out[rank] = ci;
+    }
+  }
+}
+
+template <int D, int KMAX>
+hipError_t launch_hier_prefill_t(const Shape& s, const void* Q, const float* mu,
+                                 const float* sigma, const float* gmu, const float* gS,
+                                 const float* grl, int m, int32_t* idx, int32_t* evaluated,
+                                 void* ws, hipStream_t st) {
+  const int64_t n_bkv = int64_t(s.b) * s.hkv;
+  const int64_t n_tiles = route_tiles(s);
+  const int64_t rows_total = s.n * s.g;
+  const int64_t G = hier_groups(s, m);
+  const HierWs w = hier_ws_layout(s, m, ws);
+  const unsigned grid = unsigned(n_tiles * n_bkv);
+  if (s.nb == 0) {
+    // no complete block: every row gets -1 padding; no tile scores anything
+    if (s.k > 0)
+      hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((n_bkv * rows_total * s.k + 255) / 256, 1024))),
+                         dim3(256), 0, st, idx, int64_t(s.b) * s.hq * s.n * s.k, -1);
+    if (evaluated != nullptr)
+      hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((grid + 255) / 256, 1024))),
+                         dim3(256), 0, st, evaluated, int64_t(grid), 0);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<int32_t*>(w.qmax),
+                     5 * n_bkv, 0);
+  // counts of the last chunk's missing tiles stay zero
+  const int64_t n_cnt = n_bkv * G * hier_chunks(n_tiles) * kHierChunk;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((n_cnt + 255) / 256, 1024))),
+                     dim3(256), 0, st, w.gcnt, n_cnt, 0);
+  const int64_t per_group = int64_t(s.g) * s.n * D;
+  const unsigned gx = unsigned(std::min<int64_t>((per_group / 8 + 255) / 256, 256));
+  hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(Q), w.qmax, per_group);
+  hipLaunchKernelGGL((route_prep_kernel<false, D>), dim3(unsigned(s.nb), unsigned(n_bkv)),
+                     dim3(256), 0, st, mu, sigma, w.qmax, w.qmax + n_bkv, w.dbar, w.img, s.nb,
+                     s.beta, sigma, s.nb);
+  hipLaunchKernelGGL((route_prep_kernel<false, D>), dim3(unsigned(G), unsigned(n_bkv)),
+                     dim3(256), 0, st, gmu, gS, w.qmax, w.gbounds, w.gdbar, w.gimg, G, s.beta,
+                     sigma, s.nb);
+  hipLaunchKernelGGL((hier_ub_kernel<D>), dim3(grid), dim3(kRouteThreads), 0, st,
+                     static_cast<const bf16_t*>(Q), w.gimg, grl, w.qmax, w.ub, w.best, w.gcnt,
+                     s.n, s.g, s.hq, s.hkv, s.B, s.nb, m, G, n_tiles, n_bkv, s.beta);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(unsigned(n_bkv)), dim3(1024), 0, st, w.gcnt, w.goff,
+                     w.gtot, G * hier_chunks(n_tiles) * kHierChunk);
+  hipLaunchKernelGGL(hier_order_kernel, dim3(grid), dim3(kRouteThreads), 0, st, w.best, w.goff,
+                     w.list, rows_total, G, n_tiles);
+  hipLaunchKernelGGL((hier_visit_kernel<D, KMAX>), dim3(grid), dim3(kRouteThreads), 0, st,
+                     static_cast<const bf16_t*>(Q), w.img, w.qmax, w.ub, w.list, idx, evaluated,
+                     s.n, s.g, s.hq, s.hkv, s.B, s.nb, m, G, s.k, n_tiles, n_bkv);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_hier_prefill_d(const Shape& s, const void* Q, const float* mu,
+                                 const float* sigma, const float* gmu, const float* gS,
+                                 const float* grl, int m, int32_t* idx, int32_t* evaluated,
+                                 void* ws, hipStream_t st) {
+  if (s.k <= 8)
+    return launch_hier_prefill_t<D, 8>(s, Q, mu, sigma, gmu, gS, grl, m, idx, evaluated, ws, st);
+  if (s.k <= 16)
+    return launch_hier_prefill_t<D, 16>(s, Q, mu, sigma, gmu, gS, grl, m, idx, evaluated, ws, st);
+  return launch_hier_prefill_t<D, 32>(s, Q, mu, sigma, gmu, gS, grl, m, idx, evaluated, ws, st);
+}
+
 }  // namespace
 
 size_t route_workspace_bytes(const Shape& s) { return route_ws_layout(s, nullptr).bytes; }
@@ -1508,6 +2041,20 @@ hipError_t launch_route_topk(const Shape& s, const void* Q, const float* mu, con
                      : launch_route_d<false, 128>(s, Q, mu, sigma, idx, kth, ws, st);
   return s.d == 64 ? launch_route_d<true, 64>(s, Q, mu, sigma, idx, kth, ws, st)
                    : launch_route_d<true, 128>(s, Q, mu, sigma, idx, kth, ws, st);
+}
+
+size_t route_hier_prefill_workspace_bytes(const Shape& s, int m) {
+  return hier_ws_layout(s, m, nullptr).bytes;
+}
+int hier_prefill_max_groups() { return kHierSortMax; }
+int64_t route_tile_count(const Shape& s) { return route_tiles(s); }
+
+hipError_t launch_route_hier_prefill(const Shape& s, const void* Q, const float* mu,
+                                     const float* sigma, const float* gmu, const float* gS,
+                                     const float* grl, int m, int32_t* idx, int32_t* evaluated,
+                                     void* ws, hipStream_t st) {
+  return s.d == 64 ? launch_hier_prefill_d<64>(s, Q, mu, sigma, gmu, gS, grl, m, idx, evaluated, ws, st)
+                   : launch_hier_prefill_d<128>(s, Q, mu, sigma, gmu, gS, grl, m, idx, evaluated, ws, st);
 }
 
 }  // namespace ssa

@@ -275,6 +275,67 @@ ssa_status ssa_route_hier(const ssa_params* p, const void* q, const float* mu, c
                   "ssa_route_hier");
 }
 
+namespace {
+
+ssa_status check_hier_prefill(const ssa_params* p, int32_t group_blocks, ssa::Shape* s) {
+  ssa_status st = check_params(p, s);
+  if (st != SSA_OK) return st;
+  if (!(p->beta >= 0.f))
+    return fail(SSA_ERR_INVALID_ARGUMENT, "the group bound needs beta >= 0");
+  if (group_blocks < 1 || group_blocks > ssa::hier_max_group())
+    return fail(SSA_ERR_INVALID_ARGUMENT, "group_blocks %d out of [1, %d]", group_blocks,
+                ssa::hier_max_group());
+  if (!s->in_bf16)
+    return fail(SSA_ERR_UNSUPPORTED, "hierarchical prefill routing is built for bfloat16 inputs");
+  const int64_t G = (s->nb + group_blocks - 1) / group_blocks;
+  if (G > ssa::hier_prefill_max_groups())
+    return fail(SSA_ERR_UNSUPPORTED, "%lld groups per sequence exceed %d", (long long)G,
+                ssa::hier_prefill_max_groups());
+  if (int64_t(s->b) * s->hkv * ssa::route_tile_count(*s) >= (int64_t(1) << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "too many 512-row tiles for one launch");
+  if (int64_t(s->b) * s->hkv > 65535)
+    return fail(SSA_ERR_UNSUPPORTED, "more than 65535 (sequence, KV head) pairs");
+  return SSA_OK;
+}
+
+}  // namespace
+
+ssa_status ssa_route_hier_prefill_workspace_size(const ssa_params* p, int32_t group_blocks,
+                                                 size_t* bytes) {
+  ssa::Shape s;
+  ssa_status st = check_hier_prefill(p, group_blocks, &s);
+  if (st != SSA_OK) return st;
+  SSA_NONNULL(bytes);
+  *bytes = ssa::route_hier_prefill_workspace_bytes(s, group_blocks);
+  return ok();
+}
+
+ssa_status ssa_route_hier_prefill(const ssa_params* p, const void* Q, const float* mu,
+                                  const float* sigma, const float* gmu, const float* gsigma,
+                                  const float* grl, int32_t group_blocks, int32_t* idx,
+                                  int32_t* evaluated, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  ssa::Shape s;
+  ssa_status st = check_hier_prefill(p, group_blocks, &s);
+  if (st != SSA_OK) return st;
+  SSA_NONNULL(Q);
+  if (s.k > 0) SSA_NONNULL(idx);
+  if (s.nb > 0) {
+    SSA_NONNULL(mu);
+    SSA_NONNULL(sigma);
+    SSA_NONNULL(gmu);
+    SSA_NONNULL(gsigma);
+    SSA_NONNULL(grl);
+  }
+  if (s.k == 0 && evaluated == nullptr) return ok();
+  st = check_ws(ssa::route_hier_prefill_workspace_bytes(s, group_blocks), workspace,
+                workspace_bytes);
+  if (st != SSA_OK) return st;
+  return from_hip(ssa::launch_route_hier_prefill(s, Q, mu, sigma, gmu, gsigma, grl, group_blocks,
+                                                 idx, evaluated, workspace, (hipStream_t)stream),
+                  "ssa_route_hier_prefill");
+}
+
 ssa_status ssa_workspace_size(const ssa_params* p, int32_t op, size_t* bytes) {
   ssa::Shape s;
   ssa_status st = check_params(p, &s);

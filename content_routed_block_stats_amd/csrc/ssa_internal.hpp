@@ -99,6 +99,17 @@ hipError_t launch_route_hier(const Shape& s, const void* q, const float* mu, con
                              const int32_t* pos, int32_t* idx, int32_t* evaluated, void* ws,
                              hipStream_t st);
 
+// exact hierarchical routing of prefill rows (bfloat16 inputs): group bounds
+// per 512-row tile of a KV head's rows, then a visit per tile;
+// evaluated [b*hkv][route_tile_count] blocks scored per tile (or nullptr)
+size_t route_hier_prefill_workspace_bytes(const Shape& s, int m);
+int hier_prefill_max_groups();
+int64_t route_tile_count(const Shape& s);
+hipError_t launch_route_hier_prefill(const Shape& s, const void* Q, const float* mu,
+                                     const float* sigma, const float* gmu, const float* gS,
+                                     const float* grl, int m, int32_t* idx, int32_t* evaluated,
+                                     void* ws, hipStream_t st);
+
 // decode step
 size_t decode_workspace_bytes(const Shape& s);
 // the allocation-free variant's scratch: a device array of this many bytes,

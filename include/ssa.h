@@ -271,6 +271,42 @@ ssa_status ssa_route_hier(const ssa_params* p, const void* q, const float* mu, c
                           int32_t* evaluated, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Exact hierarchical routing of prefill query rows (write-up, module table:
+ * branch-and-bound exact selection under an admissible bound and a tree
+ * router; opening paragraph: near-linear cost with a hierarchical router).
+ * Returns the selection ssa_route_topk defines (ties to the lower block),
+ * scoring only the groups of group_blocks consecutive blocks whose bound
+ *   UB_G(q) = r_G(q) + ||q|| R_G + (beta/2) lam_G ||q||^2
+ * (r_G: the routing score of the group's mean centroid and mean covariance;
+ * R_G, lam_G: radius and covariance slack, all from ssa_group_stats) reaches
+ * some row's running k-th score.  The rows rho = t (Hq/Hkv) + j of one
+ * (sequence, KV head) (rho < n Hq/Hkv) are listed chunk by chunk (8192
+ * consecutive rows each), within a chunk by the group of their largest bound
+ * (ties: lower group; then row order), and taken in tiles of 512 consecutive
+ * list entries; a tile visits its groups in decreasing order
+ * of their largest bound over its rows and scores a group's blocks against
+ * all its rows unless, for every row, the group's bound (with a relative
+ * margin of 1e-4 over float32 rounding) is strictly below the row's running
+ * k-th score.
+ *   Q          [b, Hq, n, d] bfloat16
+ *   mu, sigma  as ssa_block_stats writes them for K [b, Hkv, n, d]
+ *   gmu, gsigma, grl  ssa_group_stats of mu/sigma with the same group_blocks
+ *   idx        [b, Hq, n, k] int32, written as ssa_route_topk writes it
+ *   evaluated  [b, Hkv, ceil(n (Hq/Hkv) / 512)] int32, written if not NULL:
+ *              blocks each listed tile scored (against all of its rows)
+ *   workspace  >= ssa_route_hier_prefill_workspace_size(p, group_blocks, .)
+ *              bytes, 256-byte aligned (it grows with the number of groups)
+ * Limits: group_blocks in [1, 64] and beta >= 0 (SSA_ERR_INVALID_ARGUMENT);
+ * bfloat16 inputs, at most 4096 groups per sequence, b * Hkv <= 65535 and
+ * b * Hkv * ceil(n (Hq/Hkv) / 512) < 2^31 (SSA_ERR_UNSUPPORTED). */
+ssa_status ssa_route_hier_prefill_workspace_size(const ssa_params* p, int32_t group_blocks,
+                                                 size_t* bytes);
+ssa_status ssa_route_hier_prefill(const ssa_params* p, const void* Q, const float* mu,
+                                  const float* sigma, const float* gmu, const float* gsigma,
+                                  const float* grl, int32_t group_blocks, int32_t* idx,
+                                  int32_t* evaluated, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* One decode step per sequence (write-up, module table: the decode path routes
  * and attends one new query per step against the cache).  With
  * L = cache_len[b] tokens already cached, for every sequence b:

@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import content_routed_block_stats_amd as ssa
 from content_routed_block_stats_amd import binding as B
@@ -214,3 +215,39 @@ def test_peak_probes_check_arguments_on_host():
     assert lib.ssa_probe_hbm_read(ctypes.c_void_p(4100), 1024, dummy, 8, None) == \
         B.SSA_ERR_INVALID_ARGUMENT
     assert lib.ssa_probe_hbm_read(dummy, 1024, dummy, 0, None) == B.SSA_ERR_INVALID_ARGUMENT
+
+
+def test_hier_prefill_checked_on_host():
+    L = ssa.lib()
+    p = _p(in_dtype=torch.bfloat16)
+    need = B.ssa_route_hier_prefill_workspace_size(p, 8)
+    assert need > B.ssa_route_hier_prefill_workspace_size(p, 64) > 0   # more groups, more bounds
+    # Q, mu, sigma, gmu, gsigma, grl, group_blocks, idx, evaluated, workspace
+    good = [256, 256, 256, 256, 256, 256, 8, 256, None, 256]
+    for i in (0, 1, 2, 3, 4, 5, 7, 9):
+        args = list(good)
+        args[i] = None
+        got = L.ssa_route_hier_prefill(ctypes.byref(p), *args, need, None)
+        assert got == B.SSA_ERR_INVALID_ARGUMENT, (i, B.status_string(got))
+    assert L.ssa_route_hier_prefill(ctypes.byref(p), *good, need - 1, None) == \
+        B.SSA_ERR_WORKSPACE_TOO_SMALL
+    for m in (0, 65):
+        args = list(good)
+        args[6] = m
+        assert L.ssa_route_hier_prefill(ctypes.byref(p), *args, need, None) == \
+            B.SSA_ERR_INVALID_ARGUMENT
+    pb = _p(in_dtype=torch.bfloat16)
+    pb.beta = -1.0
+    assert L.ssa_route_hier_prefill(ctypes.byref(pb), *good, need, None) == \
+        B.SSA_ERR_INVALID_ARGUMENT
+    pf = _p(in_dtype=torch.float32)
+    assert L.ssa_route_hier_prefill(ctypes.byref(pf), *good, need, None) == B.SSA_ERR_UNSUPPORTED
+    # more than 4096 groups: 2^20 tokens / B 64 = 16384 blocks, m = 2
+    pg = _p(in_dtype=torch.bfloat16, seq_len=1 << 20, block_size=64)
+    n = ctypes.c_size_t(0)
+    assert L.ssa_route_hier_prefill_workspace_size(ctypes.byref(pg), 2, ctypes.byref(n)) == \
+        B.SSA_ERR_UNSUPPORTED
+    # nothing requested (k = 0, no counts): returns before any launch
+    p0 = _p(in_dtype=torch.bfloat16, top_k=0)
+    assert L.ssa_route_hier_prefill(ctypes.byref(p0), 256, 256, 256, 256, 256, 256, 8, None, None,
+                                    None, 0, None) == B.SSA_OK
