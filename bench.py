@@ -70,6 +70,14 @@ def gather_bytes(wl) -> float:
     return float(sel * per_sel + rows * per_row + kv)
 
 
+def stats_bytes(wl) -> float:
+    """Algorithmic HBM bytes of ssa_block_stats: K read once, mu and Sigma written."""
+    e = 2 if wl.dtype == "bf16" else 4
+    nb = wl.seq_len // wl.block
+    heads = wl.batch * wl.n_kv_heads
+    return float(heads * (wl.seq_len * wl.head_dim * e + nb * (wl.head_dim + wl.head_dim ** 2) * 4))
+
+
 def compulsory_gather_bytes(wl) -> float:
     """Bytes ssa_sparse_attn_fwd cannot avoid: Q, K and V read once, idx read
     once, O and LSE written once."""
@@ -324,6 +332,9 @@ def bench_decode(steps: int, warmup: int) -> dict:
             "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
             "hbm_gbs_algorithmic": round((sig + gat) / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round((sig + gat) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": float(sig + gat),
+            "traffic": counted_traffic("decode_step", kernel_source_digest("decode.hip",
+                                                                           "ssa_common.hpp")),
             "steps": steps,
             "hier_route": {"group_blocks": m, "ms": round(hier_ms, 4),
                            "group_stats_ms_once": round(gs_ms, 3),
@@ -432,6 +443,79 @@ def recall_sweep(wl, seed: int, betas: list[float]) -> dict:
             "rows": rows}
 
 
+def hier_prefill_study(wl, m: int, reps: int, seed: int) -> dict:
+    """Exact hierarchical routing of the prefill rows (ssa_group_stats +
+    ssa_route_hier_prefill, groups of m blocks) beside the flat router
+    (ssa_route_topk) on the same inputs, for the standard keys and for
+    clustered keys (tight blocks around well separated group centres):
+    median times, the (row, block) scores the visit computed (each listed
+    tile's blocks times its 512 rows) over the routable pairs, and whether the
+    selections agree."""
+    import statistics
+
+    import torch
+
+    import content_routed_block_stats_amd as ssa
+    from synth_inputs import make_prefill
+
+    def timed(fn):
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return statistics.median(out)
+
+    rows = []
+    for keys, w in (("standard", wl),
+                    ("clustered", wl.replace(center_std=0.05, noise_std=0.05, group_std=1.0,
+                                             group_blocks=m))):
+        data = make_prefill(w, seed=seed, device="cuda")
+        Q, K = data["Q"], data["K"]
+        del data["V"]
+        mu, sigma = ssa.ssa_block_stats(K, w.block)
+        b, hq, n, d = Q.shape
+        hkv, nb = mu.shape[1], mu.shape[2]
+        idx_f = torch.empty((b, hq, n, w.top_k), dtype=torch.int32, device="cuda")
+        idx_h = torch.empty_like(idx_f)
+        p = ssa.make_params(batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, seq_len=n,
+                            block_size=w.block, top_k=w.top_k, beta=w.beta, in_dtype=Q.dtype)
+        ws_f = torch.empty(ssa.ssa_workspace_size(p, 1), dtype=torch.uint8, device="cuda")
+        ws_h = torch.empty(ssa.ssa_route_hier_prefill_workspace_size(p, m), dtype=torch.uint8,
+                           device="cuda")
+        flat = lambda: ssa.ssa_route_topk(Q, mu, sigma, block_size=w.block, top_k=w.top_k,
+                                          beta=w.beta, idx=idx_f, workspace=ws_f)
+        gs = ssa.ssa_group_stats(mu, sigma, block_size=w.block, group_blocks=m)
+        hier = lambda: ssa.ssa_route_hier_prefill(Q, mu, sigma, *gs, block_size=w.block,
+                                                  group_blocks=m, top_k=w.top_k, beta=w.beta,
+                                                  idx=idx_h, workspace=ws_h)
+        flat()
+        _, ev = ssa.ssa_route_hier_prefill(Q, mu, sigma, *gs, block_size=w.block, group_blocks=m,
+                                           top_k=w.top_k, beta=w.beta, idx=idx_h,
+                                           want_evaluated=True, workspace=ws_h)
+        torch.cuda.synchronize()
+        t_flat = timed(flat)
+        t_gs = timed(lambda: ssa.ssa_group_stats(mu, sigma, block_size=w.block, group_blocks=m))
+        t_hier = timed(hier)
+        g = hq // hkv
+        nbk = n // w.block
+        # (row, block) pairs routable: sum over positions of min(nb, (t+1)/B), per q-head
+        full = max(0, n - nbk * w.block + 1)
+        pairs = (w.block * nbk * (nbk - 1) // 2 + full * nbk) * g * b * hkv
+        agree = float((idx_f == idx_h).all(-1).float().mean())
+        rows.append({"keys": keys, "flat_route_ms": round(t_flat, 3),
+                     "group_stats_ms": round(t_gs, 3), "hier_route_ms": round(t_hier, 3),
+                     "pairs_scored_frac": round(float(ev.long().sum()) * 512 / max(1, pairs), 4),
+                     "rows_equal_to_flat": round(agree, 6)})
+        del Q, K, mu, sigma, idx_f, idx_h, ws_f, ws_h, gs, ev, data
+        torch.cuda.empty_cache()
+    return {"study": "exact hierarchical prefill routing vs the flat router",
+            "workload": wl.name, "group_blocks": m, "reps": reps, "rows": rows}
+
+
 def onbox_peaks() -> dict:
     """The card's own ceilings: the dense bf16 MFMA loop and a streaming read
     of 4 GiB (larger than every cache), medians of 5 timed launches each."""
@@ -458,7 +542,7 @@ def onbox_peaks() -> dict:
     flops = ssa.ssa_probe_mfma_bf16(wgs, 1)[1] * iters
     ms_m = timed(lambda: ssa.ssa_probe_mfma_bf16(wgs, iters))
     buf = torch.ones(1 << 30, dtype=torch.int32, device="cuda")     # 4 GiB
-    rwgs = 4096
+    rwgs = 8192
     out = torch.empty(rwgs * 256, dtype=torch.int32, device="cuda")
     ms_r = timed(lambda: ssa.ssa_probe_hbm_read(buf, rwgs, out))
     nbytes = buf.numel() * 4
@@ -467,7 +551,8 @@ def onbox_peaks() -> dict:
             "hbm_read_gbs": round(nbytes / (ms_r * 1e-3) / 1e9, 1),
             "how": (f"ssa_probe_mfma_bf16: {wgs} workgroups x 4 waves x {iters} x 16 "
                     "v_mfma_f32_32x32x16_bf16 on 4 chains; ssa_probe_hbm_read: 4 GiB, "
-                    f"{rwgs} workgroups x 256 threads x 16 B loads; medians of 5 launches")}
+                    f"{rwgs} workgroups x 256 threads x 8 nontemporal 16 B loads in flight; "
+                    "medians of 5 launches")}
 
 
 def main() -> int:
@@ -480,8 +565,13 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the prefill step (no tile-shared, backward or tempered sections)")
     ap.add_argument("--recall-sweep", action="store_true",
                     help="only print the planted-recall-vs-beta study for --workload")
+    ap.add_argument("--hier-prefill", action="store_true",
+                    help="only the hierarchical-vs-flat prefill routing study for --workload")
+    ap.add_argument("--group-blocks", type=int, default=16)
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the on-card bf16 MFMA and HBM read ceilings")
     ap.add_argument("--no-flush", action="store_true",
@@ -520,6 +610,10 @@ def main() -> int:
     if wl.decode:
         print("choose a prefill workload", file=sys.stderr)
         return 2
+    if args.hier_prefill:
+        print(json.dumps(hier_prefill_study(wl, args.group_blocks, max(3, args.steps // 2),
+                                            args.seed)), flush=True)
+        return 0
     if args.recall_sweep:
         betas = [0.0, 0.25, 0.5, 1.0, 2.0, 4.0, 8.0, 16.0, 32.0]
         print(json.dumps(recall_sweep(wl, args.seed, betas)), flush=True)
@@ -647,109 +741,115 @@ def main() -> int:
                                                       "pair as a per-row gather would read them, "
                                                       "over the stage time")},
         "onbox_peaks": peaks,
+        "block_stats": {"kernel": "block_stats", "bound": "alu", "ms": round(t_stats, 4),
+                        "algorithmic_bytes_per_launch": stats_bytes(wl),
+                        "gbs": round(stats_bytes(wl) / (t_stats * 1e-3) / 1e9, 1),
+                        "traffic": counted_traffic("block_stats", kernel_source_digest(
+                            "block_stats.hip", "ssa_common.hpp"))},
     }
-    # the query-tile-shared variant: one selection per tile of B positions
-    tiles = (n + wl.block - 1) // wl.block
-    idx_t = torch.empty((b, hq, tiles, wl.top_k), dtype=torch.int32, device=dev)
-    ws_rt = torch.empty(ssa.ssa_workspace_size(p, 4), dtype=torch.uint8, device=dev)
-    ws_ta = torch.empty(ssa.ssa_workspace_size(p, 5), dtype=torch.uint8, device=dev)
+    if not args.step_only:
+        # the query-tile-shared variant: one selection per tile of B positions
+        tiles = (n + wl.block - 1) // wl.block
+        idx_t = torch.empty((b, hq, tiles, wl.top_k), dtype=torch.int32, device=dev)
+        ws_rt = torch.empty(ssa.ssa_workspace_size(p, 4), dtype=torch.uint8, device=dev)
+        ws_ta = torch.empty(ssa.ssa_workspace_size(p, 5), dtype=torch.uint8, device=dev)
 
-    def tile_step(ev=None):
-        if ev:
-            ev[0].record()
-        ssa.ssa_block_stats(K, wl.block, mu=mu, sigma=sigma)
-        if ev:
-            ev[1].record()
-        ssa.ssa_route_tiles(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta,
-                            idx=idx_t, workspace=ws_rt)
-        if ev:
-            ev[2].record()
-        ssa.ssa_tile_attn_fwd(Q, K, V, idx_t, block_size=wl.block, window=wl.window,
-                              scale=wl.scale, out=O, lse=lse, workspace=ws_ta)
-        if ev:
-            ev[3].record()
+        def tile_step(ev=None):
+            if ev:
+                ev[0].record()
+            ssa.ssa_block_stats(K, wl.block, mu=mu, sigma=sigma)
+            if ev:
+                ev[1].record()
+            ssa.ssa_route_tiles(Q, mu, sigma, block_size=wl.block, top_k=wl.top_k, beta=wl.beta,
+                                idx=idx_t, workspace=ws_rt)
+            if ev:
+                ev[2].record()
+            ssa.ssa_tile_attn_fwd(Q, K, V, idx_t, block_size=wl.block, window=wl.window,
+                                  scale=wl.scale, out=O, lse=lse, workspace=ws_ta)
+            if ev:
+                ev[3].record()
 
-    tile_step()
-    torch.cuda.synchronize()
-    treps = max(3, args.steps // 2)
-    tevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(treps)]
-    for i in range(treps):
-        tile_step(tevs[i])
-    torch.cuda.synchronize()
-    tst = [sum(e[j].elapsed_time(e[j + 1]) for e in tevs) / treps for j in range(3)]
-    t_tile = sum(tst)
-    ta_fl = tile_attn_flops(wl, idx_t)
-    ta_tf = ta_fl / (tst[2] * 1e-3) / 1e12
-    plants = data["plants"]
-    pb = torch.tensor([q["b"] for q in plants], device=dev)
-    ph = torch.tensor([q["h"] for q in plants], device=dev)
-    pt = torch.tensor([q["t"] for q in plants], device=dev)
-    pc = torch.tensor([q["block"] for q in plants], device=dev, dtype=torch.int32)
-    rec_tile = float((idx_t[pb, ph, pt // wl.block] == pc[:, None]).any(-1).float().mean())
-    rec_row = float((idx[pb, ph, pt] == pc[:, None]).any(-1).float().mean())
-    res["tile_routed"] = {
-        "what": "one selection per query tile of B positions (summed routing score), same workload",
-        "ms_per_step": round(t_tile, 4), "value": round(tokens / (t_tile * 1e-3), 1),
-        "unit": "query-tokens/s", "speedup_vs_per_query": round(ms / t_tile, 3),
-        "stages_ms": {"block_stats": round(tst[0], 4), "route_tiles": round(tst[1], 4),
-                      "tile_attn_fwd": round(tst[2], 4)},
-        "planted_recall": round(rec_tile, 4), "planted_recall_per_query": round(rec_row, 4),
-        "roofline": {"kernel": "tile_attn", "bound": "mfma", "achieved": round(ta_tf, 1),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ta_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": counted_traffic("tile_attn", kernel_source_digest(
-                         "tile_attn.hip", "kv_chunks.hpp", "ssa_common.hpp")),
-                     "algorithmic_flops_per_launch": ta_fl},
-        "steps": treps}
-    del ws_rt, ws_ta, idx_t
+        tile_step()
+        torch.cuda.synchronize()
+        treps = max(3, args.steps // 2)
+        tevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(treps)]
+        for i in range(treps):
+            tile_step(tevs[i])
+        torch.cuda.synchronize()
+        tst = [sum(e[j].elapsed_time(e[j + 1]) for e in tevs) / treps for j in range(3)]
+        t_tile = sum(tst)
+        ta_fl = tile_attn_flops(wl, idx_t)
+        ta_tf = ta_fl / (tst[2] * 1e-3) / 1e12
+        plants = data["plants"]
+        pb = torch.tensor([q["b"] for q in plants], device=dev)
+        ph = torch.tensor([q["h"] for q in plants], device=dev)
+        pt = torch.tensor([q["t"] for q in plants], device=dev)
+        pc = torch.tensor([q["block"] for q in plants], device=dev, dtype=torch.int32)
+        rec_tile = float((idx_t[pb, ph, pt // wl.block] == pc[:, None]).any(-1).float().mean())
+        rec_row = float((idx[pb, ph, pt] == pc[:, None]).any(-1).float().mean())
+        res["tile_routed"] = {
+            "what": "one selection per query tile of B positions (summed routing score), same workload",
+            "ms_per_step": round(t_tile, 4), "value": round(tokens / (t_tile * 1e-3), 1),
+            "unit": "query-tokens/s", "speedup_vs_per_query": round(ms / t_tile, 3),
+            "stages_ms": {"block_stats": round(tst[0], 4), "route_tiles": round(tst[1], 4),
+                          "tile_attn_fwd": round(tst[2], 4)},
+            "planted_recall": round(rec_tile, 4), "planted_recall_per_query": round(rec_row, 4),
+            "roofline": {"kernel": "tile_attn", "bound": "mfma", "achieved": round(ta_tf, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ta_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": counted_traffic("tile_attn", kernel_source_digest(
+                             "tile_attn.hip", "kv_chunks.hpp", "ssa_common.hpp")),
+                         "algorithmic_flops_per_launch": ta_fl},
+            "steps": treps}
+        del ws_rt, ws_ta, idx_t
 
-    # the backward through the attention with the step's selections (training);
-    # the tile-shared step above overwrote O and lse, so the forward runs again
-    ssa.ssa_sparse_attn_fwd(Q, K, V, idx, block_size=wl.block, window=wl.window, scale=wl.scale,
-                            out=O, lse=lse, workspace=ws_a)
-    dO = torch.randn(Q.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
-                     dtype=torch.float32).to(Q.dtype)
-    ws_b = torch.empty(ssa.ssa_workspace_size(p, 6), dtype=torch.uint8, device=dev)
-    bwd = lambda: ssa.ssa_sparse_attn_bwd(Q, K, V, idx, O, lse, dO, block_size=wl.block,
-                                          window=wl.window, scale=wl.scale, workspace=ws_b)
-    bwd()
-    torch.cuda.synchronize()
-    tb0, tb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    breps = 2
-    tb0.record()
-    for _ in range(breps):
+        # the backward through the attention with the step's selections (training);
+        # the tile-shared step above overwrote O and lse, so the forward runs again
+        ssa.ssa_sparse_attn_fwd(Q, K, V, idx, block_size=wl.block, window=wl.window, scale=wl.scale,
+                                out=O, lse=lse, workspace=ws_a)
+        dO = torch.randn(Q.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
+                         dtype=torch.float32).to(Q.dtype)
+        ws_b = torch.empty(ssa.ssa_workspace_size(p, 6), dtype=torch.uint8, device=dev)
+        bwd = lambda: ssa.ssa_sparse_attn_bwd(Q, K, V, idx, O, lse, dO, block_size=wl.block,
+                                              window=wl.window, scale=wl.scale, workspace=ws_b)
         bwd()
-    tb1.record()
-    torch.cuda.synchronize()
-    t_bwd = tb0.elapsed_time(tb1) / breps
-    bwd_fl = 14.0 * wl.head_dim * pairs
-    res["backward"] = {"what": "dQ, dK, dV through the attention over the step's selections",
-                       "ms": round(t_bwd, 3), "ms_vs_forward_attention": round(t_bwd / t_attn, 2),
-                       "bound": "mfma", "achieved": round(bwd_fl / (t_bwd * 1e-3) / 1e12, 1),
-                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                       "frac": round(bwd_fl / (t_bwd * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                       "algorithmic_flops_per_launch": bwd_fl, "reps": breps,
-                       "traffic_dkv_kernel": counted_traffic("attn_bwd_dkv", kernel_source_digest(
-                           "attn_bwd.hip", "kv_chunks.hpp", "ssa_common.hpp"))}
-    del ws_b, dO
+        torch.cuda.synchronize()
+        tb0, tb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        breps = 2
+        tb0.record()
+        for _ in range(breps):
+            bwd()
+        tb1.record()
+        torch.cuda.synchronize()
+        t_bwd = tb0.elapsed_time(tb1) / breps
+        bwd_fl = 14.0 * wl.head_dim * pairs
+        res["backward"] = {"what": "dQ, dK, dV through the attention over the step's selections",
+                           "ms": round(t_bwd, 3), "ms_vs_forward_attention": round(t_bwd / t_attn, 2),
+                           "bound": "mfma", "achieved": round(bwd_fl / (t_bwd * 1e-3) / 1e12, 1),
+                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(bwd_fl / (t_bwd * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "algorithmic_flops_per_launch": bwd_fl, "reps": breps,
+                           "traffic_dkv_kernel": counted_traffic("attn_bwd_dkv", kernel_source_digest(
+                               "attn_bwd.hip", "kv_chunks.hpp", "ssa_common.hpp"))}
+        del ws_b, dO
 
-    # the exact tempered score (same workload and beta), outside the step
-    ssa.ssa_route_tempered(Q, K, block_size=wl.block, top_k=wl.top_k, beta=wl.beta, idx=idx)
-    te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
-    te0.record()
-    for _ in range(reps):
+        # the exact tempered score (same workload and beta), outside the step
         ssa.ssa_route_tempered(Q, K, block_size=wl.block, top_k=wl.top_k, beta=wl.beta, idx=idx)
-    te1.record()
-    torch.cuda.synchronize()
-    t_temp = te0.elapsed_time(te1) / reps
-    tf = tempered_flops(wl) / (t_temp * 1e-3) / 1e12
-    res["tempered_route"] = {"kernel": "tempered_route", "ms": round(t_temp, 3), "bound": "mfma",
-                             "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": counted_traffic("tempered_route", kernel_source_digest(
-                                 "tempered_route.hip", "kv_chunks.hpp", "ssa_common.hpp")),
-                             "algorithmic_flops_per_launch": tempered_flops(wl), "reps": reps}
+        te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        te0.record()
+        for _ in range(reps):
+            ssa.ssa_route_tempered(Q, K, block_size=wl.block, top_k=wl.top_k, beta=wl.beta, idx=idx)
+        te1.record()
+        torch.cuda.synchronize()
+        t_temp = te0.elapsed_time(te1) / reps
+        tf = tempered_flops(wl) / (t_temp * 1e-3) / 1e12
+        res["tempered_route"] = {"kernel": "tempered_route", "ms": round(t_temp, 3), "bound": "mfma",
+                                 "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                 "traffic": counted_traffic("tempered_route", kernel_source_digest(
+                                     "tempered_route.hip", "kv_chunks.hpp", "ssa_common.hpp")),
+                                 "algorithmic_flops_per_launch": tempered_flops(wl), "reps": reps}
     del O, lse, ws_a, ws_r
     if not args.no_decode:
         print("[bench] decode step", file=sys.stderr, flush=True)

@@ -37,18 +37,27 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float* __restrict__ out
     if (threadIdx.x == 0) out[blockIdx.x] = s;
 }
 
-__global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ buf, size_t n16,
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// Grid-stride streaming read, eight 16-byte nontemporal loads in flight per
+// thread (of the layouts tried on MI355X -- four or eight loads, cached or
+// nontemporal, grid-stride or one contiguous span per workgroup -- this one
+// read fastest).
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4v* __restrict__ buf, size_t n16,
                                                          uint32_t* __restrict__ out) {
+  constexpr int U = 8;
   const size_t stride = size_t(gridDim.x) * 256;
   size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   uint32_t acc = 0u;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = buf[i], v1 = buf[i + stride], v2 = buf[i + 2 * stride], v3 = buf[i + 3 * stride];
-    acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
-    acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4v v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
-    const uint4 v = buf[i];
+    const u32x4v v = buf[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   out[size_t(blockIdx.x) * 256 + threadIdx.x] = acc;
@@ -74,6 +83,6 @@ extern "C" ssa_status ssa_probe_hbm_read(const void* buf, size_t bytes, uint32_t
       reinterpret_cast<uintptr_t>(buf) % 16 != 0)
     return SSA_ERR_INVALID_ARGUMENT;
   hipLaunchKernelGGL(probe_read_kernel, dim3(unsigned(workgroups)), dim3(256), 0,
-                     (hipStream_t)stream, static_cast<const uint4*>(buf), bytes / 16, out);
+                     (hipStream_t)stream, static_cast<const u32x4v*>(buf), bytes / 16, out);
   return launch_status(hipGetLastError());
 }

@@ -30,8 +30,8 @@ ssa_status ssa_probe_mfma_bf16(float* out, int32_t workgroups, int32_t iters, do
                                void* stream);
 
 /* Streaming read of `bytes` bytes at `buf` (16-byte aligned, bytes a multiple
- * of 16) by `workgroups` workgroups of 256 threads, 16 bytes per load, four
- * loads in flight per thread.  out: uint32 [workgroups * 256], written (an XOR
+ * of 16) by `workgroups` workgroups of 256 threads, grid-stride, eight 16-byte
+ * nontemporal loads in flight per thread.  out: uint32 [workgroups * 256], written (an XOR
  * of what each thread read). */
 ssa_status ssa_probe_hbm_read(const void* buf, size_t bytes, uint32_t* out, int32_t workgroups,
                               void* stream);
