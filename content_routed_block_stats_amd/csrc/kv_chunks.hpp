@@ -323,12 +323,18 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
     // when some row of the wave sees a logit more than kLazyLog2 above it, so
     // probabilities stay below 2^kLazyLog2 and most chunks skip the rescale.
     if (__builtin_amdgcn_ballot_w64(mloc > st[nt].m2 + kLazyLog2) != 0) {
-      const float mnew = fmaxf(st[nt].m2, mloc);
-      const float alpha = __builtin_amdgcn_exp2f(st[nt].m2 - (mnew == -__builtin_inff() ? 0.f : mnew));
+      const float mold = st[nt].m2;
+      const float mnew = fmaxf(mold, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -__builtin_inff() ? 0.f : mnew));
       st[nt].m2 = mnew;
       st[nt].l *= alpha;
+      // a row whose reference is still -inf has o = 0 (or NaN from a
+      // non-finite value), which alpha = 0 leaves as it is: a wave whose
+      // rows all start here -- every first chunk -- skips the products
+      if (__builtin_amdgcn_ballot_w64(mold != -__builtin_inff()) != 0) {
 #pragma unroll
-      for (int i = 0; i < A::MTD; ++i) st[nt].o[i] *= alpha;
+        for (int i = 0; i < A::MTD; ++i) st[nt].o[i] *= alpha;
+      }
     }
     const float mref = st[nt].m2 == -__builtin_inff() ? 0.f : st[nt].m2;
     float lsum = 0.f;
@@ -378,6 +384,78 @@ __device__ __forceinline__ void attend_chunk(const uint8_t* lds,
   }
 }
 
+
+// N resident chunks against one 32-row tile, 16-bit inputs and no mask: the
+// arithmetic of attend_chunk (the same products in the same order, so the
+// same results), with each key tile's score chain for chunk c+1 issued into
+// the accumulator that tile's probabilities of chunk c have just left --
+// the matrix core works on the next chunk's scores while the vector ALU
+// finishes this chunk's softmax, within the registers of one chunk.
+template <int D, int N>
+__device__ __forceinline__ void attend_segment(const uint8_t* lds, const bf16x8 (&bq)[D / 16],
+                                               float scale2, int lane, RowState<D>& st) {
+  using A = AT<false, D>;
+  constexpr int NS = A::NS, MTD = A::MTD;
+  auto kfrag = [&](int c, int mt, int s) {
+    return *reinterpret_cast<const bf16x8*>(lds + c * A::CHUNK + (mt * NS + s) * A::FRAG + lane * 16);
+  };
+  auto vfrag = [&](int c, int mt, int sp) {
+    return *reinterpret_cast<const f16x8*>(lds + c * A::CHUNK + A::KBYTES + (mt * 4 + sp) * A::FRAG +
+                                           lane * 16);
+  };
+  auto scores = [&](int c, int mt) {
+    floatx16 acc = mma16(kfrag(c, mt, 0), bq[0], floatx16{});
+#pragma unroll
+    for (int s = 1; s < NS; ++s) acc = mma16(kfrag(c, mt, s), bq[s], acc);
+    return acc;
+  };
+  floatx16 sacc[2] = {scores(0, 0), scores(0, 1)};
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, sacc[mt][j]);
+    mloc = fmaxf(mloc, wave_shfl_xor(mloc, 32)) * scale2;
+    if (__builtin_amdgcn_ballot_w64(mloc > st.m2 + kLazyLog2) != 0) {
+      const float mold = st.m2;
+      const float mnew = fmaxf(mold, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -__builtin_inff() ? 0.f : mnew));
+      st.m2 = mnew;
+      st.l *= alpha;
+      if (__builtin_amdgcn_ballot_w64(mold != -__builtin_inff()) != 0) {
+#pragma unroll
+        for (int i = 0; i < MTD; ++i) st.o[i] *= alpha;
+      }
+    }
+    const float mref = st.m2 == -__builtin_inff() ? 0.f : st.m2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f16x8 pf[2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][j], scale2, -mref));
+        sacc[mt][j] = p;
+        lsum += p;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = sacc[mt][4 * (2 * q + (e >> 2)) + (e & 3)];
+        pf[q] = to_f16x8(pv);
+      }
+      if (c + 1 < N) sacc[mt] = scores(c + 1, mt);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int m = 0; m < MTD; ++m) st.o[m] = mma16(vfrag(c, m, 2 * mt + q), pf[q], st.o[m]);
+    }
+    st.l += lsum;
+  }
+}
 
 }  // namespace
 }  // namespace ssa

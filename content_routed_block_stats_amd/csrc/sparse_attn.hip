@@ -266,7 +266,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
 // blocks, the 256-key segment) changes; within a segment the chunks need no
 // barriers.  The next task's row entries are fetched at the start of a task
 // and its query rows after the first chunk, so they arrive behind compute.
-template <bool F32, int D, typename PartT>
+// SEG > 0 (16-bit inputs): segments of exactly SEG chunks (SEG divides B / 64),
+// each run as one unrolled attend_segment; SEG = 0: chunk by chunk.
+template <bool F32, int D, typename PartT, int SEG>
 __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
     const typename AT<F32, D>::In* __restrict__ Q, const uint8_t* __restrict__ img,
     int64_t n_chunks, const int4* __restrict__ tasks,
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
   const int r = 32 * wave + ln;             // this lane's row within a task
   const int block_chunks = B / kKeyChunk;
-  const int seg_chunks = min(block_chunks, SEG_CHUNKS);
+  const int seg_chunks = SEG > 0 ? SEG : min(block_chunks, SEG_CHUNKS);
   const int segs = (block_chunks + seg_chunks - 1) / seg_chunks;
 
   // (segment ids, (sequence, KV head) pairs and row ids all fit 32 bits:
@@ -358,10 +360,15 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
         __syncthreads();                    // the new segment is in LDS
         resident = sid;
       }
-      if (wave_active)
-        for (int ch = 0; ch < here; ++ch)
-          attend_chunk<F32, D, 1>(lds + ch * A::CHUNK, bq, scale2, lane, st,
-                                  [](int, int, int, int) { return true; });
+      if (wave_active) {
+        if constexpr (SEG > 0 && !F32) {
+          attend_segment<D, SEG>(lds, bq[0], scale2, lane, st[0]);
+        } else {
+          for (int ch = 0; ch < here; ++ch)
+            attend_chunk<F32, D, 1>(lds + ch * A::CHUNK, bq, scale2, lane, st,
+                                    [](int, int, int, int) { return true; });
+        }
+      }
     }
     // (c) the partial of every row of the task: the unnormalised sums
     // o = sum_j p_j v_j (values pre-scaled by 2^-ev) times 2^-e, where
@@ -709,6 +716,20 @@ AttnWs attn_ws_layout(const Shape& s, void* base) {
   return w;
 }
 
+// The block pass for blocks of bc chunks: for 16-bit inputs the instance
+// whose segment length is the largest divisor of bc that fits the resident
+// LDS; for float32 inputs the chunk-by-chunk one.
+template <bool F32, int D, typename PartT, int SEG = kResidentBytes / AT<F32, D>::CHUNK>
+auto block_kernel_for(int bc) -> decltype(&block_attn_kernel<F32, D, PartT, 0>) {
+  if constexpr (F32) {
+    return &block_attn_kernel<F32, D, PartT, 0>;
+  } else {
+    if constexpr (SEG > 1)
+      if (bc % SEG != 0) return block_kernel_for<F32, D, PartT, SEG - 1>(bc);
+    return &block_attn_kernel<F32, D, PartT, SEG>;
+  }
+}
+
 template <bool F32, int D, typename OutT>
 hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const void* Vv,
                          const int32_t* idx, void* Ov, float* lse, void* ws, hipStream_t st) {
@@ -753,7 +774,7 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
     hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(256), hshm, st, idx, w.cursor, w.entries,
                        w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    auto bk = block_attn_kernel<F32, D, PartT>;
+    auto bk = block_kernel_for<F32, D, PartT>(s.B / kKeyChunk);
     const size_t bshm = size_t(kResidentBytes) + (kBlockThreads / 64) * size_t(kStageBytes);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(bk),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(bshm))) != hipSuccess)
