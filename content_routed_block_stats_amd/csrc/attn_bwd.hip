@@ -1095,7 +1095,7 @@ hipError_t launch_bwd_t(const Shape& s, const void* Qv, const void* Kv, const vo
                      reinterpret_cast<int32_t*>(w.domax), n_bh, 0);
   if (!F32) {
     const int64_t per_head = s.n * D;
-    const unsigned gx = unsigned(std::min<int64_t>((per_head / 8 + 255) / 256, 256));
+    const unsigned gx = value_max_groups(per_head);
     hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
                        reinterpret_cast<const bf16_t*>(Kv), w.kmax, per_head);
     hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bh)), dim3(256), 0, st,

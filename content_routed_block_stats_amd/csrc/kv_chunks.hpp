@@ -216,23 +216,48 @@ __device__ __forceinline__ void stage_chunk_dma(uint8_t* lds, const uint8_t* src
 }
 
 // Largest |v| of every (sequence, KV head), as bfloat16 bits (order-preserving
-// for non-negative values), for the float16 value scale.
+// for non-negative values), for the float16 value scale.  Each thread keeps
+// kMaxLoads 16-byte loads in flight per round, and a workgroup folds its
+// waves in LDS before a single atomic (thousands of atomics on one address
+// serialise at the cache and dominated small inputs).
+constexpr int kMaxLoads = 8;
+
+// Workgroups per (sequence, KV head) for value_max_kernel over per_head
+// bfloat16 values: one round of kMaxLoads loads per thread, at most 128.
+inline unsigned value_max_groups(int64_t per_head) {
+  const int64_t n16 = per_head / 8, per_group = 256 * kMaxLoads;
+  return unsigned(std::max<int64_t>(1, std::min<int64_t>((n16 + per_group - 1) / per_group, 128)));
+}
+
 __global__ __launch_bounds__(256) void value_max_kernel(const bf16_t* __restrict__ V,
                                                         uint32_t* __restrict__ vmax,
                                                         int64_t per_head) {
+  __shared__ uint32_t wmax[4];
   const int64_t bkv = blockIdx.y;
   const u32x4* src = reinterpret_cast<const u32x4*>(V + bkv * per_head);
   const int64_t n16 = per_head / 8;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   uint32_t m = 0;
-  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n16;
-       i += int64_t(gridDim.x) * blockDim.x) {
-    const u32x4 w = src[i];
+  for (int64_t i0 = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i0 < n16; i0 += kMaxLoads * stride) {
+    u32x4 w[kMaxLoads];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    for (int u = 0; u < kMaxLoads; ++u) {
+      const int64_t i = i0 + u * stride;
+      w[u] = i < n16 ? src[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxLoads; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = max(m, max(w[u][j] & 0x7FFFu, (w[u][j] >> 16) & 0x7FFFu));
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = max(m, uint32_t(__shfl_xor(int(m), o, 64)));
-  if ((threadIdx.x & 63) == 0) atomicMax(&vmax[bkv], m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t r = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    atomicMax(&vmax[bkv], r);
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t v) {

@@ -281,8 +281,14 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
     const int64_t m = shift_nb < kShiftBlocks ? shift_nb : kShiftBlocks;
     const float* S0 = shift_sigma + bkv * shift_nb * int64_t(D) * D;
     for (int j = tid; j < D; j += blockDim.x) {
+      // the (at most kShiftBlocks) loads go out together, summed in block order
+      float dv[kShiftBlocks];
+#pragma unroll
+      for (int c = 0; c < kShiftBlocks; ++c) dv[c] = c < m ? S0[(c * D + j) * D + j] : 0.f;
       float acc = 0.f;
-      for (int64_t c = 0; c < m; ++c) acc += half_beta * S0[(c * D + j) * D + j];
+#pragma unroll
+      for (int c = 0; c < kShiftBlocks; ++c)
+        if (c < m) acc += half_beta * dv[c];
       sdb[j] = acc / float(m);
       if (blockIdx.x == 0) dbar[bkv * D + j] = sdb[j];
     }
@@ -294,13 +300,27 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
     if (i == j) return F32 ? half_beta * sij : half_beta * sij - sdb[i];
     return 0.f;
   };
-  // float16 parts: scale by 2^-e so that the largest |T'_ij| lies in [2^14, 2^15)
+  // float16 parts: scale by 2^-e so that the largest |T'_ij| lies in [2^14, 2^15).
+  // One pass over Sigma gives that maximum and, for the bound G below, the
+  // absolute column sums of sym(T'_c) (Sigma is symmetric, so column sums
+  // equal row sums and read coalesced): thread (column j, quarter r) covers
+  // rows [r D/QR, (r+1) D/QR) of column j, sixteen loads in flight.
   float scale = 1.f, unscale = 1.f;
+  static_assert(D * 4 <= 512 && 256 % D == 0, "column split");
+  constexpr int QR = 256 / D;   // row groups per column
+  __shared__ float colsum[256];
   if constexpr (!F32) {
     float mx = 0.f;
-    for (int w = tid; w < D * D; w += blockDim.x) {
-      const int i = w / D, j = w % D;
-      if (i <= j) mx = fmaxf(mx, fabsf(tval(i, j)));
+    {
+      const int j = tid % D, r = tid / D;
+      float cs = 0.f;
+#pragma unroll 16
+      for (int i = r * (D / QR); i < (r + 1) * (D / QR); ++i) {
+        const float sij = S[i * D + j];
+        cs += i == j ? fabsf(half_beta * sij - sdb[j]) : fabsf(half_beta * sij);
+        if (i <= j) mx = fmaxf(mx, fabsf(i < j ? beta * sij : half_beta * sij - sdb[i]));
+      }
+      colsum[tid] = cs;
     }
     mx = wave_max(mx);
     if (lane == 0) red[0][wave] = mx;
@@ -363,20 +383,8 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
   }
   if (tid == 0) *reinterpret_cast<float*>(out + Lay::SCALE_OFF) = unscale;
   if constexpr (!F32) {
-    // G: largest absolute row sum of sym(T'_c) (real units) -- Sigma is
-    // symmetric, so column sums, read coalesced: thread (column j, quarter
-    // r) sums rows [r D/4, (r+1) D/4) of column j; nu = ||mu_c||
-    static_assert(D * 4 <= 512 && 256 % D == 0, "column split");
-    constexpr int QR = 256 / D;   // row groups per column
-    __shared__ float colsum[256];
-    {
-      const int j = tid % D, r = tid / D;
-      float cs = 0.f;
-#pragma unroll 8
-      for (int i = r * (D / QR); i < (r + 1) * (D / QR); ++i)
-        cs += i == j ? fabsf(half_beta * S[i * D + j] - sdb[j]) : fabsf(half_beta * S[i * D + j]);
-      colsum[tid] = cs;
-    }
+    // G: largest absolute row sum of sym(T'_c) (real units), from the
+    // column sums above; nu = ||mu_c||
     float nu2 = 0.f;
     for (int i = tid; i < D; i += blockDim.x) nu2 = fmaf(M[i], M[i], nu2);
     __syncthreads();   // A and the column sums complete
@@ -1480,7 +1488,7 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
                      5 * n_bkv, 0);
   if constexpr (!F32) {
     const int64_t per_group = int64_t(s.g) * s.n * D;
-    const unsigned gx = unsigned(std::min<int64_t>((per_group / 8 + 255) / 256, 256));
+    const unsigned gx = value_max_groups(per_group);
     hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
                        static_cast<const bf16_t*>(Q), w.qmax, per_group);
   }
@@ -1996,7 +2004,7 @@ hipError_t launch_hier_prefill_t(const Shape& s, const void* Q, const float* mu,
   hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((n_cnt + 255) / 256, 1024))),
                      dim3(256), 0, st, w.gcnt, n_cnt, 0);
   const int64_t per_group = int64_t(s.g) * s.n * D;
-  const unsigned gx = unsigned(std::min<int64_t>((per_group / 8 + 255) / 256, 256));
+  const unsigned gx = value_max_groups(per_group);
   hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
                      static_cast<const bf16_t*>(Q), w.qmax, per_group);
   hipLaunchKernelGGL((route_prep_kernel<false, D>), dim3(unsigned(s.nb), unsigned(n_bkv)),

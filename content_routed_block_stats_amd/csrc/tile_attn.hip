@@ -174,7 +174,7 @@ hipError_t launch_tile_attn_t(const Shape& s, const void* Qv, const void* Kv, co
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st,
                        reinterpret_cast<int32_t*>(w.vmax), n_bkv, 0);
     const int64_t per_head = s.n * D;
-    const unsigned gx = unsigned(std::min<int64_t>((per_head / 8 + 255) / 256, 256));
+    const unsigned gx = value_max_groups(per_head);
     hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
                        reinterpret_cast<const bf16_t*>(Vv), w.vmax, per_head);
   }
