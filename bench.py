@@ -446,11 +446,13 @@ def recall_sweep(wl, seed: int, betas: list[float]) -> dict:
 def hier_prefill_study(wl, m: int, reps: int, seed: int) -> dict:
     """Exact hierarchical routing of the prefill rows (ssa_group_stats +
     ssa_route_hier_prefill, groups of m blocks) beside the flat router
-    (ssa_route_topk) on the same inputs, for the standard keys and for
-    clustered keys (tight blocks around well separated group centres):
-    median times, the (row, block) scores the visit computed (each listed
-    tile's blocks times its 512 rows) over the routable pairs, and whether the
-    selections agree."""
+    (ssa_route_topk) on the same inputs, for the standard keys, for
+    clustered keys (tight blocks around well separated group centres) and for
+    clustered keys with topical queries (each 1024-token segment's queries
+    lean toward one earlier group; no planted outliers, whose single far keys
+    widen their group's spectral bound for every query): median times, the
+    (row, block) scores the visit computed (each listed tile's blocks times
+    its 512 rows) over the routable pairs, and whether the selections agree."""
     import statistics
 
     import torch
@@ -470,9 +472,10 @@ def hier_prefill_study(wl, m: int, reps: int, seed: int) -> dict:
         return statistics.median(out)
 
     rows = []
-    for keys, w in (("standard", wl),
-                    ("clustered", wl.replace(center_std=0.05, noise_std=0.05, group_std=1.0,
-                                             group_blocks=m))):
+    clustered = wl.replace(center_std=0.05, noise_std=0.05, group_std=1.0, group_blocks=m)
+    for keys, w in (("standard", wl), ("clustered", clustered),
+                    ("clustered, topical queries",
+                     clustered.replace(plants=0, query_topic=0.5, topic_span=1024))):
         data = make_prefill(w, seed=seed, device="cuda")
         Q, K = data["Q"], data["K"]
         del data["V"]
@@ -739,7 +742,14 @@ def main() -> int:
                             "effective_gather_gbs": round(logical / (t_attn * 1e-3) / 1e9, 1),
                             "effective_gather_note": ("K and V bytes of every (row, key of S(t)) "
                                                       "pair as a per-row gather would read them, "
-                                                      "over the stage time")},
+                                                      "over the stage time"),
+                            # the same stage against the matrix cores: 4d flops
+                            # (q.k and p v) per (row, key of S(t)); with large
+                            # blocks (the 1M workload) this, not HBM, is the bound
+                            "algorithmic_flops_per_launch": pairs * 4 * wl.head_dim,
+                            "mfma_tflops": round(pairs * 4 * wl.head_dim / (t_attn * 1e-3) / 1e12, 1),
+                            "mfma_frac": round(pairs * 4 * wl.head_dim / (t_attn * 1e-3) / 1e12
+                                               / MFMA_BF16_PEAK_TFLOPS, 4)},
         "onbox_peaks": peaks,
         "block_stats": {"kernel": "block_stats", "bound": "alu", "ms": round(t_stats, 4),
                         "algorithmic_bytes_per_launch": stats_bytes(wl),

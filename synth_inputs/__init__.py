@@ -14,7 +14,14 @@ These plants play the role of single-needle targets.  With group_std > 0 each
 run of group_blocks consecutive block centres also shares a group centre
 N(0, group_std^2 I), a geometry in which whole groups of blocks can be ruled out
 for a query (the hierarchical router's test case); group_std = 0, the default,
-leaves every existing stream unchanged.
+leaves every existing stream unchanged.  query_topic > 0 (with group_std > 0)
+also gives the queries topics: the sequence is cut into segments of
+topic_span tokens, each segment picks one earlier key group (uniformly among
+those whose blocks all end before it) and every query of the segment, in all
+q-heads of the KV head, gets query_topic * sqrt(d) times that group centre's
+unit vector added -- neighbouring queries then want the same groups, the
+structure a tree router prunes on; query_topic = 0, the default, leaves Q
+unchanged.
 
 Everything is drawn with torch generators seeded per tensor, so a workload is a
 pure function of (config, seed, device).  CPU and GPU generators give different

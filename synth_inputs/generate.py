@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 _TAG_Q, _TAG_K_CENTRE, _TAG_K_NOISE, _TAG_V, _TAG_PLANT = 11, 13, 17, 19, 23
-_TAG_QNEW, _TAG_VNEW, _TAG_K_GROUP = 29, 31, 37
+_TAG_QNEW, _TAG_VNEW, _TAG_K_GROUP, _TAG_Q_TOPIC = 29, 31, 37, 41
 
 
 def _mix(*parts: int) -> int:
@@ -44,7 +44,8 @@ class Workload:
     decode: bool = False
     group_std: float = 0.0    # std of a centre shared by group_blocks consecutive blocks
     group_blocks: int = 16    # (0 std: no group structure, the default)
-
+    query_topic: float = 0.0  # strength of a segment's topic in its queries (needs group_std)
+    topic_span: int = 1024    # tokens per topic segment
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
 
@@ -151,11 +152,41 @@ def _keys(wl: Workload, seed: int, b: int, kv: int, n_keys: int, device) -> torc
     centre = _randn((nbp, d), device, seed, _TAG_K_CENTRE, b, kv) * wl.center_std
     if wl.group_std > 0:
         # routable geometry: block centres scattered around shared group centres
-        ngp = -(-nbp // wl.group_blocks)
-        grp = _randn((ngp, d), device, seed, _TAG_K_GROUP, b, kv) * wl.group_std
+        grp = _group_centres(wl, seed, b, kv, n_keys, device)
         centre = centre + grp.repeat_interleave(wl.group_blocks, dim=0)[:nbp]
     noise = _randn((n_keys, d), device, seed, _TAG_K_NOISE, b, kv) * wl.noise_std
     return noise.add_(centre.repeat_interleave(B, dim=0)[:n_keys])
+
+
+def _group_centres(wl: Workload, seed: int, b: int, kv: int, n_keys: int, device) -> torch.Tensor:
+    nbp = -(-n_keys // wl.block)
+    ngp = -(-nbp // wl.group_blocks)
+    return _randn((ngp, wl.head_dim), device, seed, _TAG_K_GROUP, b, kv) * wl.group_std
+
+
+def _topics(wl: Workload, seed: int, b: int, kv: int, n: int) -> list[int]:
+    """Topic group of every topic_span-token segment of one (sequence, KV head):
+    uniform over the groups whose blocks are all complete before the segment
+    starts, -1 while there is none.  A CPU generator keeps it device-independent."""
+    gen = _gen("cpu", seed, _TAG_Q_TOPIC, b, kv)
+    out = []
+    for t0 in range(0, n, wl.topic_span):
+        top = t0 // wl.block // wl.group_blocks - 1
+        out.append(int(torch.randint(top + 1, (1,), generator=gen)) if top >= 0 else -1)
+    return out
+
+
+def _add_topics(Qf: torch.Tensor, wl: Workload, seed: int, b: int, kv: int, device) -> None:
+    """Queries of a segment lean toward their topic group's key centre:
+    q += query_topic * sqrt(d) * (unit group centre), the same for every
+    q-head of the KV head."""
+    n, d = Qf.shape[-2], Qf.shape[-1]
+    grp = _group_centres(wl, seed, b, kv, n, device)
+    unit = grp / torch.linalg.vector_norm(grp, dim=-1, keepdim=True)
+    for s, gi in enumerate(_topics(wl, seed, b, kv, n)):
+        if gi >= 0:
+            t0 = s * wl.topic_span
+            Qf[:, t0:t0 + wl.topic_span] += wl.query_topic * math.sqrt(d) * unit[gi]
 
 
 def _plant(K: torch.Tensor, plants: list[dict], qrow) -> None:
@@ -174,9 +205,16 @@ def make_prefill(wl: Workload, seed: int = 0, device="cpu") -> dict:
     K = torch.empty((b_, hkv, n, d), dtype=dt, device=device)
     V = torch.empty((b_, hkv, n, d), dtype=dt, device=device)
     ledger: list[dict] = []
+    if wl.query_topic > 0 and wl.group_std <= 0:
+        raise ValueError("query topics lean toward key group centres: set group_std > 0")
+    g = wl.group
     for b in range(b_):
-        for h in range(hq):
-            Q[b, h] = _randn((n, d), device, seed, _TAG_Q, b, h).to(dt)
+        for kv in range(hkv):
+            Qf = torch.stack([_randn((n, d), device, seed, _TAG_Q, b, h)
+                              for h in range(kv * g, (kv + 1) * g)])
+            if wl.query_topic > 0:
+                _add_topics(Qf, wl, seed, b, kv, device)
+            Q[b, kv * g:(kv + 1) * g] = Qf.to(dt)
         for kv in range(hkv):
             V[b, kv] = _randn((n, d), device, seed, _TAG_V, b, kv).to(dt)
             plants = _plan_plants(wl, seed, b, kv, n, n)

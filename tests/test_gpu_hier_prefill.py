@@ -54,6 +54,11 @@ CASES = {
     # clustered keys: most groups pruned
     "clustered_m16": (_BASE.replace(batch=1, n_q_heads=8, n_kv_heads=2, seq_len=64 * 256,
                                     block=64, top_k=8, window=64, plants=2, **_CLUSTER), 16),
+    # clustered keys and topical queries (each 1024-token segment leans toward
+    # one earlier group), no planted outliers: whole groups pruned per tile
+    "topical_m16": (_BASE.replace(batch=1, n_q_heads=8, n_kv_heads=2, seq_len=64 * 512, block=64,
+                                  top_k=8, window=64, plants=0, group_blocks=16, query_topic=0.5,
+                                  topic_span=1024, **_CLUSTER), 16),
     # k >= nb for the early rows and more: every routable block kept
     "dense_k": (_BASE.replace(batch=1, n_q_heads=2, n_kv_heads=1, seq_len=64 * 20 + 9, block=64,
                               top_k=32, window=64, plants=1), 4),

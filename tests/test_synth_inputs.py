@@ -61,3 +61,36 @@ def test_decode_inputs():
     assert data["q"].shape == (2, 4, 128) and data["k_new"].shape == (2, 2, 128)
     for p in data["plants"]:
         assert p["pos"] < 1000 and p["t"] == 1000
+
+
+def test_topical_queries():
+    """query_topic adds the segment's topic direction to every query of the
+    segment (all q-heads of the KV head), the topic is an earlier group, and
+    query_topic = 0 leaves Q as the plain generator draws it."""
+    base = CONFIGS["tiny_prefill_4k"].replace(n_q_heads=2, n_kv_heads=1, seq_len=2048, plants=0,
+                                              center_std=0.05, noise_std=0.05, group_std=1.0,
+                                              group_blocks=4)
+    plain = make_prefill(base, seed=3)
+    assert torch.equal(plain["Q"], make_prefill(base.replace(topic_span=256), seed=3)["Q"])
+    wl = base.replace(query_topic=0.5, topic_span=256)
+    top = make_prefill(wl, seed=3)
+    assert torch.equal(top["K"], plain["K"]) and torch.equal(top["V"], plain["V"])
+    d, B, m = wl.head_dim, wl.block, wl.group_blocks
+    shift = (top["Q"] - plain["Q"])[0]                           # [heads, n, d]
+    n_seg = wl.seq_len // wl.topic_span
+    for s in range(n_seg):
+        seg = shift[:, s * 256:(s + 1) * 256]
+        t0 = s * 256
+        if t0 // B < m:
+            assert torch.count_nonzero(seg) == 0                 # no complete group yet
+            continue
+        v = seg[0, 0]
+        assert torch.allclose(v.norm(), torch.tensor(0.5 * np.sqrt(d), dtype=torch.float32), rtol=1e-5)
+        assert torch.allclose(seg, v.expand_as(seg), atol=1e-5)  # one direction, every head and row
+        # the direction is one of the groups complete before the segment: it
+        # aligns with that group's key mean (the centre dominates the noise)
+        K = top["K"][0, 0]
+        top_group = t0 // B // m - 1
+        means = torch.stack([K[gi * m * B:(gi + 1) * m * B].mean(0) for gi in range(top_group + 1)])
+        cos = (means @ v) / (means.norm(dim=1) * v.norm())
+        assert cos.max() > 0.99
