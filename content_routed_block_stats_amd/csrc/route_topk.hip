@@ -1253,8 +1253,10 @@ constexpr int kRescoreThreads = 256;
 // times the image's scale.  Lane (ln, h) returns row ln of query tile h.
 //
 // With lin != nullptr it also returns, in the same units, the mean term
-// <q, mu> alone (the row-dot of q with the image's mu).
-template <int D>
+// <q, mu> alone (the row-dot of q with the image's mu).  LO = false: the hi
+// part alone (the single pass's arithmetic), within the single pass's error
+// bound e of the hi + lo score.
+template <int D, bool LO = true>
 __device__ __forceinline__ float hilo_score(const uint8_t* L, const f16x8 (&bq)[2][D / 16],
                                             int lane, float* lin = nullptr) {
   using Lay = RouteLayout<D>;
@@ -1270,7 +1272,8 @@ __device__ __forceinline__ float hilo_score(const uint8_t* L, const f16x8 (&bq)[
   // read before this chunk's four MFMAs); the scheduling barriers keep the
   // compiler from reading the whole image ahead, which needs more registers
   // than a wave has
-  f16x8 cur[2] = {frag(MT - 1, 0, 0), frag(MT - 1, 0, 1)};
+  constexpr int PARTS = LO ? 2 : 1;
+  f16x8 cur[2] = {frag(MT - 1, 0, 0), LO ? frag(MT - 1, 0, 1) : f16x8{}};
 #pragma unroll
   for (int mt = MT - 1; mt >= 0; --mt) {
     floatx16 acc[2];
@@ -1298,13 +1301,13 @@ __device__ __forceinline__ float hilo_score(const uint8_t* L, const f16x8 (&bq)[
       f16x8 nxt[2] = {cur[0], cur[1]};
       if (s2 < 2 * mt + 1) {
         nxt[0] = frag(mt, s2 + 1, 0);
-        nxt[1] = frag(mt, s2 + 1, 1);
+        if constexpr (LO) nxt[1] = frag(mt, s2 + 1, 1);
       } else if (mt > 0) {
         nxt[0] = frag(mt - 1, 0, 0);
-        nxt[1] = frag(mt - 1, 0, 1);
+        if constexpr (LO) nxt[1] = frag(mt - 1, 0, 1);
       }
 #pragma unroll
-      for (int part = 0; part < 2; ++part)
+      for (int part = 0; part < PARTS; ++part)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[nt] = mma16(cur[part], bq[nt][s2], acc[nt]);
       cur[0] = nxt[0];
@@ -1570,8 +1573,10 @@ hipError_t launch_route_d(const Shape& s, const void* Q, const float* mu, const 
 // r_G the routing score of (mu_G, S_G).  r_G is computed like a block score:
 // the summaries are prepared into the same images (with the blocks' diagonal
 // shift, so bounds and scores leave out the same q^T diag(D) q) and scored
-// with the exact pass's hi + lo arithmetic; the bound carries a relative
-// margin (kHierPrefillMargin of its terms' magnitudes) over float32 rounding.
+// with the hi part alone, as in the single pass, plus that pass's rigorous
+// bound e on |hi - (hi + lo)| (the group images' own constants), so it never
+// falls below the exact pass's r_G; the bound carries a relative margin
+// (kHierPrefillMargin of its terms' magnitudes) over float32 rounding.
 //
 // Blocks are scored for a tile of rows at a time (one image in LDS serves
 // 512 rows), so a tile pays for the union of what its rows need.  Rows are
@@ -1607,7 +1612,7 @@ struct HierWs {
   uint8_t* img;      // block images [b*hkv][nb]
   uint8_t* gimg;     // group images [b*hkv][G]
   uint32_t* qmax;    // [b*hkv], then bounds [b*hkv][4] (unused here)
-  uint32_t* gbounds; // [b*hkv][4] (unused here)
+  uint32_t* gbounds; // [b*hkv][4]: the group images' error-bound constants
   float* dbar;       // [b*hkv][d]
   float* gdbar;      // [b*hkv][d]
   float* ub;         // [b*hkv][rows][G]: bounds, row-major
@@ -1715,7 +1720,8 @@ __device__ __forceinline__ void stage_image(const uint8_t* src, uint8_t* dst, in
 // when it has none), and the tile's count of rows per best group.
 template <int D>
 __global__ __launch_bounds__(kRouteThreads) void hier_ub_kernel(
-    const bf16_t* __restrict__ Q, const uint8_t* __restrict__ gimg, const float* __restrict__ grl, const uint32_t* __restrict__ qmax, float* __restrict__ ub,
+    const bf16_t* __restrict__ Q, const uint8_t* __restrict__ gimg, const float* __restrict__ grl,
+    const uint32_t* __restrict__ qmax, const uint32_t* __restrict__ gbounds, float* __restrict__ ub,
     int32_t* __restrict__ best, int32_t* __restrict__ gcnt, int64_t n, int g, int hq, int hkv,
     int B, int64_t nb, int m, int64_t G, int64_t n_tiles, int64_t n_bkv, float beta) {
   using Lay = RouteLayout<D>;
@@ -1749,6 +1755,18 @@ __global__ __launch_bounds__(kRouteThreads) void hier_ub_kernel(
   for (int64_t i = tid; i < G; i += kRouteThreads) hist[i] = 0;
   const float nq2 = row_norm2<D>(bq, h);
   const float qn = sqrtf(nq2);
+  // r_G is scored with the hi part only: |hi - (hi + lo)| <= e, the single
+  // pass's bound with the group images' own constants (lam, G, nu, max|D|)
+  float e_hi;
+  {
+    const float nq2e = nq2 * (1.f + 0x1p-16f);
+    const float lam = __uint_as_float(gbounds[bkv * 4 + 0]);
+    const float Gs = __uint_as_float(gbounds[bkv * 4 + 1]);
+    const float nu = __uint_as_float(gbounds[bkv * 4 + 2]);
+    const float dm = __uint_as_float(gbounds[bkv * 4 + 3]);
+    e_hi = 1.25f * (lam * nq2e + 0x1p-17f * (Gs * nq2e + nu * qsc * sqrtf(nq2e)) +
+                    0x1p-22f * (dm + Gs) * nq2e);
+  }
   float* my_ub = ub + (bkv * rows_total + (my_valid ? my_rho : 0)) * G;
   float best_u = -__builtin_inff();
   int best_g = 0;
@@ -1767,7 +1785,7 @@ __global__ __launch_bounds__(kRouteThreads) void hier_ub_kernel(
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) asm volatile("" : "+v"(bq[nt][s2]));
     float lin;   // the mean term <q, mu_G>, in the same (score) units
-    const float su = hilo_score<D>(lds + (gi & 1) * Lay::LDS_BYTES, bq, lane, &lin);
+    const float su = hilo_score<D, false>(lds + (gi & 1) * Lay::LDS_BYTES, bq, lane, &lin) + e_hi;
     const float R = grl[(bkv * G + gi) * 2], lam = grl[(bkv * G + gi) * 2 + 1];
     const float rad = qn * R * qsc, slack = 0.5f * beta * lam * nq2;
     const float mag = fabsf(lin) + fabsf(su - lin) + rad + slack;
@@ -1999,6 +2017,8 @@ hipError_t launch_hier_prefill_t(const Shape& s, const void* Q, const float* mu,
   }
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<int32_t*>(w.qmax),
                      5 * n_bkv, 0);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st,
+                     reinterpret_cast<int32_t*>(w.gbounds), 4 * n_bkv, 0);
   // counts of the last chunk's missing tiles stay zero
   const int64_t n_cnt = n_bkv * G * hier_chunks(n_tiles) * kHierChunk;
   hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((n_cnt + 255) / 256, 1024))),
@@ -2014,7 +2034,7 @@ hipError_t launch_hier_prefill_t(const Shape& s, const void* Q, const float* mu,
                      dim3(256), 0, st, gmu, gS, w.qmax, w.gbounds, w.gdbar, w.gimg, G, s.beta,
                      sigma, s.nb);
   hipLaunchKernelGGL((hier_ub_kernel<D>), dim3(grid), dim3(kRouteThreads), 0, st,
-                     static_cast<const bf16_t*>(Q), w.gimg, grl, w.qmax, w.ub, w.best, w.gcnt,
+                     static_cast<const bf16_t*>(Q), w.gimg, grl, w.qmax, w.gbounds, w.ub, w.best, w.gcnt,
                      s.n, s.g, s.hq, s.hkv, s.B, s.nb, m, G, n_tiles, n_bkv, s.beta);
   hipLaunchKernelGGL(route_scan_kernel, dim3(unsigned(n_bkv)), dim3(1024), 0, st, w.gcnt, w.goff,
                      w.gtot, G * hier_chunks(n_tiles) * kHierChunk);
