@@ -62,6 +62,35 @@ __device__ __forceinline__ void dma_copy(uint8_t* lds, const uint8_t* src, int b
                                      0, 0);
 }
 
+// The same copy written in asm (m0 saved and restored around each
+// instruction), so the compiler does not know of it: it then does not make
+// every later LDS read wait for the copy (it cannot tell the LDS buffers
+// apart), and a copy into one buffer overlaps the work on another.  The
+// caller waits for it itself -- s_waitcnt vmcnt(0), then a workgroup
+// barrier -- before anything reads the copied bytes.  (Loads complete in
+// order, so the compiler's own counted waits for later or earlier loads stay
+// correct; they only wait longer.)
+__device__ __forceinline__ void dma_copy_async(uint8_t* lds, const uint8_t* src, int bytes, int tid,
+                                               int nthreads) {
+  const int wave = tid / 64, lane = tid % 64, waves = nthreads / 64;
+  const uint32_t base =
+      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(lds)));
+  for (int r = wave; r < bytes / 1024; r += waves) {
+    const uint8_t* g = src + r * 1024 + lane * 16;
+    const uint32_t l = __builtin_amdgcn_readfirstlane(base + uint32_t(r * 1024));
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "v"(g), "s"(l)
+        : "memory");
+  }
+}
+
 template <bool F32, int D>
 __device__ __forceinline__ typename AT<F32, D>::Frag load_row_frag(const typename AT<F32, D>::In* row,
                                                                    int s, int h, bool valid) {
@@ -199,20 +228,6 @@ __global__ __launch_bounds__(kAttnThreads) void kv_image_kernel(
   ChunkRegs<F32, D> cr;
   cr.load(K + bkv * n * D, V + bkv * n * D, ci * kKeyChunk, n, threadIdx.x);
   cr.store(img + (bkv * n_chunks + ci) * A::CHUNK, threadIdx.x, vscale);
-}
-
-// Copy one chunk image (A::CHUNK bytes) into LDS: each wave moves a quarter,
-// 1 KB per instruction, global -> LDS directly.
-template <bool F32, int D>
-__device__ __forceinline__ void stage_chunk_dma(uint8_t* lds, const uint8_t* src, int tid) {
-  constexpr int PER_WAVE = AT<F32, D>::CHUNK / (kAttnThreads / 64);
-  const int wave = tid / 64, lane = tid % 64;
-#pragma unroll
-  for (int i = 0; i < PER_WAVE / 1024; ++i) {
-    const int off = wave * PER_WAVE + i * 1024;
-    __builtin_amdgcn_global_load_lds(src + off + lane * 16,
-                                     (__attribute__((address_space(3))) void*)(lds + off), 16, 0, 0);
-  }
 }
 
 // Largest |v| of every (sequence, KV head), as bfloat16 bits (order-preserving

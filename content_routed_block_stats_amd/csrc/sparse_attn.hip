@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int64_t ch0 = key_lo / kKeyChunk, ch1 = t_hi / kKeyChunk;
   const uint8_t* src = img + bkv * n_chunks * A::CHUNK;
   const int ev = F32 ? 0 : value_exponent(vmax[bkv]);
-  stage_chunk_dma<F32, D>(lds, src + ch0 * A::CHUNK, tid);
+  dma_copy_async(lds, src + ch0 * A::CHUNK, A::CHUNK, tid, kAttnThreads);
 
   for (int w = tid; w < kWinRows * k; w += kAttnThreads) {
     const int rr = w / k, i = w % k;   // coalesced idx reads, transposed LDS writes
@@ -469,11 +469,22 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 
   RowState<D> st[1];
   row_state_init(st[0]);
+  // the query fragments and index rows are in before the loop, so the
+  // compiler's own waits inside it (it cannot see the chunk copies) have
+  // nothing left to wait for
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int64_t ch = ch0; ch <= ch1; ++ch) {
     const int buf = int((ch - ch0) & 1);
     const bool more = ch + 1 <= ch1;
-    if (more) stage_chunk_dma<F32, D>(lds + (buf ^ 1) * A::CHUNK, src + (ch + 1) * A::CHUNK, tid);
+    // chunk ch has landed (this wave's copies, then everyone's), and every
+    // wave is done with chunk ch-1, whose buffer the next copy refills while
+    // chunk ch is computed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (more)
+      dma_copy_async(lds + (buf ^ 1) * A::CHUNK, src + (ch + 1) * A::CHUNK, A::CHUNK, tid,
+                     kAttnThreads);
     const int64_t key0 = ch * kKeyChunk;
     // does this wave's token range touch the chunk at all?
     const bool touch = wave_active && key0 <= wave_t_hi && key0 + kKeyChunk - 1 > wave_t_lo - W;
@@ -491,10 +502,10 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
                                 return (j <= tv) & (j > tv - W);
                               });
     }
-    __syncthreads();
   }
+  __syncthreads();   // every wave is done with the chunk buffers
   // ---- hand the window part over to the merge layout (LDS, reusing the
-  // first chunk buffer; the loop above ended on a barrier), normalised by its
+  // first chunk buffer), normalised by its
   // sum and in the partials' precision.  Element e of a row is column
   // pi(e) = 32mt + 8a + 4h + b for e = h D/2 + 16mt + 4a + b -- the order
   // partials are stored in -- so a lane half's values are one contiguous

@@ -88,15 +88,22 @@ __global__ __launch_bounds__(kTileThreads) void tile_attn_kernel(
   const int64_t tv = valid ? t : -(int64_t(1) << 40);
   RowState<D> st[1];
   row_state_init(st[0]);
+  // the query fragments are in before the loop, so the compiler's own waits
+  // inside it (it cannot see the chunk copies) have nothing left to wait for
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nsel = nlist[0], cnt = nlist[1];
-  if (cnt > 0) dma_copy(lds, src + int64_t(list[0]) * A::CHUNK, A::CHUNK, tid, kTileThreads);
-  __syncthreads();
+  if (cnt > 0) dma_copy_async(lds, src + int64_t(list[0]) * A::CHUNK, A::CHUNK, tid, kTileThreads);
   for (int i = 0; i < cnt; ++i) {
     const int buf = i & 1;
+    // chunk i has landed (this wave's copies, then everyone's), and every
+    // wave is done with chunk i-1, whose buffer the next copy refills while
+    // chunk i is computed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     if (i + 1 < cnt)
-      dma_copy(lds + (buf ^ 1) * A::CHUNK, src + int64_t(list[i + 1]) * A::CHUNK, A::CHUNK, tid,
-               kTileThreads);
+      dma_copy_async(lds + (buf ^ 1) * A::CHUNK, src + int64_t(list[i + 1]) * A::CHUNK, A::CHUNK,
+                     tid, kTileThreads);
     const int64_t key0 = int64_t(list[i]) * kKeyChunk;
     // a selected block lies before the tile: every key counts for every row;
     // a window chunk counts keys in (t - W, t]
@@ -112,7 +119,6 @@ __global__ __launch_bounds__(kTileThreads) void tile_attn_kernel(
                                 return (kj <= hi) & (kj > lo);
                               });
     }
-    __syncthreads();
   }
 
   // O^T accumulators: lane (ln, h) holds columns 32mt + 8a + 4h + b of row t
