@@ -294,12 +294,6 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
     }
     __syncthreads();
   }
-  auto tval = [&](int i, int j) -> float {
-    const float sij = S[i * D + j];
-    if (i < j) return beta * sij;
-    if (i == j) return F32 ? half_beta * sij : half_beta * sij - sdb[i];
-    return 0.f;
-  };
   // float16 parts: scale by 2^-e so that the largest |T'_ij| lies in [2^14, 2^15).
   // One pass over Sigma gives that maximum and, for the bound G below, the
   // absolute column sums of sym(T'_c) (Sigma is symmetric, so column sums
@@ -313,12 +307,22 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
     float mx = 0.f;
     {
       const int j = tid % D, r = tid / D;
+      const float dj = sdb[j];
       float cs = 0.f;
-#pragma unroll 16
-      for (int i = r * (D / QR); i < (r + 1) * (D / QR); ++i) {
-        const float sij = S[i * D + j];
-        cs += i == j ? fabsf(half_beta * sij - sdb[j]) : fabsf(half_beta * sij);
-        if (i <= j) mx = fmaxf(mx, fabsf(i < j ? beta * sij : half_beta * sij - sdb[i]));
+      // sixteen loads go out before any is used, and the sums take selects,
+      // not branches (a branch per element would make every load wait alone)
+      for (int i0 = r * (D / QR); i0 < (r + 1) * (D / QR); i0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = S[(i0 + u) * D + j];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int i = i0 + u;
+          const float diag = fabsf(half_beta * v[u] - dj);
+          cs += i == j ? diag : fabsf(half_beta * v[u]);
+          const float t = i < j ? fabsf(beta * v[u]) : diag;
+          mx = i <= j ? fmaxf(mx, t) : mx;
+        }
       }
       colsum[tid] = cs;
     }
@@ -339,9 +343,17 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
     while ((mt + 1) * (mt + 2) <= f) ++mt;
     const int s = f - mt * (mt + 1);
     const int j = 32 * mt + m;
-    float x[8];
+    // the eight loads go out together; tval's cases are then selects
+    float raw[8], x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = tval(frag_k(s, h, e), j);
+    for (int e = 0; e < 8; ++e) raw[e] = S[frag_k(s, h, e) * D + j];
+    const float dj = F32 ? 0.f : sdb[j];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = frag_k(s, h, e);
+      const float diag = half_beta * raw[e] - dj;
+      x[e] = i < j ? beta * raw[e] : (i == j ? diag : 0.f);
+    }
     if constexpr (F32) {
       floatx8 v;
 #pragma unroll
