@@ -162,14 +162,20 @@ def test_long_prefill_1m_fullsize():
 
 
 @pytest.mark.timeout(900)
-def test_long_prefill_1m_hier_fullsize():
+@pytest.mark.parametrize("keys", ["standard", "topical"])
+def test_long_prefill_1m_hier_fullsize(keys):
     """Exact hierarchical prefill routing (groups of 16 blocks) at 1M tokens:
     every row equals the flat router's exact pass (the same arithmetic on
     the blocks it scores), and sampled rows equal the oracle's flat top-k
-    under R1; the share of (row, block) scores computed is reported."""
+    under R1; the share of (row, block) scores computed is reported.
+    "topical": clustered keys and topical queries (no plants), where whole
+    groups are pruned -- the share must then stay well below one."""
     wl = CONFIGS["long_prefill_1m"]
     m = 16
-    say("case long_prefill_1m hierarchical routing: generating on the GPU")
+    if keys == "topical":
+        wl = wl.replace(center_std=0.05, noise_std=0.05, group_std=1.0, group_blocks=m, plants=0,
+                        query_topic=0.5, topic_span=1024)
+    say(f"case long_prefill_1m hierarchical routing, {keys} inputs: generating on the GPU")
     data = make_prefill(wl, seed=0, device=DEV)
     Q, K = data["Q"], data["K"]
     del data["V"]
@@ -185,8 +191,10 @@ def test_long_prefill_1m_hier_fullsize():
     n, B, g = wl.seq_len, wl.block, wl.group
     nb = n // B
     routable = (B * nb * (nb - 1) // 2 + (n - nb * B + 1) * nb) * g * wl.n_kv_heads
-    say(f"  (row, block) scores computed: {ev.long().sum().item() * 512 / routable:.3f} of the "
-        "routable pairs")
+    frac = ev.long().sum().item() * 512 / routable
+    say(f"  (row, block) scores computed: {frac:.3f} of the routable pairs")
+    if keys == "topical":
+        assert frac < 0.5, f"topical inputs: {frac:.3f} of the pairs scored, expected pruning"
     idx_h = idx.cpu().numpy()
     del flat, idx
     p = O.Params(wl.block, wl.top_k, wl.window, wl.beta, wl.scale)
