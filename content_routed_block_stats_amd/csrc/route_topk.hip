@@ -543,8 +543,8 @@ __device__ __forceinline__ void load_q_tiles(typename QFrag<F32>::T (&bq)[2][D /
 // hi + lo (float16) or float32 contraction against every routable block of
 // each row.  Dense mode: the workgroup owns 512 consecutive rows of its
 // (sequence, KV head).  List mode (rows != nullptr): it owns positions
-// [512 j, 512 j + 512) of the KV head's ascending row list (j its tile);
-// workgroups past the end of the list exit.
+// [512 j, 512 j + 512) of the KV head's row list (j its tile), in any row
+// order; workgroups past the end of the list exit.
 template <bool F32, int D, int KMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const typename QFrag<F32>::In* __restrict__ Q, const uint8_t* __restrict__ prep,
@@ -590,9 +590,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int64_t my_rho = my_valid ? row_at(my_p) : 0;
   const int64_t my_t = my_valid ? split_rho(my_rho, g).t : 0;
   const int64_t my_C = my_valid ? min(nb, (my_t + 1) / B) : 0;
-  // positions are in ascending row order: the last valid one has the largest t
-  const int64_t t_max = min(n - 1, row_at(min(list_len, rho0 + kRouteRows) - 1) / g);
-  const int64_t C_wg = min(nb, (t_max + 1) / B);
+  // the workgroup's routable range: in dense mode its last row's; a list
+  // need not be in row order (the hierarchical visit's is not), so there the
+  // largest over its rows
+  int64_t C_wg;
+  if (!listed) {
+    const int64_t t_max = min(n - 1, (rho0 + kRouteRows - 1) / g);
+    C_wg = min(nb, (t_max + 1) / B);
+  } else {
+    __shared__ int32_t cw[kRouteThreads / 64];
+    int c = int(my_C);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c = max(c, __shfl_xor(c, o, 64));
+    if (lane == 0) cw[wave] = c;
+    __syncthreads();
+    C_wg = 0;
+#pragma unroll
+    for (int w = 0; w < kRouteThreads / 64; ++w) C_wg = max(C_wg, int64_t(cw[w]));
+  }
 
   float ls[KMAX + 1];
   int li[KMAX + 1];
@@ -836,6 +851,155 @@ __device__ __forceinline__ float key_score(uint32_t key) {
   return __uint_as_float(u);
 }
 
+// The single pass's way out for one lane's row, from its running top-NL
+// packed keys (shared by the flat single pass and the hierarchical visit):
+// certification against the rigorous error bound e of the hi-part scores,
+// then either the row's selection (certified), a rescore record of its band
+// (block-major exact scores, then the final top-k), a full row (exact scores
+// on every routable block) or, past the caps, the exact pass.  nq2 is the
+// row's ||q||^2 in scaled units (float16 values, float32 sum, times
+// 1 + 2^-16); every wave of the workgroup calls it (ballots and barriers).
+template <int KMAX>
+__device__ __forceinline__ void certify_emit(
+    const uint32_t (&lk)[KMAX + 1 + kExtra], float nq2, float qsc, uint32_t mask,
+    const uint32_t* __restrict__ bounds, int64_t bkv, int64_t tile, int64_t n_tiles,
+    bool my_valid, int64_t my_rho, int64_t my_t, int64_t my_C, int* wave_rec, int* wave_unc,
+    int tid, int wave, int lane, int32_t* __restrict__ idx, int32_t* __restrict__ tcnt,
+    int32_t* __restrict__ trows, int32_t* __restrict__ rcnt, int4* __restrict__ rmeta,
+    int32_t* __restrict__ rblk, int32_t* __restrict__ rrank, int32_t* __restrict__ pcnt,
+    int32_t* __restrict__ fcnt, int32_t* __restrict__ frow, int32_t* __restrict__ fpos, int64_t n,
+    int g, int hq, int hkv, int64_t nb, int k) {
+  constexpr int NL = KMAX + 1 + kExtra;
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  // Rows with at most k routable blocks keep them all.  Otherwise: a packed
+  // key stands for every score with the same top bits (its bucket), whose
+  // ends are the key with its low bits cleared and set; e bounds |approximate
+  // - exact| for every block.  A listed block whose bucket floor minus e
+  // exceeds the ceiling plus e of the (k+1)-th key's bucket is in the exact
+  // top-k (only blocks of the approximate top-k can beat it); a block whose
+  // ceiling plus e is below the floor minus e of the k-th key's bucket is out
+  // (k blocks beat it).  Keys are sorted, so the in-blocks are list positions
+  // [0, p0), the out-blocks [p1, NL) and every unlisted block when p1 < NL.
+  // p0 == k certifies the row.  Otherwise the blocks at [p0, p1) get exact
+  // scores, block-major (a record of the row); when p1 == NL and blocks past
+  // the list may be in, or the tile's records are full, every block of the
+  // row does (a full row); rows with a non-finite key, and full rows past
+  // the cap, go to the exact pass.
+  bool cert = true, ok = true, wide = false;
+  int p0 = 0, p1 = 0;
+  if (my_C > k) {
+    uint32_t kk = 0u, kk1 = 0u;
+#pragma unroll
+    for (int i = 0; i <= KMAX; ++i) {
+      if (i == k - 1) kk = lk[i];
+      if (i == k) kk1 = lk[i];
+    }
+    const float lam = __uint_as_float(bounds[bkv * 4 + 0]);
+    const float G = __uint_as_float(bounds[bkv * 4 + 1]);
+    const float nu = __uint_as_float(bounds[bkv * 4 + 2]);
+    const float dm = __uint_as_float(bounds[bkv * 4 + 3]);
+    // the hi part's rounding; float32 accumulation (and the diagonal shift's
+    // own float32 rounding, at most 2^-23 (|D| + |T'_ii|) per diagonal entry),
+    // the latter taken 1.25 times
+    const float e_hi = lam * nq2;
+    const float e_acc = 0x1p-17f * (G * nq2 + nu * qsc * sqrtf(nq2)) + 0x1p-22f * (dm + G) * nq2;
+    const float e = 1.25f * (e_hi + e_acc);
+    const float lo_k = key_score(kk & ~mask), hi_k1 = key_score(kk1 | mask);
+    ok = kk != 0u && kk1 != 0u && fabsf(lo_k) >= 0x1p-100f && fabsf(hi_k1) >= 0x1p-100f &&
+         e < __builtin_inff();
+    const float in_edge = hi_k1 + 2.f * e, out_edge = lo_k - 2.f * e;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float lo_i = key_score(lk[i] & ~mask), hi_i = key_score(lk[i] | mask);
+      const bool listed = lk[i] != 0u;
+      ok = ok && (!listed || (fabsf(lo_i) < __builtin_inff() && fabsf(hi_i) < __builtin_inff()));
+      p0 += (listed && lo_i > in_edge) ? 1 : 0;
+      p1 += (listed && hi_i >= out_edge) ? 1 : 0;
+    }
+    cert = ok && p0 == k;
+    wide = p1 == NL && my_C > NL;
+  }
+  // records first: rows with a band inside the list, in row order, up to
+  // kRecCap per tile (wave ballots; lane = row offset within the wave)
+  const bool want_rec = my_valid && !cert && ok && !wide;
+  const uint64_t bal_r = __ballot(want_rec);
+  if (lane == 0) wave_rec[wave] = __popcll(bal_r);
+  __syncthreads();
+  int rbase = 0, rtotal = 0;
+#pragma unroll
+  for (int w = 0; w < kRouteThreads / 64; ++w) {
+    rbase += w < wave ? wave_rec[w] : 0;
+    rtotal += wave_rec[w];
+  }
+  const int rslot = rbase + __popcll(bal_r & ((uint64_t(1) << lane) - 1u));
+  const bool rec = want_rec && rslot < kRecCap;
+  // then full rows, up to kFullCap per KV head
+  int fslot = kFullCap;
+  if (my_valid && !cert && ok && !rec) fslot = atomicAdd(&fcnt[bkv], 1);
+  const bool full = fslot < kFullCap;
+  if (full) {
+    frow[bkv * kFullCap + fslot] = int32_t(my_rho);
+    fpos[bkv * kFullCap + fslot] = int32_t(my_t);
+  }
+  // everything else uncertain -> this tile's list for the exact pass
+  const bool unc = my_valid && !cert && !rec && !full;
+  const uint64_t bal = __ballot(unc);
+  if (lane == 0) wave_unc[wave] = __popcll(bal);
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kRouteThreads / 64; ++w) {
+    base += w < wave ? wave_unc[w] : 0;
+    total += wave_unc[w];
+  }
+  const int64_t tix = bkv * n_tiles + tile;
+  if (unc) {
+    const int rank = __popcll(bal & ((uint64_t(1) << lane) - 1u));
+    trows[tix * kRouteRows + base + rank] = int32_t(my_rho);
+  }
+  if (tid == 0) {
+    tcnt[tix] = total;
+    rcnt[tix] = min(rtotal, kRecCap);
+  }
+  if (rec) {
+    // the record: (row, p0, p1), the first p1 blocks, and each in-band block's
+    // rank in its block's pair list
+    const int64_t r = tix * kRecCap + rslot;
+    rmeta[r] = int4{int32_t(my_rho), p0, p1, 0};
+    int32_t* rb = rblk + r * NL;
+    int32_t* rr = rrank + r * NL;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if (i < p1) {
+        const int32_t c = int32_t(mask - (lk[i] & mask));
+        rb[i] = c;
+        if (i >= p0) rr[i] = atomicAdd(&pcnt[bkv * nb + c], 1);
+      }
+    }
+  }
+  if (!my_valid || !cert || k == 0) return;
+  // certified: the blocks of the first min(k, C) keys, ascending, -1 padded
+  const int64_t orow = (b * hq + kv * g + split_rho(my_rho, g).jg) * n + my_t;
+  int32_t* out = idx + orow * k;
+  int cidx[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i)
+    cidx[i] = (i < my_C && lk[i] != 0u) ? int(mask - (lk[i] & mask)) : -1;
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    if (i < k) {
+      const unsigned key_i = unsigned(cidx[i]);
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) {
+          const unsigned key_j = unsigned(cidx[j]);
+          rank += (key_j < key_i || (key_j == key_i && j < i)) ? 1 : 0;
+        }
+      out[rank] = cidx[i];
+    }
+  }}
+
 template <int D, int KMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_fast_kernel(
     const bf16_t* __restrict__ Q, const uint8_t* __restrict__ prep,
@@ -1056,134 +1220,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_fast_kernel(
   const float nq0 = nq[0] + wave_shfl_xor(nq[0], 32);
   const float nq1 = nq[1] + wave_shfl_xor(nq[1], 32);
   const float nq2 = (h ? nq1 : nq0) * (1.f + 0x1p-16f);
-  // Rows with at most k routable blocks keep them all.  Otherwise: a packed
-  // key stands for every score with the same top bits (its bucket), whose
-  // ends are the key with its low bits cleared and set; e bounds |approximate
-  // - exact| for every block.  A listed block whose bucket floor minus e
-  // exceeds the ceiling plus e of the (k+1)-th key's bucket is in the exact
-  // top-k (only blocks of the approximate top-k can beat it); a block whose
-  // ceiling plus e is below the floor minus e of the k-th key's bucket is out
-  // (k blocks beat it).  Keys are sorted, so the in-blocks are list positions
-  // [0, p0), the out-blocks [p1, NL) and every unlisted block when p1 < NL.
-  // p0 == k certifies the row.  Otherwise the blocks at [p0, p1) get exact
-  // scores, block-major (a record of the row); when p1 == NL and blocks past
-  // the list may be in, or the tile's records are full, every block of the
-  // row does (a full row); rows with a non-finite key, and full rows past
-  // the cap, go to the exact pass.
-  bool cert = true, ok = true, wide = false;
-  int p0 = 0, p1 = 0;
-  if (my_C > k) {
-    uint32_t kk = 0u, kk1 = 0u;
-#pragma unroll
-    for (int i = 0; i <= KMAX; ++i) {
-      if (i == k - 1) kk = lk[i];
-      if (i == k) kk1 = lk[i];
-    }
-    const float lam = __uint_as_float(bounds[bkv * 4 + 0]);
-    const float G = __uint_as_float(bounds[bkv * 4 + 1]);
-    const float nu = __uint_as_float(bounds[bkv * 4 + 2]);
-    const float dm = __uint_as_float(bounds[bkv * 4 + 3]);
-    // the hi part's rounding; float32 accumulation (and the diagonal shift's
-    // own float32 rounding, at most 2^-23 (|D| + |T'_ii|) per diagonal entry),
-    // the latter taken 1.25 times
-    const float e_hi = lam * nq2;
-    const float e_acc = 0x1p-17f * (G * nq2 + nu * qsc * sqrtf(nq2)) + 0x1p-22f * (dm + G) * nq2;
-    const float e = 1.25f * (e_hi + e_acc);
-    const float lo_k = key_score(kk & ~mask), hi_k1 = key_score(kk1 | mask);
-    ok = kk != 0u && kk1 != 0u && fabsf(lo_k) >= 0x1p-100f && fabsf(hi_k1) >= 0x1p-100f &&
-         e < __builtin_inff();
-    const float in_edge = hi_k1 + 2.f * e, out_edge = lo_k - 2.f * e;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const float lo_i = key_score(lk[i] & ~mask), hi_i = key_score(lk[i] | mask);
-      const bool listed = lk[i] != 0u;
-      ok = ok && (!listed || (fabsf(lo_i) < __builtin_inff() && fabsf(hi_i) < __builtin_inff()));
-      p0 += (listed && lo_i > in_edge) ? 1 : 0;
-      p1 += (listed && hi_i >= out_edge) ? 1 : 0;
-    }
-    cert = ok && p0 == k;
-    wide = p1 == NL && my_C > NL;
-  }
-  // records first: rows with a band inside the list, in row order, up to
-  // kRecCap per tile (wave ballots; lane = row offset within the wave)
-  const bool want_rec = my_valid && !cert && ok && !wide;
-  const uint64_t bal_r = __ballot(want_rec);
-  if (lane == 0) wave_rec[wave] = __popcll(bal_r);
-  __syncthreads();
-  int rbase = 0, rtotal = 0;
-#pragma unroll
-  for (int w = 0; w < kRouteThreads / 64; ++w) {
-    rbase += w < wave ? wave_rec[w] : 0;
-    rtotal += wave_rec[w];
-  }
-  const int rslot = rbase + __popcll(bal_r & ((uint64_t(1) << lane) - 1u));
-  const bool rec = want_rec && rslot < kRecCap;
-  // then full rows, up to kFullCap per KV head
-  int fslot = kFullCap;
-  if (my_valid && !cert && ok && !rec) fslot = atomicAdd(&fcnt[bkv], 1);
-  const bool full = fslot < kFullCap;
-  if (full) {
-    frow[bkv * kFullCap + fslot] = int32_t(my_rho);
-    fpos[bkv * kFullCap + fslot] = int32_t(my_t);
-  }
-  // everything else uncertain -> this tile's list for the exact pass
-  const bool unc = my_valid && !cert && !rec && !full;
-  const uint64_t bal = __ballot(unc);
-  if (lane == 0) wave_unc[wave] = __popcll(bal);
-  __syncthreads();
-  int base = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kRouteThreads / 64; ++w) {
-    base += w < wave ? wave_unc[w] : 0;
-    total += wave_unc[w];
-  }
-  const int64_t tix = bkv * n_tiles + tile;
-  if (unc) {
-    const int rank = __popcll(bal & ((uint64_t(1) << lane) - 1u));
-    trows[tix * kRouteRows + base + rank] = int32_t(my_rho);
-  }
-  if (tid == 0) {
-    tcnt[tix] = total;
-    rcnt[tix] = min(rtotal, kRecCap);
-  }
-  if (rec) {
-    // the record: (row, p0, p1), the first p1 blocks, and each in-band block's
-    // rank in its block's pair list
-    const int64_t r = tix * kRecCap + rslot;
-    rmeta[r] = int4{int32_t(my_rho), p0, p1, 0};
-    int32_t* rb = rblk + r * NL;
-    int32_t* rr = rrank + r * NL;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      if (i < p1) {
-        const int32_t c = int32_t(mask - (lk[i] & mask));
-        rb[i] = c;
-        if (i >= p0) rr[i] = atomicAdd(&pcnt[bkv * nb + c], 1);
-      }
-    }
-  }
-  if (!my_valid || !cert || k == 0) return;
-  // certified: the blocks of the first min(k, C) keys, ascending, -1 padded
-  const int64_t orow = (b * hq + kv * g + split_rho(my_rho, g).jg) * n + my_t;
-  int32_t* out = idx + orow * k;
-  int cidx[KMAX];
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i)
-    cidx[i] = (i < my_C && lk[i] != 0u) ? int(mask - (lk[i] & mask)) : -1;
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) {
-    if (i < k) {
-      const unsigned key_i = unsigned(cidx[i]);
-      int rank = 0;
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (j < k) {
-          const unsigned key_j = unsigned(cidx[j]);
-          rank += (key_j < key_i || (key_j == key_i && j < i)) ? 1 : 0;
-        }
-      out[rank] = cidx[i];
-    }
-  }
+
+  certify_emit<KMAX>(lk, nq2, qsc, mask, bounds, bkv, tile, n_tiles, my_valid, my_rho, my_t, my_C,
+                     wave_rec, wave_unc, tid, wave, lane, idx, tcnt, trows, rcnt, rmeta, rblk, rrank,
+                     pcnt, fcnt, frow, fpos, n, g, hq, hkv, nb, k);
+
 }
 
 // Exclusive prefix of the per-tile uncertain counts of one (sequence, KV
@@ -1489,6 +1530,54 @@ __global__ __launch_bounds__(kRecCap) void route_finalize_kernel(
   for (int i = count; i < k; ++i) out[i] = -1;
 }
 
+// Before the single pass (or the hierarchical visit): the counts its rows
+// add to start at zero, and every full-row slot at position -1 (no blocks).
+void route_resolve_clear(const Shape& s, const RouteWs& w, int64_t n_bkv, hipStream_t st) {
+  const int64_t pairs = n_bkv * s.nb;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((pairs + 255) / 256, 1024))),
+                     dim3(256), 0, st, w.pcnt, pairs, 0);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, w.fcnt, n_bkv, 0);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((n_bkv * kFullCap + 255) / 256, 1024))),
+                     dim3(256), 0, st, w.fpos, n_bkv * kFullCap, -1);
+}
+
+// After the single pass (or the hierarchical visit), which certified what it
+// could and left records, full rows and uncertain rows in the workspace: the
+// exact selection of every row that is left.
+template <int D, int KMAX>
+hipError_t route_resolve(const Shape& s, const void* Q, const RouteWs& w, int32_t* idx,
+                         int64_t n_tiles, int64_t n_bkv, hipStream_t st) {
+  const unsigned grid = unsigned(n_tiles * n_bkv);
+  const int L = route_list_len(s.k);
+  // rows the records could not take: the exact pass over the compacted list
+  hipLaunchKernelGGL(route_scan_kernel, dim3(unsigned(n_bkv)), dim3(1024), 0, st, w.tcnt, w.toff,
+                     w.dcnt, n_tiles);
+  hipLaunchKernelGGL(route_gather_kernel, dim3(grid), dim3(64), 0, st, w.tcnt, w.toff, w.trows,
+                     w.drows, n_tiles);
+  hipLaunchKernelGGL((route_topk_kernel<false, D, KMAX>), dim3(grid), dim3(kRouteThreads), 0,
+                     st, static_cast<const bf16_t*>(Q), w.img, w.qmax, w.dbar, w.drows, w.dcnt,
+                     idx, nullptr, s.n, s.g, s.hq, s.hkv, s.B, s.nb, s.k, n_tiles, n_bkv);
+  // the records: block-major pair lists, exact band scores, final top-k
+  hipLaunchKernelGGL(route_scan_kernel, dim3(unsigned(n_bkv)), dim3(1024), 0, st, w.pcnt, w.poff,
+                     w.pscratch, s.nb);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(grid), dim3(kRecCap), 0, st, w.rcnt, w.rmeta,
+                     w.rblk, w.rrank, w.poff, w.pent, s.nb, n_tiles, L);
+  hipLaunchKernelGGL((route_rescore_kernel<D>), dim3(unsigned(s.nb), unsigned(n_bkv)),
+                     dim3(kRescoreThreads), 0, st, static_cast<const bf16_t*>(Q), w.img, w.qmax,
+                     w.pcnt, w.poff, w.pent, w.rmeta, w.rscore, w.fcnt, w.frow, w.fpos, w.fscore,
+                     s.n, s.g, s.hq, s.hkv, s.B, s.nb, n_tiles, L);
+  hipLaunchKernelGGL((route_finalize_kernel<KMAX>), dim3(grid), dim3(kRecCap), 0, st, w.rcnt,
+                     w.rmeta, w.rblk, w.rscore, idx, s.n, s.g, s.hq, s.hkv, s.k, n_tiles);
+  // the full rows: the wave top-k over each one's scores (unused slots have
+  // position -1, hence no blocks), then out to idx
+  hipError_t e = launch_decode_topk(w.fscore, w.fpos, w.fidx, s.k, s.nb, 1, s.B,
+                                    n_bkv * kFullCap, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_full_out_kernel, dim3(unsigned(n_bkv)), dim3(256), 0, st, w.fcnt,
+                     w.frow, w.fidx, idx, s.n, s.g, s.hq, s.hkv, s.k);
+  return hipGetLastError();
+}
+
 template <bool F32, int D, int KMAX>
 hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const float* sigma,
                           int32_t* idx, float* kth, void* ws, hipStream_t st) {
@@ -1526,43 +1615,13 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
     return hipGetLastError();
   }
   if constexpr (!F32) {
-    const int L = route_list_len(s.k);
-    const int64_t pairs = n_bkv * s.nb;
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((pairs + 255) / 256, 1024))),
-                       dim3(256), 0, st, w.pcnt, pairs, 0);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, w.fcnt, n_bkv, 0);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((n_bkv * kFullCap + 255) / 256, 1024))),
-                       dim3(256), 0, st, w.fpos, n_bkv * kFullCap, -1);
+    route_resolve_clear(s, w, n_bkv, st);
     hipLaunchKernelGGL((route_fast_kernel<D, KMAX>), dim3(grid), dim3(kRouteThreads), 0, st,
                        static_cast<const bf16_t*>(Q), w.img, w.qmax, w.bounds, idx, w.tcnt, w.trows,
                        w.rcnt, w.rmeta, w.rblk, w.rrank, w.pcnt, w.fcnt, w.frow, w.fpos, s.n, s.g,
                        s.hq, s.hkv, s.B, s.nb, s.k, key_bits, n_tiles, n_bkv);
-    // rows the records could not take: the exact pass over the compacted list
-    hipLaunchKernelGGL(route_scan_kernel, dim3(unsigned(n_bkv)), dim3(1024), 0, st, w.tcnt, w.toff,
-                       w.dcnt, n_tiles);
-    hipLaunchKernelGGL(route_gather_kernel, dim3(grid), dim3(64), 0, st, w.tcnt, w.toff, w.trows,
-                       w.drows, n_tiles);
-    hipLaunchKernelGGL((route_topk_kernel<false, D, KMAX>), dim3(grid), dim3(kRouteThreads), 0,
-                       st, static_cast<const bf16_t*>(Q), w.img, w.qmax, w.dbar, w.drows, w.dcnt,
-                       idx, nullptr, s.n, s.g, s.hq, s.hkv, s.B, s.nb, s.k, n_tiles, n_bkv);
-    // the records: block-major pair lists, exact band scores, final top-k
-    hipLaunchKernelGGL(route_scan_kernel, dim3(unsigned(n_bkv)), dim3(1024), 0, st, w.pcnt, w.poff,
-                       w.pscratch, s.nb);
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(grid), dim3(kRecCap), 0, st, w.rcnt, w.rmeta,
-                       w.rblk, w.rrank, w.poff, w.pent, s.nb, n_tiles, L);
-    hipLaunchKernelGGL((route_rescore_kernel<D>), dim3(unsigned(s.nb), unsigned(n_bkv)),
-                       dim3(kRescoreThreads), 0, st, static_cast<const bf16_t*>(Q), w.img, w.qmax,
-                       w.pcnt, w.poff, w.pent, w.rmeta, w.rscore, w.fcnt, w.frow, w.fpos, w.fscore,
-                       s.n, s.g, s.hq, s.hkv, s.B, s.nb, n_tiles, L);
-    hipLaunchKernelGGL((route_finalize_kernel<KMAX>), dim3(grid), dim3(kRecCap), 0, st, w.rcnt,
-                       w.rmeta, w.rblk, w.rscore, idx, s.n, s.g, s.hq, s.hkv, s.k, n_tiles);
-    // the full rows: the wave top-k over each one's scores (unused slots have
-    // position -1, hence no blocks), then out to idx
-    hipError_t e = launch_decode_topk(w.fscore, w.fpos, w.fidx, s.k, s.nb, 1, s.B,
-                                      n_bkv * kFullCap, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(route_full_out_kernel, dim3(unsigned(n_bkv)), dim3(256), 0, st, w.fcnt,
-                       w.frow, w.fidx, idx, s.n, s.g, s.hq, s.hkv, s.k);
+    if (hipError_t e = route_resolve<D, KMAX>(s, Q, w, idx, n_tiles, n_bkv, st); e != hipSuccess)
+      return e;
   }
   return hipGetLastError();
 }
@@ -1621,9 +1680,11 @@ __host__ __device__ inline int64_t hier_chunks(int64_t n_tiles) {
 int64_t hier_groups(const Shape& s, int m) { return (s.nb + m - 1) / m; }
 
 struct HierWs {
-  uint8_t* img;      // block images [b*hkv][nb]
+  RouteWs rw;        // the flat router's workspace: block images, max|q|, the
+                     // blocks' error-bound constants, records and full rows
+  uint8_t* img;      // = rw.img: block images [b*hkv][nb]
   uint8_t* gimg;     // group images [b*hkv][G]
-  uint32_t* qmax;    // [b*hkv], then bounds [b*hkv][4] (unused here)
+  uint32_t* qmax;    // = rw.qmax: [b*hkv], then the blocks' bounds [b*hkv][4]
   uint32_t* gbounds; // [b*hkv][4]: the group images' error-bound constants
   float* dbar;       // [b*hkv][d]
   float* gdbar;      // [b*hkv][d]
@@ -1642,17 +1703,15 @@ HierWs hier_ws_layout(const Shape& s, int m, void* base) {
   const size_t n_bkv = size_t(s.b) * s.hkv, nt = size_t(route_tiles(s));
   const size_t rows = size_t(s.n) * size_t(s.g);
   const size_t G = size_t(hier_groups(s, m));
-  size_t off = 0;
+  w.rw = route_ws_layout(s, base);
+  size_t off = w.rw.bytes;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off += align_up(bytes);
     return o;
   };
-  const size_t o_img = take(n_bkv * size_t(s.nb) * per + 1024);
   const size_t o_gimg = take(n_bkv * G * per + 1024);
-  const size_t o_q = take(n_bkv * 4 * 5);
   const size_t o_gb = take(n_bkv * 4 * 4);
-  const size_t o_db = take(n_bkv * size_t(s.d) * 4);
   const size_t o_gdb = take(n_bkv * size_t(s.d) * 4);
   const size_t o_ub = take(n_bkv * rows * G * 4);
   const size_t o_best = take(n_bkv * rows * 4);
@@ -1664,11 +1723,11 @@ HierWs hier_ws_layout(const Shape& s, int m, void* base) {
   w.bytes = off;
   if (base != nullptr) {
     uint8_t* p = static_cast<uint8_t*>(base);
-    w.img = p + o_img;
+    w.img = w.rw.img;
     w.gimg = p + o_gimg;
-    w.qmax = reinterpret_cast<uint32_t*>(p + o_q);
+    w.qmax = w.rw.qmax;
     w.gbounds = reinterpret_cast<uint32_t*>(p + o_gb);
-    w.dbar = reinterpret_cast<float*>(p + o_db);
+    w.dbar = w.rw.dbar;
     w.gdbar = reinterpret_cast<float*>(p + o_gdb);
     w.ub = reinterpret_cast<float*>(p + o_ub);
     w.best = reinterpret_cast<int32_t*>(p + o_best);
@@ -2006,6 +2065,171 @@ __global__ __launch_bounds__(kRouteThreads) void hier_visit_kernel(
   }
 }
 
+// Workgroup (listed tile, KV head): the visit with the single pass's
+// arithmetic.  Blocks of the needed groups are scored with the hi part alone
+// (hilo_score<D, false>) into each row's running top-NL packed keys, exactly
+// as the single pass keeps them; a group is skipped when, for every row of
+// the tile, its bound is below the row's running k-th key's bucket floor
+// minus e (the k listed blocks' exact scores are all above that, so no block
+// of the group can displace them).  The rows then leave through the single
+// pass's certification (certify_emit): certified rows write their selection,
+// the rest become rescore records, full rows or exact-pass rows, resolved
+// afterwards by the flat router's kernels -- so every row gets the exact
+// pass's selection, as with the flat router.
+template <int D, int KMAX>
+__global__ __launch_bounds__(kRouteThreads) void hier_visit_fast_kernel(
+    const bf16_t* __restrict__ Q, const uint8_t* __restrict__ img,
+    const uint32_t* __restrict__ qmax, const uint32_t* __restrict__ bounds,
+    const float* __restrict__ ub, const int32_t* __restrict__ list, int32_t* __restrict__ idx,
+    int32_t* __restrict__ evaluated, int32_t* __restrict__ tcnt, int32_t* __restrict__ trows,
+    int32_t* __restrict__ rcnt, int4* __restrict__ rmeta, int32_t* __restrict__ rblk,
+    int32_t* __restrict__ rrank, int32_t* __restrict__ pcnt, int32_t* __restrict__ fcnt,
+    int32_t* __restrict__ frow, int32_t* __restrict__ fpos, int64_t n, int g, int hq, int hkv,
+    int B, int64_t nb, int m, int64_t G, int k, int key_bits, int64_t n_tiles, int64_t n_bkv) {
+  using Lay = RouteLayout<D>;
+  constexpr int NS = D / 16, BYTES = Lay::BLOCK_BYTES;
+  constexpr int NL = KMAX + 1 + kExtra;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Lay::LDS_BYTES];
+  __shared__ uint64_t order[kHierSortMax];
+  __shared__ uint32_t gmax[kHierSortMax];
+  __shared__ int32_t cmax[kRouteThreads / 64];
+  __shared__ int wave_unc[kRouteThreads / 64];
+  __shared__ int wave_rec[kRouteThreads / 64];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, h = lane / 32;
+  const int64_t wid = blockIdx.x;
+  const int64_t bkv = wid % n_bkv;
+  const int64_t tile = wid / n_bkv;
+  const int64_t b = bkv / hkv, kv = bkv % hkv;
+  const int64_t rows_total = n * g;
+  const int64_t p0_tile = tile * kRouteRows;
+  const int32_t* lst = list + bkv * rows_total;
+  const uint32_t mask = (1u << key_bits) - 1u;
+  const float qsc = ldexpf(1.f, -query_exponent(qmax[bkv]));
+  f16x8 bq[2][NS];
+  {
+    const int64_t p0 = p0_tile + 64 * wave + ln, p1 = p0 + 32;
+    const bool valid[2] = {p0 < rows_total, p1 < rows_total};
+    const int64_t rho_of[2] = {valid[0] ? int64_t(lst[p0]) : 0, valid[1] ? int64_t(lst[p1]) : 0};
+    load_q_tiles<false, D>(bq, Q, rho_of, valid, b, kv, g, hq, n, h, qsc);
+  }
+  const int64_t my_p = p0_tile + 64 * wave + 32 * h + ln;
+  const bool my_valid = my_p < rows_total;
+  const int64_t my_rho = my_valid ? int64_t(lst[my_p]) : 0;
+  const int64_t my_t = my_valid ? split_rho(my_rho, g).t : 0;
+  const int64_t my_C = my_valid ? min(nb, (my_t + 1) / B) : 0;
+  const float* my_ub = ub + (bkv * rows_total + my_rho) * G;
+  // the row's ||q||^2 (as the certification takes it) and its score error bound
+  const float nq2 = row_norm2<D>(bq, h) * (1.f + 0x1p-16f);
+  float e_row;
+  {
+    const float lam = __uint_as_float(bounds[bkv * 4 + 0]);
+    const float Gs = __uint_as_float(bounds[bkv * 4 + 1]);
+    const float nu = __uint_as_float(bounds[bkv * 4 + 2]);
+    const float dm = __uint_as_float(bounds[bkv * 4 + 3]);
+    e_row = 1.25f * (lam * nq2 + 0x1p-17f * (Gs * nq2 + nu * qsc * sqrtf(nq2)) +
+                     0x1p-22f * (dm + Gs) * nq2);
+  }
+  // the tile's routable blocks (largest over its rows) and groups
+  {
+    int c = int(my_C);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c = max(c, __shfl_xor(c, o, 64));
+    if (lane == 0) cmax[wave] = c;
+  }
+  for (int i = tid; i < kHierSortMax; i += kRouteThreads) gmax[i] = 0u;
+  __syncthreads();
+  int64_t C_wg = 0;
+#pragma unroll
+  for (int w = 0; w < kRouteThreads / 64; ++w) C_wg = max(C_wg, int64_t(cmax[w]));
+  const int G_wg = int((C_wg + m - 1) / m);
+  auto bound = [&](int gi) {
+    return (my_valid && int64_t(gi) * m < my_C) ? my_ub[gi] : -__builtin_inff();
+  };
+  for (int gi = 0; gi < G_wg; ++gi) {
+    const float u = bound(gi);
+    const uint32_t bits = __float_as_uint(u);
+    uint32_t o = bits ^ (uint32_t(int32_t(bits) >> 31) | 0x80000000u);
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) o = max(o, uint32_t(__shfl_xor(int(o), sh, 64)));
+    if (lane == 0) atomicMax(&gmax[gi], o);
+  }
+  __syncthreads();
+  // groups in decreasing order of that bound (lower group first among equal
+  // bounds): a descending bitonic sort of (bound bits, ~group)
+  int P = 1;
+  while (P < G_wg) P <<= 1;
+  for (int i = tid; i < P; i += kRouteThreads)
+    order[i] = i < G_wg ? (uint64_t(gmax[i]) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(i)) : 0;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1)
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P; i += kRouteThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t a = order[i], c = order[j];
+          if (desc ? a < c : a > c) {
+            order[i] = c;
+            order[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+  uint32_t lk[NL];   // running top-NL packed keys, descending (as the single pass)
+#pragma unroll
+  for (int i = 0; i < NL; ++i) lk[i] = 0u;
+  // a lower bound on the exact k-th score of the blocks listed so far (-inf
+  // until k are listed; +inf for k = 0: nothing is needed)
+  auto kth_floor = [&]() {
+    uint32_t kk = 0u;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      if (i == k - 1) kk = lk[i];
+    if (k == 0) return __builtin_inff();
+    return kk == 0u ? -__builtin_inff() : key_score(kk & ~mask) - e_row;
+  };
+  int scored = 0;
+  const uint8_t* src = img + bkv * nb * int64_t(BYTES);
+  for (int j = 0; j < G_wg; ++j) {
+    const int gi = int(0xFFFFFFFFu - uint32_t(order[j] & 0xFFFFFFFFu));
+    const float u = bound(gi);
+    const bool need = __syncthreads_or(my_valid && !(u < kth_floor()));
+    if (!need) continue;
+    const int64_t c0 = int64_t(gi) * m, c1 = min(C_wg, c0 + m);
+    stage_image<D>(src + c0 * BYTES, lds, wave, lane, kRouteThreads / 64);
+    for (int64_t c = c0; c < c1; ++c) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();   // image c is in LDS; every wave is done with c - 1's buffer
+      if (c + 1 < c1)
+        stage_image<D>(src + (c + 1) * BYTES, lds + ((c + 1 - c0) & 1) * Lay::LDS_BYTES, wave,
+                       lane, kRouteThreads / 64);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)   // (q stays in float16 registers; see hier_ub_kernel)
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) asm volatile("" : "+v"(bq[nt][s2]));
+      const float a = hilo_score<D, false>(lds + ((c - c0) & 1) * Lay::LDS_BYTES, bq, lane);
+      const uint32_t bits = __float_as_uint(a);
+      const uint32_t o = bits ^ (uint32_t(int32_t(bits) >> 31) | 0x80000000u);
+      uint32_t key = (c < my_C && a == a) ? (o & ~mask) | (mask - uint32_t(c)) : 0u;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const uint32_t v = lk[i];
+        lk[i] = max(v, key);
+        key = min(v, key);
+      }
+    }
+    scored += int(c1 - c0);
+    __syncthreads();   // the last image's buffer is free before the next group stages
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (evaluated != nullptr && tid == 0) evaluated[bkv * n_tiles + tile] = scored;
+  certify_emit<KMAX>(lk, nq2, qsc, mask, bounds, bkv, tile, n_tiles, my_valid, my_rho, my_t, my_C,
+                     wave_rec, wave_unc, tid, wave, lane, idx, tcnt, trows, rcnt, rmeta, rblk, rrank,
+                     pcnt, fcnt, frow, fpos, n, g, hq, hkv, nb, k);
+}
+
 template <int D, int KMAX>
 hipError_t launch_hier_prefill_t(const Shape& s, const void* Q, const float* mu,
                                  const float* sigma, const float* gmu, const float* gS,
@@ -2052,6 +2276,20 @@ hipError_t launch_hier_prefill_t(const Shape& s, const void* Q, const float* mu,
                      w.gtot, G * hier_chunks(n_tiles) * kHierChunk);
   hipLaunchKernelGGL(hier_order_kernel, dim3(grid), dim3(kRouteThreads), 0, st, w.best, w.goff,
                      w.list, rows_total, G, n_tiles);
+  int key_bits = 1;
+  while ((int64_t(1) << key_bits) < s.nb) ++key_bits;
+  if (s.k > 0 && key_bits <= kMaxKeyBits && n_tiles * kRecCap <= (int64_t(1) << 26)) {
+    const RouteWs& rw = w.rw;
+    route_resolve_clear(s, rw, n_bkv, st);
+    hipLaunchKernelGGL((hier_visit_fast_kernel<D, KMAX>), dim3(grid), dim3(kRouteThreads), 0, st,
+                       static_cast<const bf16_t*>(Q), rw.img, rw.qmax, rw.bounds, w.ub, w.list,
+                       idx, evaluated, rw.tcnt, rw.trows, rw.rcnt, rw.rmeta, rw.rblk, rw.rrank,
+                       rw.pcnt, rw.fcnt, rw.frow, rw.fpos, s.n, s.g, s.hq, s.hkv, s.B, s.nb, m, G,
+                       s.k, key_bits, n_tiles, n_bkv);
+    return route_resolve<D, KMAX>(s, Q, rw, idx, n_tiles, n_bkv, st);
+  }
+  // (k = 0, or keys or records out of the single pass's range) every needed
+  // block scored exactly
   hipLaunchKernelGGL((hier_visit_kernel<D, KMAX>), dim3(grid), dim3(kRouteThreads), 0, st,
                      static_cast<const bf16_t*>(Q), w.img, w.qmax, w.ub, w.list, idx, evaluated,
                      s.n, s.g, s.hq, s.hkv, s.B, s.nb, m, G, s.k, n_tiles, n_bkv);
