@@ -1664,10 +1664,13 @@ hipError_t launch_route_d(const Shape& s, const void* Q, const float* mu, const 
 //    (ties keep row order); tiles of 512 consecutive list entries.
 //  * visit: per listed tile, the groups in decreasing order of the tile's
 //    largest bound; a group is scored -- each of its blocks against all the
-//    tile's rows, merged into each row's running top-k -- unless, for every
-//    row, its bound is strictly below the row's running k-th score.  Skipped
-//    blocks score below each row's k-th (ties included), so every row gets
-//    exactly the flat selection, with the exact pass's scores.
+//    tile's rows with the single pass's arithmetic, into each row's running
+//    packed keys -- unless, for every row, its bound is strictly below what
+//    the row's k listed blocks are known to score exactly.  The rows then
+//    leave through the single pass's certification and resolution, so every
+//    row gets exactly the flat selection.  (k = 0, or keys or records beyond
+//    the single pass's range: a visit that scores every needed block with
+//    the exact pass's arithmetic and prunes against the exact k-th score.)
 
 constexpr float kHierPrefillMargin = 1e-4f;
 constexpr int kHierSortMax = 4096;   // groups per (sequence, KV head) the visit orders
