@@ -328,6 +328,25 @@ def bench_decode(steps: int, warmup: int) -> dict:
     routable = int(((pos.long() + 1) // wl.block).clamp(max=mu.shape[2]).sum()) * wl.n_kv_heads
     scored = int(ev.long().sum())
     del data
+    # the same on clustered keys with a topical query (the query leans toward
+    # one earlier group; no plants): the case a tree router prunes
+    wt = wl.replace(center_std=0.05, noise_std=0.05, group_std=1.0, group_blocks=m, plants=0,
+                    query_topic=0.5, topic_span=1024)
+    dt_ = make_decode(wt, seed=0, device="cuda", capacity=cap)
+    mu_t, sg_t = ssa.ssa_block_stats(dt_["K_cache"], wt.block)
+    gs_t = ssa.ssa_group_stats(mu_t, sg_t, block_size=wt.block, group_blocks=m)
+    idx_t, ev_t = ssa.ssa_route_hier(dt_["q"], mu_t, sg_t, *gs_t, pos, block_size=wt.block,
+                                     group_blocks=m, top_k=wt.top_k, beta=wt.beta,
+                                     want_evaluated=True, workspace=hws)
+    e0.record()
+    for _ in range(steps):
+        ssa.ssa_route_hier(dt_["q"], mu_t, sg_t, *gs_t, pos, block_size=wt.block, group_blocks=m,
+                           top_k=wt.top_k, beta=wt.beta, idx=idx_t, workspace=hws)
+    e1.record()
+    torch.cuda.synchronize()
+    hier_t_ms = e0.elapsed_time(e1) / steps
+    scored_t = int(ev_t.long().sum())
+    del dt_, mu_t, sg_t, gs_t
     return {"workload": wl.name, "ms_per_step": round(ms, 4),
             "tokens_per_s": round(wl.batch / (ms * 1e-3), 1),
             "hbm_gbs_algorithmic": round((sig + gat) / (ms * 1e-3) / 1e9, 1),
@@ -339,7 +358,11 @@ def bench_decode(steps: int, warmup: int) -> dict:
             "hier_route": {"group_blocks": m, "ms": round(hier_ms, 4),
                            "group_stats_ms_once": round(gs_ms, 3),
                            "blocks_scored_frac": round(scored / max(1, routable), 4),
-                           "keys": "standard decode keys (no group structure)"}}
+                           "keys": "standard decode keys (no group structure)",
+                           "topical": {"ms": round(hier_t_ms, 4),
+                                       "blocks_scored_frac": round(scored_t / max(1, routable), 4),
+                                       "keys": "clustered keys, topical query (query_topic 0.5), "
+                                               "no plants"}}}
 
 
 def tempered_flops(wl) -> float:

@@ -246,9 +246,20 @@ def make_decode(wl: Workload, seed: int = 0, device="cpu", capacity: int | None 
     K = torch.zeros((b_, hkv, cap, d), dtype=dt, device=device)
     V = torch.zeros((b_, hkv, cap, d), dtype=dt, device=device)
     ledger: list[dict] = []
+    if wl.query_topic > 0 and wl.group_std <= 0:
+        raise ValueError("query topics lean toward key group centres: set group_std > 0")
+    g = wl.group
     for b in range(b_):
-        for h in range(hq):
-            q[b, h] = _randn((d,), device, seed, _TAG_QNEW, b, h).to(dt)
+        for kv in range(hkv):
+            qf = torch.stack([_randn((d,), device, seed, _TAG_QNEW, b, h)
+                              for h in range(kv * g, (kv + 1) * g)])
+            if wl.query_topic > 0:
+                # the query at t = L takes the topic of the segment holding L
+                gi = _topics(wl, seed, b, kv, L + 1)[L // wl.topic_span]
+                if gi >= 0:
+                    grp = _group_centres(wl, seed, b, kv, L + 1, device)[gi]
+                    qf += wl.query_topic * math.sqrt(d) * grp / torch.linalg.vector_norm(grp)
+            q[b, kv * g:(kv + 1) * g] = qf.to(dt)
         for kv in range(hkv):
             vals = _randn((L + 1, d), device, seed, _TAG_V, b, kv).to(dt)
             V[b, kv, :L] = vals[:L]

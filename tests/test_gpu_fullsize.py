@@ -324,15 +324,19 @@ def test_gqa_prefill_128k_tiles_fullsize():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("keys", ["standard", "clustered"])
+@pytest.mark.parametrize("keys", ["standard", "clustered", "topical"])
 def test_decode_256k_hier_fullsize(keys):
     """Exact hierarchical routing on the 32 x 256K decode caches (groups of 16
     blocks): every row's selection equals the flat decode router's up to
     near-ties, and sampled (sequence, KV head) pairs equal the oracle's flat
-    top-k; on clustered keys at most 60% of the blocks are scored."""
+    top-k; on clustered keys at most 60% of the blocks are scored, and with a
+    topical query (leaning toward one earlier group; no plants) at most 30%."""
     wl = CONFIGS["decode_256k"]
     if keys == "clustered":
         wl = wl.replace(center_std=0.05, noise_std=0.05, group_std=1.0, plants=2)
+    if keys == "topical":
+        wl = wl.replace(center_std=0.05, noise_std=0.05, group_std=1.0, plants=0, group_blocks=16,
+                        query_topic=0.5, topic_span=1024)
     L, m = wl.seq_len, 16
     say(f"case decode_256k hierarchical routing, {keys} keys: generating on the GPU")
     data = make_decode(wl, seed=0, device=DEV, capacity=L + 1)
@@ -359,6 +363,8 @@ def test_decode_256k_hier_fullsize(keys):
     assert np.all(ev_h <= nbc)
     if keys == "clustered":
         assert frac <= 0.6
+    if keys == "topical":
+        assert frac <= 0.3
     rng = np.random.default_rng(1)
     for b, kv in [(int(rng.integers(wl.batch)), int(rng.integers(wl.n_kv_heads))) for _ in range(2)]:
         muo, sgo = O.block_stats(O.as_f64(Kc[b, kv, :nbc * wl.block].cpu()), wl.block)

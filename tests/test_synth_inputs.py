@@ -94,3 +94,28 @@ def test_topical_queries():
         means = torch.stack([K[gi * m * B:(gi + 1) * m * B].mean(0) for gi in range(top_group + 1)])
         cos = (means @ v) / (means.norm(dim=1) * v.norm())
         assert cos.max() > 0.99
+
+
+def test_topical_decode_query():
+    """The decode query leans toward the topic of the segment holding t = L,
+    one direction for every q-head of a KV head; the cache is unchanged."""
+    base = CONFIGS["decode_256k"].replace(batch=2, seq_len=4096, block=64, plants=0,
+                                          center_std=0.05, noise_std=0.05, group_std=1.0,
+                                          group_blocks=4, topic_span=1024)
+    plain = make_decode(base, seed=2)
+    top = make_decode(base.replace(query_topic=0.5), seed=2)
+    assert torch.equal(plain["K_cache"], top["K_cache"]) and torch.equal(plain["V_cache"], top["V_cache"])
+    d, g = base.head_dim, base.group
+    shift = top["q"].float() - plain["q"].float()          # [b, hq, d]
+    for b in range(base.batch):
+        for kv in range(base.n_kv_heads):
+            s = shift[b, kv * g:(kv + 1) * g]
+            v = s[0]
+            assert abs(float(v.norm()) - 0.5 * np.sqrt(d)) < 0.05   # bf16 rounding of q
+            assert torch.allclose(s, v.expand_as(s), atol=0.05)
+            # toward a group whose blocks all end before t = L
+            K = top["K_cache"][b, kv].float()
+            m, B, L = base.group_blocks, base.block, base.seq_len
+            means = torch.stack([K[gi * m * B:(gi + 1) * m * B].mean(0) for gi in range(L // B // m)])
+            cos = (means @ v) / (means.norm(dim=1) * v.norm())
+            assert cos.max() > 0.99
