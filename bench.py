@@ -95,23 +95,28 @@ def kernel_source_digest(*names: str) -> str:
     return h.hexdigest()[:16]
 
 
-def counted_traffic(kernel: str, digest: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or None."""
+def counted_traffic(kernel: str, digest: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the summary is missing, was taken on another workload, or the kernel
+    source changed since."""
     path = os.path.join(PROFILES, f"{kernel}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("workload") != workload:
+        return None          # counters of another workload's shapes
     if rec.get("source_digest") != digest:
         return None          # the kernel changed since the counters were taken
     return rec.get("hbm_bytes_per_launch")
 
 
-def counted_mfma_busy(prefix: str, digest: str):
+def counted_mfma_busy(prefix: str, digest: str, workload: str):
     """Share of SIMD cycles with the matrix core busy, from the committed
-    rocprofv3 counter summary of the routing kernel, or None if it changed."""
+    rocprofv3 counter summary of the routing kernel (taken on the 128K GQA
+    workload), or None for another workload or if the kernel changed."""
     path = os.path.join(PROFILES, "gqa_prefill_128k_mfma_busy.json")
-    if not os.path.exists(path):
+    if workload != "gqa_prefill_128k" or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
@@ -353,7 +358,8 @@ def bench_decode(steps: int, warmup: int) -> dict:
             "frac_hbm": round((sig + gat) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_step": float(sig + gat),
             "traffic": counted_traffic("decode_step", kernel_source_digest("decode.hip",
-                                                                           "ssa_common.hpp")),
+                                                                           "ssa_common.hpp"),
+                                       wl.name),
             "steps": steps,
             "hier_route": {"group_blocks": m, "ms": round(hier_ms, 4),
                            "group_stats_ms_once": round(gs_ms, 3),
@@ -748,15 +754,15 @@ def main() -> int:
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "peak_onbox": peaks["mfma_bf16_tflops"],
                      "frac_onbox": round(achieved / peaks["mfma_bf16_tflops"], 4),
-                     "traffic": counted_traffic("route_topk", route_digest),
-                     "mfma_busy_counted": counted_mfma_busy("route_fast_kernel", route_digest),
+                     "traffic": counted_traffic("route_topk", route_digest, wl.name),
+                     "mfma_busy_counted": counted_mfma_busy("route_fast_kernel", route_digest, wl.name),
                      "algorithmic_flops_per_launch": rf},
         "roofline_gather": {"kernel": "sparse_attn_fwd", "bound": "hbm", "achieved": round(gbs, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4),
                             "peak_onbox": peaks["hbm_read_gbs"],
                             "frac_onbox": round(gbs / peaks["hbm_read_gbs"], 4),
-                            "traffic": counted_traffic("sparse_attn_fwd", attn_digest),
+                            "traffic": counted_traffic("sparse_attn_fwd", attn_digest, wl.name),
                             "bytes_basis": "design bytes (this design's reads and writes, "
                                            "fp16 partials included)",
                             "design_bytes_per_launch": gb,
@@ -778,7 +784,7 @@ def main() -> int:
                         "algorithmic_bytes_per_launch": stats_bytes(wl),
                         "gbs": round(stats_bytes(wl) / (t_stats * 1e-3) / 1e9, 1),
                         "traffic": counted_traffic("block_stats", kernel_source_digest(
-                            "block_stats.hip", "ssa_common.hpp"))},
+                            "block_stats.hip", "ssa_common.hpp"), wl.name)},
     }
     if not args.step_only:
         # the query-tile-shared variant: one selection per tile of B positions
@@ -831,7 +837,7 @@ def main() -> int:
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ta_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": counted_traffic("tile_attn", kernel_source_digest(
-                             "tile_attn.hip", "kv_chunks.hpp", "ssa_common.hpp")),
+                             "tile_attn.hip", "kv_chunks.hpp", "ssa_common.hpp"), wl.name),
                          "algorithmic_flops_per_launch": ta_fl},
             "steps": treps}
         del ws_rt, ws_ta, idx_t
@@ -863,7 +869,7 @@ def main() -> int:
                            "frac": round(bwd_fl / (t_bwd * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                            "algorithmic_flops_per_launch": bwd_fl, "reps": breps,
                            "traffic_dkv_kernel": counted_traffic("attn_bwd_dkv", kernel_source_digest(
-                               "attn_bwd.hip", "kv_chunks.hpp", "ssa_common.hpp"))}
+                               "attn_bwd.hip", "kv_chunks.hpp", "ssa_common.hpp"), wl.name)}
         del ws_b, dO
 
         # the exact tempered score (same workload and beta), outside the step
@@ -881,7 +887,8 @@ def main() -> int:
                                  "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                  "traffic": counted_traffic("tempered_route", kernel_source_digest(
-                                     "tempered_route.hip", "kv_chunks.hpp", "ssa_common.hpp")),
+                                     "tempered_route.hip", "kv_chunks.hpp", "ssa_common.hpp"),
+                                     wl.name),
                                  "algorithmic_flops_per_launch": tempered_flops(wl), "reps": reps}
     del O, lse, ws_a, ws_r
     if not args.no_decode:
