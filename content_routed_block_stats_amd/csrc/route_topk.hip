@@ -1015,7 +1015,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_fast_kernel(
   constexpr int MT = Lay::MT, NS = Lay::NS, BYTES = Lay::BLOCK_BYTES;
   constexpr int NL = KMAX + 1 + kExtra;                // list length (route_list_len)
   constexpr int NBUF = 3;                              // block images in flight
-  constexpr int R = (HL::DMA_ROWS + 7) / 8;            // copy instructions per wave per block
+  constexpr int NW = kRouteThreads / 64;
+  constexpr int R = (HL::DMA_ROWS + NW - 1) / NW;      // copy instructions per wave per block
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * HL::LDS_BYTES];
   __shared__ int wave_unc[kRouteThreads / 64];
   __shared__ int wave_rec[kRouteThreads / 64];
@@ -1062,11 +1063,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_fast_kernel(
   const uint8_t* src_base = prep + bkv * nb * int64_t(BYTES);
   const uint32_t lds_base =
       uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(lds)));
-  auto stage = [&](int64_t c, int buf) {
-    const uint8_t* src = src_base + c * BYTES;
+  // the wave index as a uniform (scalar) value: the copies' LDS rows are then
+  // scalar arithmetic, with no lane-to-scalar move per copy
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  auto stage = [&](int c, int buf) {
+    const uint8_t* src = src_base + uint64_t(uint32_t(c)) * BYTES;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int r = min(wave + 8 * i, HL::DMA_ROWS - 1);
+      const int r = min(swave + NW * i, HL::DMA_ROWS - 1);
       const int off = r < Lay::NF ? r * kFragBytes : Lay::MU_OFF;
       const uint8_t* g = src + off + lane * 16;
       const uint32_t l =
@@ -1083,9 +1087,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_fast_kernel(
           : "memory");
     }
   };
-  if (C_wg > 0) {
+  // (C_wg <= nb < 2^16: block indices fit 32 bits)
+  const int C_w = int(C_wg);
+  if (C_w > 0) {
     stage(0, 0);
-    stage(min(int64_t(1), C_wg - 1), 1);
+    stage(min(1, C_w - 1), 1);
   }
 
   // The exact pass's hand-scheduled sweep with the hi part only: chunk pairs
@@ -1102,7 +1108,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_fast_kernel(
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[st2][nt][j] = 0.f;
-  float pt[2] = {0.f, 0.f};
+  // the row-dot of each row tile in two partial sums (alternate terms): two
+  // dependent chains per tile instead of one, which the vector unit overlaps
+  // better with the matrix core; any order stays within the bound's float32
+  // accumulation term
+  float pt[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   uint32_t key_ins = 0u;
   auto read_frag = [&](const uint8_t* L, int mt, int gp, int k2) {
     return *reinterpret_cast<const QT*>(L + Lay::frag(mt, 2 * gp + k2) * 1024 + lane * 16);
@@ -1120,27 +1130,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_fast_kernel(
   };
   auto dot_item = [&](int set, int mt, int i) {
     const int nt = i / 16, j = i % 16, a = j / 4, bb = j % 4;
-    pt[nt] = fmaf(acc[set][nt][j], static_cast<float>(bq[nt][2 * mt + (a >> 1)][4 * (a & 1) + bb]),
-                  pt[nt]);
+    pt[nt][j & 1] = fmaf(acc[set][nt][j],
+                         static_cast<float>(bq[nt][2 * mt + (a >> 1)][4 * (a & 1) + bb]),
+                         pt[nt][j & 1]);
   };
   float blk_scale = 1.f;
   auto reduce = [&](int64_t cb) {
-    const float p0 = pt[0] + wave_shfl_xor(pt[0], 32);
-    const float p1 = pt[1] + wave_shfl_xor(pt[1], 32);
-    pt[0] = pt[1] = 0.f;
+    const float s0 = pt[0][0] + pt[0][1], s1 = pt[1][0] + pt[1][1];
+    const float p0 = s0 + wave_shfl_xor(s0, 32);
+    const float p1 = s1 + wave_shfl_xor(s1, 32);
+    pt[0][0] = pt[0][1] = pt[1][0] = pt[1][1] = 0.f;
     const float a = (h ? p1 : p0) * blk_scale;
     const uint32_t u = __float_as_uint(a);
     const uint32_t o = u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
     const uint32_t key = (o & ~mask) | (mask - uint32_t(cb));
     key_ins = (cb >= 0 && cb < my_C && a == a) ? key : 0u;
   };
+  // the smaller key first, so the larger can take the old slot's register
+  // (no copies of the list at the loop's back edge)
   auto insert_step = [&](int i) {
     const uint32_t v = lk[i];
+    const uint32_t lower = min(v, key_ins);
     lk[i] = max(v, key_ins);
-    key_ins = min(v, key_ins);
+    key_ins = lower;
   };
 
-  auto sweep = [&](int64_t c, const uint8_t* L) {
+  auto sweep = [&](int c, const uint8_t* L) {
     const float scale_c = *reinterpret_cast<const float*>(L + HL::SCALE_OFF);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -1191,16 +1206,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_fast_kernel(
     }
     blk_scale = scale_c;
   };
-  for (int64_t c = 0; c < C_wg; ++c) {
+  // ring positions of block c (read) and block c + 2 (staged), kept as counters
+  int rbuf = 0, sbuf = 2 % NBUF;
+  for (int c = 0; c < C_w; ++c) {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(R) : "memory");
-    stage(min(c + 2, C_wg - 1), int((c + 2) % NBUF));   // past the end: a repeat, never read
-    sweep(c, lds + (c % NBUF) * HL::LDS_BYTES);
+    stage(min(c + 2, C_w - 1), sbuf);   // past the end: a repeat, never read
+    sweep(c, lds + rbuf * HL::LDS_BYTES);
+    rbuf = rbuf == NBUF - 1 ? 0 : rbuf + 1;
+    sbuf = sbuf == NBUF - 1 ? 0 : sbuf + 1;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the loop
-  if (C_wg > 0) {
+  if (C_w > 0) {
 #pragma unroll
     for (int w = 0; w < NDOT; ++w) dot_item((MT - 1) & 1, 0, w);
-    reduce(C_wg - 1);
+    reduce(C_w - 1);
 #pragma unroll
     for (int i = 0; i < NL; ++i) insert_step(i);
   }
@@ -2217,10 +2236,11 @@ __global__ __launch_bounds__(kRouteThreads) void hier_visit_fast_kernel(
       const uint32_t o = bits ^ (uint32_t(int32_t(bits) >> 31) | 0x80000000u);
       uint32_t key = (c < my_C && a == a) ? (o & ~mask) | (mask - uint32_t(c)) : 0u;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
+      for (int i = 0; i < NL; ++i) {   // smaller first: no list copies per block
         const uint32_t v = lk[i];
+        const uint32_t lower = min(v, key);
         lk[i] = max(v, key);
-        key = min(v, key);
+        key = lower;
       }
     }
     scored += int(c1 - c0);
