@@ -1470,7 +1470,9 @@ __global__ __launch_bounds__(kRescoreThreads) void route_rescore_kernel(
   const int32_t* fr = frow + bkv * kFullCap;
   const int32_t* fp = fpos + bkv * kFullCap;
   float* fs = fscore + bkv * kFullCap * nb;
-  for (int j0 = 64 * wave; j0 < fc; j0 += kRescoreThreads) {
+  // full rows start at the last wave, so that with few pairs and few full
+  // rows (the common case) both run side by side instead of one after the other
+  for (int j0 = 64 * (kRescoreThreads / 64 - 1 - wave); j0 < fc; j0 += kRescoreThreads) {
     bool valid[2];
     int64_t rho_of[2];
 #pragma unroll
@@ -1551,6 +1553,30 @@ __global__ __launch_bounds__(kRecCap) void route_finalize_kernel(
 
 // Before the single pass (or the hierarchical visit): the counts its rows
 // add to start at zero, and every full-row slot at position -1 (no blocks).
+// Up to four (pointer, count, value) int32 ranges filled by one launch
+// (unused ranges have count 0).
+struct FillSpec {
+  int32_t* p[4];
+  int64_t count[4];
+  int32_t v[4];
+};
+
+__global__ __launch_bounds__(256) void fill_ranges_kernel(FillSpec f) {
+  const int64_t stride = int64_t(gridDim.x) * 256;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < f.count[r]; i += stride)
+      f.p[r][i] = f.v[r];
+}
+
+void launch_fill_ranges(const FillSpec& f, hipStream_t st) {
+  int64_t mx = 0;
+  for (int r = 0; r < 4; ++r) mx = std::max(mx, f.count[r]);
+  if (mx == 0) return;
+  hipLaunchKernelGGL(fill_ranges_kernel, dim3(unsigned(std::min<int64_t>((mx + 255) / 256, 1024))),
+                     dim3(256), 0, st, f);
+}
+
 void route_resolve_clear(const Shape& s, const RouteWs& w, int64_t n_bkv, hipStream_t st) {
   const int64_t pairs = n_bkv * s.nb;
   hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned(std::min<int64_t>((pairs + 255) / 256, 1024))),
@@ -1606,9 +1632,21 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
   using In = typename QFrag<F32>::In;
   // per (sequence, KV head): the largest |q| of its query rows (bfloat16
   // bits), which sets the float16 scale of Q (the group's rows are
-  // contiguous); the bounds start at zero
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<int32_t*>(w.qmax),
-                     5 * n_bkv, 0);
+  // contiguous); the bounds start at zero, and so do the single pass's pair
+  // and full-row counts (full-row positions at -1), in the same launch
+  {
+    FillSpec f{};
+    f.p[0] = reinterpret_cast<int32_t*>(w.qmax);
+    f.count[0] = 5 * n_bkv;
+    f.p[1] = w.pcnt;
+    f.count[1] = n_bkv * s.nb;
+    f.p[2] = w.fcnt;
+    f.count[2] = n_bkv;
+    f.p[3] = w.fpos;
+    f.count[3] = n_bkv * kFullCap;
+    f.v[3] = -1;
+    launch_fill_ranges(f, st);
+  }
   if constexpr (!F32) {
     const int64_t per_group = int64_t(s.g) * s.n * D;
     const unsigned gx = value_max_groups(per_group);
@@ -1634,7 +1672,6 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
     return hipGetLastError();
   }
   if constexpr (!F32) {
-    route_resolve_clear(s, w, n_bkv, st);
     hipLaunchKernelGGL((route_fast_kernel<D, KMAX>), dim3(grid), dim3(kRouteThreads), 0, st,
                        static_cast<const bf16_t*>(Q), w.img, w.qmax, w.bounds, idx, w.tcnt, w.trows,
                        w.rcnt, w.rmeta, w.rblk, w.rrank, w.pcnt, w.fcnt, w.frow, w.fpos, s.n, s.g,
