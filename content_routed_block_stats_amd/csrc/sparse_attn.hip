@@ -29,6 +29,7 @@
 // probabilities leave the score accumulators and enter the value product in
 // the same registers.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "kv_chunks.hpp"
@@ -668,6 +669,67 @@ int num_cus() {
   return cus;
 }
 
+// The K/V chunk images do not depend on the selection and the dispatch does
+// not depend on the images: the images are built on a second stream of the
+// device (default priority, created on first use) while the caller's stream
+// runs the dispatch, and the caller's stream waits for them before the block
+// pass.  One lease at a time per device (a mutex held while the launches are
+// enqueued, not while they run); under stream capture, or if the stream or
+// its events cannot be created, everything stays on the caller's stream.
+class SideLease {
+ public:
+  explicit SideLease(hipStream_t st) : st_(st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return;
+    Slot& sl = slots()[dev];
+    lock_ = std::unique_lock<std::mutex>(sl.mu);
+    if (!sl.tried) {
+      sl.tried = true;
+      sl.ok = hipStreamCreateWithFlags(&sl.s, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&sl.fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&sl.join, hipEventDisableTiming) == hipSuccess;
+    }
+    if (!sl.ok || hipEventRecord(sl.fork, st) != hipSuccess ||
+        hipStreamWaitEvent(sl.s, sl.fork, 0) != hipSuccess) {
+      lock_.unlock();
+      return;
+    }
+    slot_ = &sl;
+  }
+  ~SideLease() { (void)join(); }
+  SideLease(const SideLease&) = delete;
+  SideLease& operator=(const SideLease&) = delete;
+  hipStream_t stream() const { return slot_ != nullptr ? slot_->s : st_; }
+  // the caller's stream waits for everything enqueued on stream() so far
+  hipError_t join() {
+    if (slot_ == nullptr) return hipSuccess;
+    hipError_t e = hipEventRecord(slot_->join, slot_->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st_, slot_->join, 0);
+    if (e != hipSuccess) e = hipStreamSynchronize(slot_->s);   // ordering at any cost
+    slot_ = nullptr;
+    lock_.unlock();
+    return e;
+  }
+
+ private:
+  static constexpr int kMaxDev = 64;
+  struct Slot {
+    std::mutex mu;
+    bool tried = false, ok = false;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+  };
+  static Slot* slots() {
+    static Slot s[kMaxDev];
+    return s;
+  }
+  hipStream_t st_;
+  Slot* slot_ = nullptr;
+  std::unique_lock<std::mutex> lock_;
+};
+
 struct AttnWs {
   uint32_t* vmax;
   uint8_t* img;
@@ -755,16 +817,22 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
   const int64_t nseg = n_bkv * s.nb;
   const float scale2 = s.scale * kLog2e;
   hipError_t e;
-  if (!F32) {
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st,
-                       reinterpret_cast<int32_t*>(w.vmax), n_bkv, 0);
-    const int64_t per_head = s.n * D;
-    const unsigned gx = value_max_groups(per_head);
-    hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
-                       reinterpret_cast<const bf16_t*>(Vv), w.vmax, per_head);
+  // the V scale and the chunk images, beside the dispatch below
+  SideLease side(st);
+  {
+    hipStream_t ss = side.stream();
+    if (!F32) {
+      hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, ss,
+                         reinterpret_cast<int32_t*>(w.vmax), n_bkv, 0);
+      const int64_t per_head = s.n * D;
+      const unsigned gx = value_max_groups(per_head);
+      hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, ss,
+                         reinterpret_cast<const bf16_t*>(Vv), w.vmax, per_head);
+    }
+    hipLaunchKernelGGL((kv_image_kernel<F32, D>), dim3(unsigned(w.n_chunks), unsigned(n_bkv)),
+                       dim3(kAttnThreads), 0, ss, K, V, w.vmax, w.img, s.n, w.n_chunks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((kv_image_kernel<F32, D>), dim3(unsigned(w.n_chunks), unsigned(n_bkv)),
-                     dim3(kAttnThreads), 0, st, K, V, w.vmax, w.img, s.n, w.n_chunks);
   if (s.k > 0)
     hipLaunchKernelGGL((null_partial_kernel<PartT, D>), dim3(1), dim3(64), 0, st,
                        static_cast<PartT*>(w.o_part), w.lse_part, w.null_slot);
@@ -785,6 +853,7 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
     hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(256), hshm, st, idx, w.cursor, w.entries,
                        w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = side.join()) != hipSuccess) return e;
     auto bk = block_kernel_for<F32, D, PartT>(s.B / kKeyChunk);
     const size_t bshm = size_t(kResidentBytes) + (kBlockThreads / 64) * size_t(kStageBytes);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(bk),
@@ -797,6 +866,7 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
                        w.lse_part, s.n, s.g, s.hq, s.hkv, s.B, s.nb, scale2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  if ((e = side.join()) != hipSuccess) return e;   // (k = 0: the images are still needed)
   auto wk = window_merge_kernel<F32, D, PartT, OutT>;
   const size_t wshm = 2 * size_t(A::CHUNK) + size_t(kWinRows) * std::max(s.k, 1) * 4 +
                       size_t(kWinRows) * 8 +
