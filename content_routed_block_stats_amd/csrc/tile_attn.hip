@@ -94,26 +94,36 @@ __global__ __launch_bounds__(kTileThreads) void tile_attn_kernel(
   __syncthreads();
   const int nsel = nlist[0], cnt = nlist[1];
   if (cnt > 0) dma_copy_async(lds, src + int64_t(list[0]) * A::CHUNK, A::CHUNK, tid, kTileThreads);
-  for (int i = 0; i < cnt; ++i) {
-    const int buf = i & 1;
-    // chunk i has landed (this wave's copies, then everyone's), and every
-    // wave is done with chunk i-1, whose buffer the next copy refills while
-    // chunk i is computed
+  // chunk i has landed (this wave's copies, then everyone's), and every wave
+  // is done with chunk i-1, whose buffer the next copy refills while chunk i
+  // is computed
+  auto next_chunk = [&](int i) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (i + 1 < cnt)
-      dma_copy_async(lds + (buf ^ 1) * A::CHUNK, src + int64_t(list[i + 1]) * A::CHUNK, A::CHUNK,
-                     tid, kTileThreads);
+      dma_copy_async(lds + ((i & 1) ^ 1) * A::CHUNK, src + int64_t(list[i + 1]) * A::CHUNK,
+                     A::CHUNK, tid, kTileThreads);
+  };
+  // A selected block lies before the tile: every key counts for every row, so
+  // these chunks take no mask and no branch (a wave past the tile's last row
+  // works on zero queries and discards the result).  Kept apart from the
+  // window chunks' loop, whose branch would otherwise make the compiler copy
+  // the output accumulators on every chunk.
+  for (int i = 0; i < nsel; ++i) {
+    next_chunk(i);
+    attend_chunk<F32, D, 1>(lds + (i & 1) * A::CHUNK, bq, scale2, lane, st,
+                            [](int, int, int, int) { return true; });
+  }
+  // window chunks count keys in (t - W, t]
+  for (int i = nsel; i < cnt; ++i) {
+    next_chunk(i);
     const int64_t key0 = int64_t(list[i]) * kKeyChunk;
-    // a selected block lies before the tile: every key counts for every row;
-    // a window chunk counts keys in (t - W, t]
-    const bool selected = i < nsel;
-    if (wave_active && (selected || (key0 <= wave_t_hi && key0 + kKeyChunk - 1 > wave_t_lo - W))) {
+    if (wave_active && key0 <= wave_t_hi && key0 + kKeyChunk - 1 > wave_t_lo - W) {
       // 32-bit positions and bitwise tests: no exec-mask blocks per element
-      const int32_t lo = selected ? INT32_MIN : int32_t(max(tv - W, int64_t(INT32_MIN)));
-      const int32_t hi = selected ? INT32_MAX : int32_t(max(tv, int64_t(INT32_MIN)));
+      const int32_t lo = int32_t(max(tv - W, int64_t(INT32_MIN)));
+      const int32_t hi = int32_t(max(tv, int64_t(INT32_MIN)));
       const int32_t kb = int32_t(key0) + 4 * h;
-      attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
+      attend_chunk<F32, D, 1>(lds + (i & 1) * A::CHUNK, bq, scale2, lane, st,
                               [&](int, int mt, int a, int bb) {
                                 const int32_t kj = kb + 32 * mt + 8 * a + bb;
                                 return (kj <= hi) & (kj > lo);
