@@ -352,7 +352,11 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
     const int ev = F32 ? 0 : value_exponent(vmax[uint32_t(task.x) / uint32_t(nb)]);
     RowState<D> st[1];
     row_state_init(st[0]);
-    for (int sg = 0; sg < segs; ++sg) {
+    // a block of several segments is walked in alternating directions by
+    // consecutive tasks, so the segment left in LDS by one task is the first
+    // the next task of the same block needs
+    for (int sg0 = 0; sg0 < segs; ++sg0) {
+      const int sg = (p & 1) ? segs - 1 - sg0 : sg0;
       const int64_t sid = int64_t(task.x) * segs + sg;
       const int here = min(seg_chunks, block_chunks - sg * seg_chunks);
       if (sid != resident) {
