@@ -141,6 +141,13 @@ SMALL = {
         n_q_heads=4, n_kv_heads=2, seq_len=320 * 12 + 50, block=320, top_k=4, window=100, plants=4),
     "bf16_block1024_four_segments": CONFIGS["gqa_prefill_128k"].replace(
         n_q_heads=2, n_kv_heads=1, seq_len=1024 * 5 + 5, block=1024, top_k=2, window=1024, plants=2),
+    # two whole resident segments per block, walked in alternating directions
+    # by consecutive tasks (d=128: 256 keys a segment; d=64: 384)
+    "bf16_block512_two_segments": CONFIGS["gqa_prefill_128k"].replace(
+        n_q_heads=4, n_kv_heads=1, seq_len=512 * 7 + 33, block=512, top_k=3, window=200, plants=4),
+    "bf16_d64_block768_two_segments": CONFIGS["prefill_32k"].replace(
+        n_q_heads=2, n_kv_heads=1, head_dim=64, seq_len=768 * 5 + 70, block=768, top_k=2,
+        window=300, plants=2),
     # d=64 bf16: 512 keys per segment
     "bf16_d64_block576": CONFIGS["prefill_32k"].replace(
         n_q_heads=2, n_kv_heads=2, head_dim=64, seq_len=576 * 6 + 11, block=576, top_k=3, window=64,
