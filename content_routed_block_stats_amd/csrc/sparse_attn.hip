@@ -210,11 +210,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   }
 }
 
-// Exclusive scan of the per-block task counts; emits the task list in block
-// order, task j = (segment, first entry j kTaskRows, rows), and points the
-// scatter cursor of every segment at its first task's entries.
+// Exclusive scan of the per-block task counts: points the scatter cursor of
+// every segment at its first task's entries and counts the tasks; the task
+// list itself (in block order, task j = (segment, first entry j kTaskRows,
+// rows)) is written by emit_tasks_kernel.
 __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
-    const int32_t* __restrict__ counts, int32_t* __restrict__ cursor, int4* __restrict__ tasks,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ cursor,
     int32_t* __restrict__ task_count, int64_t nseg) {
   constexpr int ITEMS = 4;
   __shared__ int32_t st[kScanThreads];
@@ -243,11 +244,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       const int64_t s = base + int64_t(tid) * ITEMS + i;
-      if (s < nseg) {
-        cursor[s] = ot * kTaskRows;
-        for (int q = 0; q < tk[i]; ++q)
-          tasks[ot + q] = int4{int32_t(s), (ot + q) * kTaskRows, min(kTaskRows, c[i] - q * kTaskRows), 0};
-      }
+      if (s < nseg) cursor[s] = ot * kTaskRows;
       ot += tk[i];
     }
     __syncthreads();
@@ -255,6 +252,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
     __syncthreads();
   }
   if (tid == 0) task_count[0] = carry_t;
+}
+
+// Task j of the list (one thread each, coalesced stores): its segment is the
+// last one whose first entry slot is at or below j's (a segment without rows
+// starts where the next one does), and its rows are the segment's rows from
+// that slot on, at most kTaskRows.  Runs between the scan and the scatter,
+// which advances the cursors.
+__global__ __launch_bounds__(256) void emit_tasks_kernel(const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ cursor,
+                                                         int4* __restrict__ tasks,
+                                                         const int32_t* __restrict__ task_count,
+                                                         int64_t nseg) {
+  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= int64_t(*task_count)) return;
+  const int32_t jr = int32_t(j) * kTaskRows;
+  int64_t lo = 0, hi = nseg;   // cursor[lo] <= jr, and every index past hi is above jr
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if (cursor[mid] <= jr) lo = mid; else hi = mid;
+  }
+  const int32_t q = (jr - cursor[lo]) / kTaskRows;
+  tasks[j] = int4{int32_t(lo), jr, min(kTaskRows, counts[lo] - q * kTaskRows), 0};
+}
+
+// The scan of the per-segment counts, then the task list.
+void launch_scan_tasks(const int32_t* counts, int32_t* cursor, int4* tasks, int32_t* task_count,
+                       int64_t nseg, int64_t max_tasks, hipStream_t st) {
+  hipLaunchKernelGGL(scan_tasks_kernel, dim3(1), dim3(kScanThreads), 0, st, counts, cursor,
+                     task_count, nseg);
+  hipLaunchKernelGGL(emit_tasks_kernel, dim3(unsigned((max_tasks + 255) / 256)), dim3(256), 0, st,
+                     counts, cursor, tasks, task_count, nseg);
 }
 
 // ---------------------------------------------------------- block attention --
@@ -852,8 +880,7 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
         return e;
     hipLaunchKernelGGL(dispatch_kernel<false>, hgrid, dim3(256), hshm, st, idx, w.counts,
                        (uint32_t*)nullptr, (int32_t*)nullptr, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
-    hipLaunchKernelGGL(scan_tasks_kernel, dim3(1), dim3(kScanThreads), 0, st, w.counts, w.cursor,
-                       w.tasks, w.task_count, nseg);
+    launch_scan_tasks(w.counts, w.cursor, w.tasks, w.task_count, nseg, w.max_tasks, st);
     hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(256), hshm, st, idx, w.cursor, w.entries,
                        w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -941,8 +968,7 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* idx, const DispatchWs&
       return e;
   hipLaunchKernelGGL(dispatch_kernel<false>, hgrid, dim3(256), hshm, st, idx, w.counts,
                      (uint32_t*)nullptr, (int32_t*)nullptr, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
-  hipLaunchKernelGGL(scan_tasks_kernel, dim3(1), dim3(kScanThreads), 0, st, w.counts, w.cursor,
-                     w.tasks, w.task_count, nseg);
+  launch_scan_tasks(w.counts, w.cursor, w.tasks, w.task_count, nseg, w.max_tasks, st);
   hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(256), hshm, st, idx, w.cursor, w.entries,
                      w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
   return hipGetLastError();
