@@ -14,12 +14,18 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous
  *    row-major in the layout stated at each call, aligned to 16 bytes.  The
  *    library never allocates, frees or retains device memory; scratch space
- *    is the caller's workspace.  It keeps no global mutable state, so calls
+ *    is the caller's workspace.  It keeps no global mutable data, so calls
  *    on different streams may run concurrently -- except
  *    ssa_decode_step_noalloc, whose scratch is a device array inside the
  *    library (see there).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns; results are ready when the stream is.
+ *    ssa_sparse_attn_fwd runs part of its work (the K/V chunk images) on a
+ *    second stream of the device, created on the first call and kept for the
+ *    process, that waits for the caller's stream and that the caller's stream
+ *    waits for again before the dependent work: ordering against the
+ *    caller's stream is as if everything ran on it.  Under stream capture
+ *    everything runs on the caller's stream.
  *  - Validation is synchronous and on the host, before anything is enqueued:
  *    on an error nothing is launched and a status other than SSA_OK is
  *    returned; ssa_last_error() then holds a message (per thread).  A launch
