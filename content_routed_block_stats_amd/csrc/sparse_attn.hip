@@ -502,6 +502,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 
   RowState<D> st[1];
   row_state_init(st[0]);
+  int32_t excl_blk = -1;   // the block whose selection test excl holds
+  bool excl = false;
   // the query fragments and index rows are in before the loop, so the
   // compiler's own waits inside it (it cannot see the chunk copies) have
   // nothing left to wait for
@@ -522,18 +524,32 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     // does this wave's token range touch the chunk at all?
     const bool touch = wave_active && key0 <= wave_t_hi && key0 + kKeyChunk - 1 > wave_t_lo - W;
     if (touch) {
-      // keys of a selected block already count in that block's partial
+      // keys of a selected block already count in that block's partial (the
+      // test is redone only when the chunk enters another block)
       const int32_t blk = int32_t(key0 / B);
-      bool excl = false;
-      for (int i = 0; i < k; ++i) excl |= sidx[i * kWinRows + r] == blk;
-      // 32-bit positions and bitwise tests: no exec-mask blocks per element
-      const int32_t tv = valid && !excl ? int32_t(t) : -(1 << 30);
-      const int32_t kb = int32_t(key0) + 4 * h;
-      attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
-                              [&](int, int mt, int a, int bb) {
-                                const int32_t j = kb + 32 * mt + 8 * a + bb;
-                                return (j <= tv) & (j > tv - W);
-                              });
+      if (blk != excl_blk) {
+        excl = false;
+        for (int i = 0; i < k; ++i) excl |= sidx[i * kWinRows + r] == blk;
+        excl_blk = blk;
+      }
+      const bool rowok = valid && !excl;
+      // a chunk inside the window of every token of the wave needs no
+      // per-key test: the row's own test decides (a lane holds one row's
+      // scores, so the test is one per lane)
+      const bool inner = key0 + kKeyChunk - 1 <= wave_t_lo && key0 > wave_t_hi - W;
+      if (inner) {
+        attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
+                                [&](int, int, int, int) { return rowok; });
+      } else {
+        // 32-bit positions and bitwise tests: no exec-mask blocks per element
+        const int32_t tv = rowok ? int32_t(t) : -(1 << 30);
+        const int32_t kb = int32_t(key0) + 4 * h;
+        attend_chunk<F32, D, 1>(lds + buf * A::CHUNK, bq, scale2, lane, st,
+                                [&](int, int mt, int a, int bb) {
+                                  const int32_t j = kb + 32 * mt + 8 * a + bb;
+                                  return (j <= tv) & (j > tv - W);
+                                });
+      }
     }
   }
   __syncthreads();   // every wave is done with the chunk buffers
