@@ -48,13 +48,17 @@ constexpr int kWinRows = 128;              // rows per window/merge tile
 constexpr int kHistTokens = 2048;          // tokens per dispatch workgroup
 constexpr int kScanThreads = 1024;
 
+using f32x2 = float __attribute__((ext_vector_type(2)));
+
 // The partials of a wave's 32 rows (row r: D values, lane half h holds
 // columns h D/2 .. in accumulator order, one row after the other in global
 // memory).  A lane's registers hold one half row, so storing them directly
 // would give each store instruction 64 scattered 16-byte pieces; instead the
 // rows pass through kStageBytes of LDS per wave (rounds of kStageBytes / row
 // bytes rows, 16-byte chunks XOR-swizzled by row against bank conflicts) and
-// leave as fully contiguous 1 KB stores.  Lanes read what other lanes of the
+// leave as fully contiguous 1 KB stores, marked nontemporal: each partial is
+// read once, much later, by the merge, and the caches are better kept for the
+// query rows and K/V images the pass re-reads.  Lanes read what other lanes of the
 // wave wrote, so every round is fenced at wavefront scope on both sides: LDS
 // keeps a wave's accesses in order, the fences keep the compiler from reusing
 // earlier loads or moving accesses across them.
@@ -102,8 +106,9 @@ __device__ __forceinline__ void store_partials(uint8_t* stage, PartT* dst, const
 #pragma unroll
     for (int k = 0; k < kStageBytes / 1024; ++k) {
       const int pc = k * 64 + lane, ri = pc / CH, c = pc % CH;
-      *reinterpret_cast<u32x4*>(out + pc * 16) =
-          *reinterpret_cast<const u32x4*>(stage + ri * ROWB + ((c ^ (ri & (CH - 1))) * 16));
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(stage + ri * ROWB + ((c ^ (ri & (CH - 1))) * 16)),
+          reinterpret_cast<u32x4*>(out + pc * 16));
     }
   }
 }
@@ -417,7 +422,8 @@ __global__ __launch_bounds__(kBlockThreads) void block_attn_kernel(
       const int64_t pidx = ti * kTaskRows + r;
       store_partials<PartT, D>(lds + kResidentBytes + wave * kStageBytes,
                                o_part + (pidx - ln) * D, st[0].o, ldexpf(1.f, -e), ln, h, lane);
-      lse_part[pidx] = float2{st[0].m2 + __log2f(l), st[0].m2 + float(e + ev)};
+      __builtin_nontemporal_store(f32x2{st[0].m2 + __log2f(l), st[0].m2 + float(e + ev)},
+                                  reinterpret_cast<f32x2*>(lse_part + pidx));
     }
     // (d) rotate the pipeline
     task = task_n;
