@@ -886,6 +886,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   dma_copy(lds, srca + ch_lo * A::CHUNK, A::KBYTES, tid, 256);
   dma_copy(lds + A::KBYTES, srcb + ch_lo * A::CHUNK, A::CHUNK, tid, 256);
   __syncthreads();
+  int32_t excl_blk = -1;   // the block whose selection test excl holds
+  bool excl = false;
   for (int64_t ch = ch_lo; ch <= ch_hi; ++ch) {
     const int buf = int((ch - ch_lo) % NBUF);
     uint8_t* L = lds + buf * BUF;
@@ -896,10 +898,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
     const int64_t key0 = ch * kKeyChunk;
     if (wave_active && key0 <= wave_t_hi && key0 + kKeyChunk - 1 > wave_t_lo - W) {
+      // (the selection test is redone only when a chunk enters another block)
       const int32_t blk = int32_t(key0 / B);
-      bool excl = false;
-      if (valid)
-        for (int i = 0; i < k; ++i) excl |= idx[row * k + i] == blk;
+      if (blk != excl_blk) {
+        excl = false;
+        if (valid)
+          for (int i = 0; i < k; ++i) excl |= idx[row * k + i] == blk;
+        excl_blk = blk;
+      }
       // positions fit in 32 bits; a row that takes no window keys here gets a
       // position no key reaches
       const int32_t tv = valid && !excl ? int32_t(t) : -(1 << 30);

@@ -169,18 +169,25 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   const int64_t t1 = min(n, t0 + kHistTokens);
   for (int64_t i = tid; i < nb; i += 256) hist[i] = 0;
   __syncthreads();
-  constexpr int KG = 8;   // a row's selections in groups: loads, then LDS counts
+  // the workgroup's selections of one q-head are one contiguous run of idx
+  // (tokens t0..t1, k each): thread tid takes elements tid, tid + 256, ...,
+  // KG at a time, so the loads (and the scatter's pos stores) are coalesced
+  // and a group's LDS operations go out together
+  constexpr int KG = 8;
+  const int run = int((t1 - t0) * k);   // at most kHistTokens x 32
   for (int j = 0; j < g; ++j) {
-    const int32_t* base = idx + ((b * hq + kv * g + j) * n) * k;
-    for (int64_t t = t0 + tid; t < t1; t += 256)
-      for (int i0 = 0; i0 < k; i0 += KG) {
-        int32_t c[KG];
+    const int32_t* src = idx + ((b * hq + kv * g + j) * n + t0) * k;
+    for (int w0 = 0; w0 < run; w0 += KG * 256) {
+      int32_t c[KG];
 #pragma unroll
-        for (int q = 0; q < KG; ++q) c[q] = i0 + q < k ? base[t * k + i0 + q] : -1;
-#pragma unroll
-        for (int q = 0; q < KG; ++q)
-          if (c[q] >= 0 && c[q] < nb) atomicAdd(&hist[c[q]], 1);
+      for (int q = 0; q < KG; ++q) {
+        const int w = w0 + q * 256 + tid;
+        c[q] = w < run ? src[w] : -1;
       }
+#pragma unroll
+      for (int q = 0; q < KG; ++q)
+        if (c[q] >= 0 && c[q] < nb) atomicAdd(&hist[c[q]], 1);
+    }
   }
   __syncthreads();
   int32_t* seg = counts_or_cursor + bkv * nb;
@@ -193,25 +200,26 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   }
   if (!SCATTER) return;
   __syncthreads();
-  // the LDS reservations of a group are independent and go out together
-  // instead of one round trip each
   for (int j = 0; j < g; ++j) {
-    const int64_t base = ((b * hq + kv * g + j) * n) * k;
-    for (int64_t t = t0 + tid; t < t1; t += 256)
-      for (int i0 = 0; i0 < k; i0 += KG) {
-        int32_t c[KG], e[KG];
+    const int64_t base = ((b * hq + kv * g + j) * n + t0) * k;
+    for (int w0 = 0; w0 < run; w0 += KG * 256) {
+      int32_t c[KG], e[KG];
 #pragma unroll
-        for (int q = 0; q < KG; ++q) c[q] = i0 + q < k ? idx[base + t * k + i0 + q] : -1;
-#pragma unroll
-        for (int q = 0; q < KG; ++q)
-          e[q] = (c[q] >= 0 && c[q] < nb) ? atomicAdd(&hist[c[q]], 1) : -1;
-#pragma unroll
-        for (int q = 0; q < KG; ++q)
-          if (e[q] >= 0) {
-            entries[e[q]] = (uint32_t(t * g + j) << 5) | uint32_t(i0 + q);
-            pos[base + t * k + i0 + q] = e[q];
-          }
+      for (int q = 0; q < KG; ++q) {
+        const int w = w0 + q * 256 + tid;
+        c[q] = w < run ? idx[base + w] : -1;
       }
+#pragma unroll
+      for (int q = 0; q < KG; ++q) e[q] = (c[q] >= 0 && c[q] < nb) ? atomicAdd(&hist[c[q]], 1) : -1;
+#pragma unroll
+      for (int q = 0; q < KG; ++q)
+        if (e[q] >= 0) {
+          const int w = w0 + q * 256 + tid;
+          const int64_t t = t0 + w / k;
+          entries[e[q]] = (uint32_t(t * g + j) << 5) | uint32_t(w % k);
+          pos[base + w] = e[q];
+        }
+    }
   }
 }
 
