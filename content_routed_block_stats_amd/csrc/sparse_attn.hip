@@ -46,7 +46,8 @@ constexpr int kRunTasks = 8;               // consecutive tasks a workgroup take
 constexpr int kStageBytes = 4096;          // LDS per wave that lines partials up for storing
 constexpr int kWinRows = 128;              // rows per window/merge tile
 constexpr int kHistTokens = 2048;          // tokens per dispatch workgroup
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 256;           // one workgroup: small, so it finds a CU at once
+constexpr int kDispatchThreads = 1024;     // dispatch workgroups: 16 waves each
 
 using f32x2 = float __attribute__((ext_vector_type(2)));
 
@@ -157,7 +158,7 @@ __global__ void null_partial_kernel(PartT* o_part, float2* lse_part, int64_t slo
 // covers kHistTokens tokens of one (sequence, KV head) and all its group's
 // q-heads.
 template <bool SCATTER>
-__global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict__ idx,
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(const int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ counts_or_cursor,
                                                        uint32_t* __restrict__ entries,
                                                        int32_t* __restrict__ pos, int64_t n,
@@ -167,21 +168,21 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   const int64_t bkv = blockIdx.y, b = bkv / hkv, kv = bkv % hkv;
   const int64_t t0 = int64_t(blockIdx.x) * kHistTokens;
   const int64_t t1 = min(n, t0 + kHistTokens);
-  for (int64_t i = tid; i < nb; i += 256) hist[i] = 0;
+  for (int64_t i = tid; i < nb; i += kDispatchThreads) hist[i] = 0;
   __syncthreads();
   // the workgroup's selections of one q-head are one contiguous run of idx
-  // (tokens t0..t1, k each): thread tid takes elements tid, tid + 256, ...,
+  // (tokens t0..t1, k each): thread tid takes elements tid + i T (T threads),
   // KG at a time, so the loads (and the scatter's pos stores) are coalesced
   // and a group's LDS operations go out together
   constexpr int KG = 8;
   const int run = int((t1 - t0) * k);   // at most kHistTokens x 32
   for (int j = 0; j < g; ++j) {
     const int32_t* src = idx + ((b * hq + kv * g + j) * n + t0) * k;
-    for (int w0 = 0; w0 < run; w0 += KG * 256) {
+    for (int w0 = 0; w0 < run; w0 += KG * kDispatchThreads) {
       int32_t c[KG];
 #pragma unroll
       for (int q = 0; q < KG; ++q) {
-        const int w = w0 + q * 256 + tid;
+        const int w = w0 + q * kDispatchThreads + tid;
         c[q] = w < run ? src[w] : -1;
       }
 #pragma unroll
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   }
   __syncthreads();
   int32_t* seg = counts_or_cursor + bkv * nb;
-  for (int64_t i = tid; i < nb; i += 256) {
+  for (int64_t i = tid; i < nb; i += kDispatchThreads) {
     const int32_t v = hist[i];
     if (v > 0) {
       const int32_t base = atomicAdd(&seg[i], v);
@@ -202,11 +203,11 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
   __syncthreads();
   for (int j = 0; j < g; ++j) {
     const int64_t base = ((b * hq + kv * g + j) * n + t0) * k;
-    for (int w0 = 0; w0 < run; w0 += KG * 256) {
+    for (int w0 = 0; w0 < run; w0 += KG * kDispatchThreads) {
       int32_t c[KG], e[KG];
 #pragma unroll
       for (int q = 0; q < KG; ++q) {
-        const int w = w0 + q * 256 + tid;
+        const int w = w0 + q * kDispatchThreads + tid;
         c[q] = w < run ? idx[base + w] : -1;
       }
 #pragma unroll
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
 #pragma unroll
       for (int q = 0; q < KG; ++q)
         if (e[q] >= 0) {
-          const int w = w0 + q * 256 + tid;
+          const int w = w0 + q * kDispatchThreads + tid;
           const int64_t t = t0 + w / k;
           entries[e[q]] = (uint32_t(t * g + j) << 5) | uint32_t(w % k);
           pos[base + w] = e[q];
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
 __global__ __launch_bounds__(kScanThreads) void scan_tasks_kernel(
     const int32_t* __restrict__ counts, int32_t* __restrict__ cursor,
     int32_t* __restrict__ task_count, int64_t nseg) {
-  constexpr int ITEMS = 4;
+  constexpr int ITEMS = 16;
   __shared__ int32_t st[kScanThreads];
   __shared__ int32_t carry_t;
   const int tid = threadIdx.x;
@@ -908,11 +909,11 @@ hipError_t launch_attn_t(const Shape& s, const void* Qv, const void* Kv, const v
       if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(hshm))) !=
           hipSuccess)
         return e;
-    hipLaunchKernelGGL(dispatch_kernel<false>, hgrid, dim3(256), hshm, st, idx, w.counts,
-                       (uint32_t*)nullptr, (int32_t*)nullptr, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
+    hipLaunchKernelGGL(dispatch_kernel<false>, hgrid, dim3(kDispatchThreads), hshm, st, idx,
+                       w.counts, (uint32_t*)nullptr, (int32_t*)nullptr, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
     launch_scan_tasks(w.counts, w.cursor, w.tasks, w.task_count, nseg, w.max_tasks, st);
-    hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(256), hshm, st, idx, w.cursor, w.entries,
-                       w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
+    hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(kDispatchThreads), hshm, st, idx,
+                       w.cursor, w.entries, w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = side.join()) != hipSuccess) return e;
     auto bk = block_kernel_for<F32, D, PartT>(s.B / kKeyChunk);
@@ -996,11 +997,11 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* idx, const DispatchWs&
     if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(hshm))) !=
         hipSuccess)
       return e;
-  hipLaunchKernelGGL(dispatch_kernel<false>, hgrid, dim3(256), hshm, st, idx, w.counts,
+  hipLaunchKernelGGL(dispatch_kernel<false>, hgrid, dim3(kDispatchThreads), hshm, st, idx, w.counts,
                      (uint32_t*)nullptr, (int32_t*)nullptr, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
   launch_scan_tasks(w.counts, w.cursor, w.tasks, w.task_count, nseg, w.max_tasks, st);
-  hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(256), hshm, st, idx, w.cursor, w.entries,
-                     w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
+  hipLaunchKernelGGL(dispatch_kernel<true>, hgrid, dim3(kDispatchThreads), hshm, st, idx, w.cursor,
+                     w.entries, w.pos, s.n, s.g, s.hq, s.hkv, s.k, s.nb);
   return hipGetLastError();
 }
 
