@@ -388,7 +388,9 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
       *reinterpret_cast<f16x8*>(out + f * kFragBytes + 1024 + ln * 16) = lo;
     }
   }
-  const float mscale = F32 ? scale : scale * ldexpf(1.f, -query_exponent(qmax[blockIdx.y]));
+  // (a null qmax leaves mu at 2^-e: route_mu_scale_kernel applies 2^-eq)
+  const float mscale =
+      F32 || qmax == nullptr ? scale : scale * ldexpf(1.f, -query_exponent(qmax[blockIdx.y]));
   for (int w = tid; w < 2 * Lay::MT * 16; w += blockDim.x) {
     const int h = w / (Lay::MT * 16), mt = (w / 16) % Lay::MT, i = w % 16;
     reinterpret_cast<float*>(out + Lay::MU_OFF)[w] = M[32 * mt + 8 * (i / 4) + 4 * h + (i % 4)] * mscale;
@@ -1623,6 +1625,26 @@ hipError_t route_resolve(const Shape& s, const void* Q, const RouteWs& w, int32_
   return hipGetLastError();
 }
 
+// Multiplies the mu section of every block image of (sequence, KV head)
+// blockIdx.y by 2^-eq, the float16 scale of that KV head's query rows, for
+// images that route_prep_kernel wrote with a null qmax (so that it could run
+// beside the max|q| pass).  Both factors are powers of two, so the result is
+// the one a single multiplication by 2^-(e + eq) gives.
+template <int D>
+__global__ __launch_bounds__(256) void route_mu_scale_kernel(const uint32_t* __restrict__ qmax,
+                                                             uint8_t* __restrict__ prep,
+                                                             int64_t nb) {
+  using Lay = RouteLayout<D>;
+  constexpr int NMU = Lay::MU_BYTES / 4;
+  const int64_t bkv = blockIdx.y;
+  const float f = ldexpf(1.f, -query_exponent(qmax[bkv]));
+  for (int64_t w = int64_t(blockIdx.x) * 256 + threadIdx.x; w < nb * NMU;
+       w += int64_t(gridDim.x) * 256) {
+    float* m = reinterpret_cast<float*>(prep + (bkv * nb + w / NMU) * Lay::BLOCK_BYTES + Lay::MU_OFF);
+    m[w % NMU] *= f;
+  }
+}
+
 template <bool F32, int D, int KMAX>
 hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const float* sigma,
                           int32_t* idx, float* kth, void* ws, hipStream_t st) {
@@ -1647,18 +1669,31 @@ hipError_t launch_route_t(const Shape& s, const void* Q, const float* mu, const 
     f.v[3] = -1;
     launch_fill_ranges(f, st);
   }
-  if constexpr (!F32) {
-    const int64_t per_group = int64_t(s.g) * s.n * D;
-    const unsigned gx = value_max_groups(per_group);
-    hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(Q), w.qmax, per_group);
-  }
-  if (s.nb > 0) {
-    hipLaunchKernelGGL((route_prep_kernel<F32, D>), dim3(unsigned(s.nb), unsigned(n_bkv)),
-                       dim3(256), 0, st, mu, sigma, w.qmax, w.bounds, w.dbar, w.img, s.nb, s.beta,
-                       sigma, s.nb);
+  // the max|q| pass (bfloat16 inputs) runs on the device's second stream
+  // beside the image preparation, which then leaves mu unscaled by the
+  // query scale until both are done
+  {
+    SideLease side(st);
+    if constexpr (!F32) {
+      const int64_t per_group = int64_t(s.g) * s.n * D;
+      const unsigned gx = value_max_groups(per_group);
+      hipLaunchKernelGGL(value_max_kernel, dim3(gx, unsigned(n_bkv)), dim3(256), 0, side.stream(),
+                         static_cast<const bf16_t*>(Q), w.qmax, per_group);
+    }
+    if (s.nb > 0)
+      hipLaunchKernelGGL((route_prep_kernel<F32, D>), dim3(unsigned(s.nb), unsigned(n_bkv)),
+                         dim3(256), 0, st, mu, sigma, nullptr, w.bounds, w.dbar, w.img, s.nb,
+                         s.beta, sigma, s.nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if ((e = side.join()) != hipSuccess) return e;
+    if (!F32 && s.nb > 0) {
+      const int64_t elems = s.nb * (RouteLayout<D>::MU_BYTES / 4);
+      const unsigned gx = unsigned(std::min<int64_t>((elems + 255) / 256, 64));
+      hipLaunchKernelGGL((route_mu_scale_kernel<D>), dim3(gx, unsigned(n_bkv)), dim3(256), 0, st,
+                         w.qmax, w.img, s.nb);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   int key_bits = 1;
   while ((int64_t(1) << key_bits) < s.nb) ++key_bits;

@@ -733,65 +733,9 @@ int num_cus() {
 }
 
 // The K/V chunk images do not depend on the selection and the dispatch does
-// not depend on the images: the images are built on a second stream of the
-// device (default priority, created on first use) while the caller's stream
-// runs the dispatch, and the caller's stream waits for them before the block
-// pass.  One lease at a time per device (a mutex held while the launches are
-// enqueued, not while they run); under stream capture, or if the stream or
-// its events cannot be created, everything stays on the caller's stream.
-class SideLease {
- public:
-  explicit SideLease(hipStream_t st) : st_(st) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return;
-    Slot& sl = slots()[dev];
-    lock_ = std::unique_lock<std::mutex>(sl.mu);
-    if (!sl.tried) {
-      sl.tried = true;
-      sl.ok = hipStreamCreateWithFlags(&sl.s, hipStreamNonBlocking) == hipSuccess &&
-              hipEventCreateWithFlags(&sl.fork, hipEventDisableTiming) == hipSuccess &&
-              hipEventCreateWithFlags(&sl.join, hipEventDisableTiming) == hipSuccess;
-    }
-    if (!sl.ok || hipEventRecord(sl.fork, st) != hipSuccess ||
-        hipStreamWaitEvent(sl.s, sl.fork, 0) != hipSuccess) {
-      lock_.unlock();
-      return;
-    }
-    slot_ = &sl;
-  }
-  ~SideLease() { (void)join(); }
-  SideLease(const SideLease&) = delete;
-  SideLease& operator=(const SideLease&) = delete;
-  hipStream_t stream() const { return slot_ != nullptr ? slot_->s : st_; }
-  // the caller's stream waits for everything enqueued on stream() so far
-  hipError_t join() {
-    if (slot_ == nullptr) return hipSuccess;
-    hipError_t e = hipEventRecord(slot_->join, slot_->s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(st_, slot_->join, 0);
-    if (e != hipSuccess) e = hipStreamSynchronize(slot_->s);   // ordering at any cost
-    slot_ = nullptr;
-    lock_.unlock();
-    return e;
-  }
-
- private:
-  static constexpr int kMaxDev = 64;
-  struct Slot {
-    std::mutex mu;
-    bool tried = false, ok = false;
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-  };
-  static Slot* slots() {
-    static Slot s[kMaxDev];
-    return s;
-  }
-  hipStream_t st_;
-  Slot* slot_ = nullptr;
-  std::unique_lock<std::mutex> lock_;
-};
+// not depend on the images: the images are built on the device's second
+// stream (SideLease) while the caller's stream runs the dispatch, and the
+// caller's stream waits for them before the block pass.
 
 struct AttnWs {
   uint32_t* vmax;

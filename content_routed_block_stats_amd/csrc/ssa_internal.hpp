@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace ssa {
 
 // Validated shapes and parameters of one call (see include/ssa.h).
@@ -15,6 +17,67 @@ struct Shape {
   int64_t nb;     // complete blocks of n (stat slots per (sequence, KV head))
   float beta, scale;
   bool in_bf16, out_bf16;
+};
+
+// A second stream of the current device (default priority, created on first
+// use) for work that can run beside the caller's stream: everything enqueued
+// on stream() after the lease starts follows the caller's stream's work so
+// far, and join() (or the destructor) makes the caller's stream wait for it.
+// One lease at a time per device (a mutex held while the launches are
+// enqueued, not while they run); under stream capture, or if the stream or
+// its events cannot be created, stream() is the caller's stream.
+class SideLease {
+ public:
+  explicit SideLease(hipStream_t st) : st_(st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return;
+    Slot& sl = slots()[dev];
+    lock_ = std::unique_lock<std::mutex>(sl.mu);
+    if (!sl.tried) {
+      sl.tried = true;
+      sl.ok = hipStreamCreateWithFlags(&sl.s, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&sl.fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&sl.join, hipEventDisableTiming) == hipSuccess;
+    }
+    if (!sl.ok || hipEventRecord(sl.fork, st) != hipSuccess ||
+        hipStreamWaitEvent(sl.s, sl.fork, 0) != hipSuccess) {
+      lock_.unlock();
+      return;
+    }
+    slot_ = &sl;
+  }
+  ~SideLease() { (void)join(); }
+  SideLease(const SideLease&) = delete;
+  SideLease& operator=(const SideLease&) = delete;
+  hipStream_t stream() const { return slot_ != nullptr ? slot_->s : st_; }
+  // the caller's stream waits for everything enqueued on stream() so far
+  hipError_t join() {
+    if (slot_ == nullptr) return hipSuccess;
+    hipError_t e = hipEventRecord(slot_->join, slot_->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st_, slot_->join, 0);
+    if (e != hipSuccess) e = hipStreamSynchronize(slot_->s);   // ordering at any cost
+    slot_ = nullptr;
+    lock_.unlock();
+    return e;
+  }
+
+ private:
+  static constexpr int kMaxDev = 64;
+  struct Slot {
+    std::mutex mu;
+    bool tried = false, ok = false;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+  };
+  static Slot* slots() {
+    static Slot s[kMaxDev];
+    return s;
+  }
+  hipStream_t st_;
+  Slot* slot_ = nullptr;
+  std::unique_lock<std::mutex> lock_;
 };
 
 constexpr size_t kWsAlign = 256;
